@@ -1,0 +1,235 @@
+/*
+ * lora.h -- C ABI of liblora, the mixed-adapter LoRA linear layer for one
+ * MI355X (gfx950) GPU.
+ *
+ * The operation (row-vector form):  for every token row t of a batch
+ *
+ *     y[t,:] = x[t,:] W  +  s_a * (x[t,:] A_a) B_a        a = ids[t]
+ *
+ * where W is the shared base weight [d_in, d_out], A_a [d_in, r_a] and
+ * B_a [r_a, d_out] are the low-rank pair of adapter slot a, s_a = alpha_a/r_a,
+ * and a = -1 means "no adapter" (base row only).
+ *   - The forward y = xW + s (xA) B with A of shape d x r and B of shape r x d'
+ *     and the BGMV / SGMV ways of batching it: "Serving multiple LoRAs:
+ *     segmented matrix multiplies and adapter scheduling", section "Not
+ *     merging the weights, computing in batches".
+ *   - s = alpha / r, the shared base product over all tokens and the
+ *     per-segment delta: "LoRAX, in depth", section "Computing a batch that
+ *     mixes adapters".
+ *   - Stacked per-slot buffers, the slot copy on activation, zeroing of an
+ *     unused slot, slot buffers sized for the maximum rank, shrink into an
+ *     fp32 rank-width buffer followed by an expand added to the output, and
+ *     -1 as the slot of a token without adapter: "Serving LoRA adapters: from
+ *     the model name to the wrapped layer", Steps 3, 4 and 5.
+ *
+ * Conventions for every function below
+ *   - Pointers named as DEVICE point to GPU memory owned by the caller (the
+ *     library never allocates or frees device memory).  HOST pointers point
+ *     to host memory owned by the caller.
+ *   - All GPU work is enqueued on the caller's `stream` and is asynchronous;
+ *     the caller keeps every buffer alive until the stream has passed the
+ *     call.  Work on one stream is ordered, so uploading into a slot after a
+ *     forward on the same stream is safe; use an event across streams.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     any status other than LORA_OK nothing was enqueued.
+ *   - Row-major everywhere.  x, W, y and the pool share one element type
+ *     (fp32 or bf16); accumulation is always fp32; v is always fp32.
+ *   - d_in and d_out must be positive multiples of 8; max_rank a multiple of
+ *     8 in [8, 128]; T >= 0 (T == 0 is a no-op returning LORA_OK).
+ *   - Device pointers must be 16-byte aligned.
+ *   - Bad adapter ids found on the device (outside [-1, n_slots) or naming a
+ *     slot of rank 0) never fault: the row is computed as a base row and the
+ *     smallest such row index is recorded in the workspace's error word,
+ *     read (and cleared) by lora_get_device_error.
+ *   - No function keeps hidden state; all are reentrant.  Two calls that
+ *     share a workspace must be ordered (same stream or events).
+ *   - Results are deterministic: the same inputs give bitwise the same
+ *     outputs (no floating-point atomics).
+ */
+#ifndef LORA_H_
+#define LORA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *lora_stream_t; /* a hipStream_t; NULL = the null stream */
+
+typedef enum {
+    LORA_OK = 0,
+    LORA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, bad dtype, misaligned pointer */
+    LORA_ERR_RANK_EXCEEDS_MAX = 2,   /* upload with r > max_rank ("Serving LoRA adapters ...", Step 3: the rank check against the maximum LoRA rank) */
+    LORA_ERR_SLOT_OUT_OF_RANGE = 3,  /* slot outside [0, n_slots) */
+    LORA_ERR_WORKSPACE_TOO_SMALL = 4,
+    LORA_ERR_UNSUPPORTED = 5,        /* combination not implemented (e.g. too many slots) */
+    LORA_ERR_HIP = 6                 /* the HIP runtime reported an error at launch */
+} lora_status_t;
+
+typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype_t;
+
+/* How the low-rank term is batched ("Serving multiple LoRAs ...", section
+ * "Not merging the weights, computing in batches"):
+ *   BGMV: every row gathers its own adapter (rows in their original order);
+ *   SGMV: rows are grouped into adapter-contiguous segments (a stable sort by
+ *         slot, built by lora_build_segments) and each segment shares one
+ *         read of its adapter;
+ *   AUTO: in lora_linear_forward, SGMV when T >= 1024, else BGMV; in
+ *         lora_shrink and lora_expand (which cannot know whether segments
+ *         were built), BGMV.
+ * The result does not depend on the mode beyond fp32 rounding order. */
+typedef enum { LORA_MODE_AUTO = 0, LORA_MODE_BGMV = 1, LORA_MODE_SGMV = 2 } lora_mode_t;
+
+/* Flags for lora_linear_forward. */
+#define LORA_FLAG_SEGMENTS_READY 0x1  /* segments already built in this workspace for these ids */
+#define LORA_FLAG_SEPARATE_EXPAND 0x2 /* expand as its own read-modify-write pass, not in the GEMM epilogue */
+
+/*
+ * The HBM adapter pool of one projection: n_slots stacked, rank-padded slots
+ * (the stacked buffers of "Serving LoRA adapters ...", Step 3/4).  A plain
+ * descriptor filled by lora_pool_create and not modified afterwards.
+ * Internal layout, per slot s (the library's choice, documented for tools):
+ *   a: A transposed, [max_rank][d_in]           -- rank rows contiguous over d_in
+ *   b: B in rank octets, [max_rank/8][d_out][8] -- 8 ranks of one column contiguous
+ * rows/octets at and beyond the slot's rank are zero.
+ */
+typedef struct {
+    int32_t n_slots, d_in, d_out, max_rank;
+    int32_t dtype;     /* lora_dtype_t */
+    void *a;           /* DEVICE, lora_pool_bytes(...).a_bytes */
+    void *b;           /* DEVICE, lora_pool_bytes(...).b_bytes */
+    float *scale;      /* DEVICE [n_slots], s = alpha / r (0 for an empty slot) */
+    int32_t *rank;     /* DEVICE [n_slots], true rank, 0 = empty slot */
+} lora_pool_t;
+
+/* Device views of the segment metadata held in a workspace (see
+ * lora_segments_view).  For T rows and n_slots slots, with key = id + 1
+ * (ids outside [-1, n_slots) count as -1):
+ *   offsets   [n_slots + 2]  exclusive prefix sum of per-key row counts
+ *   perm      [T]            rows in (key, original row) order -- a stable sort
+ *   seg_id    [n_slots]      slot of each non-empty adapter segment, ascending
+ *   seg_start [n_slots + 1]  first sorted position of each segment; entry n_seg is T
+ *   n_seg     [1]            number of adapter segments (the -1 block is not one)
+ * ("Serving multiple LoRAs ...": the stable argsort by adapter and the
+ * consecutive-unique counts of the SGMV routine; "LoRAX, in depth":
+ * segment boundaries of length n_segments + 1 and the owner of each). */
+typedef struct {
+    int32_t *offsets, *perm, *seg_id, *seg_start, *n_seg;
+} lora_segments_t;
+
+/* ---- a1: adapter pool ----------------------------------------------------- */
+
+/* Bytes of the caller-allocated pool buffers.  HOST outputs. */
+lora_status_t lora_pool_bytes(int32_t n_slots, int32_t d_in, int32_t d_out, int32_t max_rank,
+                              lora_dtype_t dtype, size_t *a_bytes, size_t *b_bytes);
+
+/* Fill *pool (HOST) with the given DEVICE buffers and zero all slots on
+ * `stream` (every slot starts empty: rank 0, scale 0). */
+lora_status_t lora_pool_create(lora_pool_t *pool, int32_t n_slots, int32_t d_in, int32_t d_out,
+                               int32_t max_rank, lora_dtype_t dtype, void *a, void *b,
+                               float *scale, int32_t *rank, lora_stream_t stream);
+
+/* Copy one adapter into `slot` (activation of an adapter into a slot):
+ *   A: DEVICE [d_in, r] row-major with row stride lda >= r elements,
+ *   B: DEVICE [r, d_out] row-major with row stride ldb >= d_out elements,
+ * both in the pool's dtype.  Ranks r..max_rank-1 of the slot are zeroed,
+ * scale[slot] = alpha / r (computed in fp32), rank[slot] = r.
+ * Errors: LORA_ERR_SLOT_OUT_OF_RANGE, LORA_ERR_RANK_EXCEEDS_MAX (r > max_rank),
+ * LORA_ERR_INVALID_ARGUMENT (r < 1, null, lda < r, ldb < d_out). */
+lora_status_t lora_pool_upload(const lora_pool_t *pool, int32_t slot, const void *A, int32_t lda,
+                               const void *B, int32_t ldb, int32_t r, float alpha,
+                               lora_stream_t stream);
+
+/* Empty one slot: zero its A and B, rank = 0, scale = 0 (the zeroing of an
+ * unused slot in "Serving LoRA adapters ...", Step 3). */
+lora_status_t lora_pool_clear(const lora_pool_t *pool, int32_t slot, lora_stream_t stream);
+
+/* ---- workspace ------------------------------------------------------------- */
+
+/* Bytes of workspace needed for batches of up to T rows against a pool of
+ * n_slots slots and max_rank, for every entry point below.  Returns 0 on
+ * bad arguments. */
+size_t lora_workspace_bytes(int32_t T, int32_t n_slots, int32_t max_rank);
+
+/* Prepare a freshly allocated DEVICE workspace: clears the error word and
+ * the internal counters.  Call once after allocation (it is kept valid by
+ * every later call). */
+lora_status_t lora_workspace_init(void *ws, size_t ws_bytes, lora_stream_t stream);
+
+/* HOST-only pointer arithmetic: device views of the segment metadata that
+ * lora_build_segments writes into `ws` for (T, n_slots, max_rank). */
+lora_status_t lora_segments_view(void *ws, size_t ws_bytes, int32_t T, int32_t n_slots,
+                                 int32_t max_rank, lora_segments_t *out);
+
+/* ---- a2: segment builder ---------------------------------------------------- */
+
+/* Build the segment metadata of DEVICE ids[T] into `ws`: a histogram of keys,
+ * an exclusive prefix sum, a stable scatter of row indices and a compaction
+ * of non-empty adapter segments.  Bad ids are counted as -1 and recorded in
+ * the error word. */
+lora_status_t lora_build_segments(const int32_t *ids, int32_t T, int32_t n_slots, int32_t max_rank,
+                                  void *ws, size_t ws_bytes, lora_stream_t stream);
+
+/* ---- a4: shrink ------------------------------------------------------------- */
+
+/* v[t, 0:r_a] = x[t,:] A_a for rows with a usable adapter a = ids[t]; all
+ * other entries of v[t, 0:max_rank] are zero.
+ *   x: DEVICE [T, d_in] (pool dtype);  v: DEVICE fp32 [T, max_rank].
+ * SGMV requires lora_build_segments on the same ids and ws beforehand. */
+lora_status_t lora_shrink(const void *x, int32_t T, const lora_pool_t *pool, const int32_t *ids,
+                          lora_mode_t mode, float *v, void *ws, size_t ws_bytes,
+                          lora_stream_t stream);
+
+/* ---- a5: expand ------------------------------------------------------------- */
+
+/* y[t,:] += s_a * v[t, 0:r_a] B_a for rows with a usable adapter a = ids[t];
+ * other rows are not touched.  A read-modify-write of y (bf16 y is rounded
+ * once, to nearest even, after the fp32 sum).
+ *   v: DEVICE fp32 [T, max_rank];  y: DEVICE [T, d_out] (pool dtype).
+ * SGMV requires lora_build_segments on the same ids and ws beforehand. */
+lora_status_t lora_expand(const float *v, int32_t T, const lora_pool_t *pool, const int32_t *ids,
+                          lora_mode_t mode, void *y, void *ws, size_t ws_bytes,
+                          lora_stream_t stream);
+
+/* ---- a3: base GEMM ---------------------------------------------------------- */
+
+/* y = x W (no adapters): x DEVICE [T, d_in], W DEVICE [d_in, d_out],
+ * y DEVICE [T, d_out], all of `dtype`; fp32 accumulation, one rounding.
+ * ws may be NULL when ws_bytes is 0. */
+lora_status_t lora_gemm(const void *x, const void *W, void *y, int32_t T, int32_t d_in,
+                        int32_t d_out, lora_dtype_t dtype, void *ws, size_t ws_bytes,
+                        lora_stream_t stream);
+
+/* ---- a3-a8: the whole layer -------------------------------------------------- */
+
+/* y = x W + s_a (x A_a) B_a per row (a = ids[t], -1 = none).
+ * x DEVICE [T, pool->d_in], W DEVICE [d_in, d_out], y DEVICE [T, d_out]
+ * (overwritten), ids DEVICE int32 [T].  `mode` picks BGMV/SGMV (AUTO by T);
+ * in SGMV the segments are built in `ws` unless LORA_FLAG_SEGMENTS_READY says
+ * they already are for these ids (reuse across the projections of one
+ * layer).  By default the expand runs inside the GEMM epilogue (one rounding
+ * of base + delta); LORA_FLAG_SEPARATE_EXPAND runs it as its own pass. */
+lora_status_t lora_linear_forward(const void *x, const void *W, void *y, int32_t T,
+                                  const lora_pool_t *pool, const int32_t *ids, lora_mode_t mode,
+                                  uint32_t flags, void *ws, size_t ws_bytes,
+                                  lora_stream_t stream);
+
+/* ---- errors ------------------------------------------------------------------- */
+
+/* Synchronise `stream`, read the workspace's error word into *first_bad_row
+ * (HOST; -1 if no bad id was seen since the last call) and clear it. */
+lora_status_t lora_get_device_error(void *ws, size_t ws_bytes, lora_stream_t stream,
+                                    int32_t *first_bad_row);
+
+/* Static string for a status code. */
+const char *lora_status_string(lora_status_t status);
+
+/* Library version string, e.g. "liblora 0.1 gfx950". */
+const char *lora_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LORA_H_ */

@@ -1,0 +1,232 @@
+// liblora C ABI: argument validation on the host, then launches on the
+// caller's stream.  No allocation, no hidden state.  The contract of every
+// entry point is stated in include/lora.h.
+#include <string.h>
+
+#include "common.hpp"
+
+using namespace lora;
+
+namespace {
+
+inline hipStream_t hs(lora_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool valid_dtype(int32_t d) { return d == LORA_F32 || d == LORA_BF16; }
+inline size_t dtype_bytes(int32_t d) { return d == LORA_F32 ? 4 : 2; }
+
+inline bool valid_dims(int32_t n_slots, int32_t d_in, int32_t d_out, int32_t max_rank) {
+    return n_slots >= 1 && n_slots <= kMaxSlots && d_in > 0 && d_out > 0 && (d_in % 8) == 0 &&
+           (d_out % 8) == 0 && max_rank >= 8 && max_rank <= 128 && (max_rank % 8) == 0 &&
+           (int64_t)d_in * max_rank < ((int64_t)1 << 31) && (int64_t)d_out * max_rank < ((int64_t)1 << 31);
+}
+
+inline bool valid_pool(const lora_pool_t *p) {
+    return p && valid_dims(p->n_slots, p->d_in, p->d_out, p->max_rank) && valid_dtype(p->dtype) &&
+           p->a && p->b && p->scale && p->rank && aligned16(p->a) && aligned16(p->b);
+}
+
+inline lora_status_t check_ws(const void *ws, size_t ws_bytes, int32_t T, int32_t n_slots,
+                              int32_t max_rank, ws_layout *L) {
+    if (!ws || !aligned16(ws)) return LORA_ERR_INVALID_ARGUMENT;
+    *L = make_ws_layout(T, n_slots, max_rank);
+    if (ws_bytes < L->total) return LORA_ERR_WORKSPACE_TOO_SMALL;
+    return LORA_OK;
+}
+
+inline bool use_sgmv(lora_mode_t mode, int32_t T) {
+    if (mode == LORA_MODE_SGMV) return true;
+    if (mode == LORA_MODE_BGMV) return false;
+    return T >= 1024;
+}
+
+inline bool valid_mode(int32_t m) {
+    return m == LORA_MODE_AUTO || m == LORA_MODE_BGMV || m == LORA_MODE_SGMV;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *lora_version(void) { return "liblora 0.1 gfx950"; }
+
+const char *lora_status_string(lora_status_t s) {
+    switch (s) {
+        case LORA_OK: return "ok";
+        case LORA_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case LORA_ERR_RANK_EXCEEDS_MAX: return "adapter rank exceeds the pool's max_rank";
+        case LORA_ERR_SLOT_OUT_OF_RANGE: return "slot index out of range";
+        case LORA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case LORA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case LORA_ERR_HIP: return "HIP runtime error at launch";
+    }
+    return "unknown status";
+}
+
+lora_status_t lora_pool_bytes(int32_t n_slots, int32_t d_in, int32_t d_out, int32_t max_rank,
+                              lora_dtype_t dtype, size_t *a_bytes, size_t *b_bytes) {
+    if (!a_bytes || !b_bytes || !valid_dtype(dtype)) return LORA_ERR_INVALID_ARGUMENT;
+    if (n_slots > kMaxSlots) return LORA_ERR_UNSUPPORTED;
+    if (!valid_dims(n_slots, d_in, d_out, max_rank)) return LORA_ERR_INVALID_ARGUMENT;
+    const size_t eb = dtype_bytes(dtype);
+    *a_bytes = (size_t)n_slots * max_rank * d_in * eb;
+    *b_bytes = (size_t)n_slots * max_rank * d_out * eb;
+    return LORA_OK;
+}
+
+lora_status_t lora_pool_create(lora_pool_t *pool, int32_t n_slots, int32_t d_in, int32_t d_out,
+                               int32_t max_rank, lora_dtype_t dtype, void *a, void *b,
+                               float *scale, int32_t *rank, lora_stream_t stream) {
+    size_t ab, bb;
+    lora_status_t st = lora_pool_bytes(n_slots, d_in, d_out, max_rank, dtype, &ab, &bb);
+    if (st != LORA_OK) return st;
+    if (!pool || !a || !b || !scale || !rank || !aligned16(a) || !aligned16(b))
+        return LORA_ERR_INVALID_ARGUMENT;
+    lora_pool_t p;
+    p.n_slots = n_slots;
+    p.d_in = d_in;
+    p.d_out = d_out;
+    p.max_rank = max_rank;
+    p.dtype = dtype;
+    p.a = a;
+    p.b = b;
+    p.scale = scale;
+    p.rank = rank;
+    st = launch_pool_fill(a, ab, b, bb, scale, rank, n_slots, hs(stream));
+    if (st == LORA_OK) *pool = p;
+    return st;
+}
+
+lora_status_t lora_pool_upload(const lora_pool_t *pool, int32_t slot, const void *A, int32_t lda,
+                               const void *B, int32_t ldb, int32_t r, float alpha,
+                               lora_stream_t stream) {
+    if (!valid_pool(pool)) return LORA_ERR_INVALID_ARGUMENT;
+    if (slot < 0 || slot >= pool->n_slots) return LORA_ERR_SLOT_OUT_OF_RANGE;
+    if (r > pool->max_rank) return LORA_ERR_RANK_EXCEEDS_MAX;
+    if (r < 1 || !A || !B || lda < r || ldb < pool->d_out) return LORA_ERR_INVALID_ARGUMENT;
+    return launch_pool_upload(*pool, slot, A, lda, B, ldb, r, alpha, hs(stream));
+}
+
+lora_status_t lora_pool_clear(const lora_pool_t *pool, int32_t slot, lora_stream_t stream) {
+    if (!valid_pool(pool)) return LORA_ERR_INVALID_ARGUMENT;
+    if (slot < 0 || slot >= pool->n_slots) return LORA_ERR_SLOT_OUT_OF_RANGE;
+    return launch_pool_clear(*pool, slot, hs(stream));
+}
+
+size_t lora_workspace_bytes(int32_t T, int32_t n_slots, int32_t max_rank) {
+    if (T < 0 || n_slots < 1 || n_slots > kMaxSlots || max_rank < 8 || max_rank > 128 ||
+        (max_rank % 8) != 0)
+        return 0;
+    return make_ws_layout(T, n_slots, max_rank).total;
+}
+
+lora_status_t lora_workspace_init(void *ws, size_t ws_bytes, lora_stream_t stream) {
+    if (!ws || !aligned16(ws) || ws_bytes < 256) return LORA_ERR_INVALID_ARGUMENT;
+    return launch_ws_init(ws, hs(stream));
+}
+
+lora_status_t lora_segments_view(void *ws, size_t ws_bytes, int32_t T, int32_t n_slots,
+                                 int32_t max_rank, lora_segments_t *out) {
+    if (!out || T < 0 || n_slots < 1 || n_slots > kMaxSlots) return LORA_ERR_INVALID_ARGUMENT;
+    ws_layout L;
+    lora_status_t st = check_ws(ws, ws_bytes, T, n_slots, max_rank, &L);
+    if (st != LORA_OK) return st;
+    out->offsets = ws_ptr<int32_t>(ws, L.offsets);
+    out->perm = ws_ptr<int32_t>(ws, L.perm);
+    out->seg_id = ws_ptr<int32_t>(ws, L.seg_id);
+    out->seg_start = ws_ptr<int32_t>(ws, L.seg_start);
+    out->n_seg = ws_ptr<int32_t>(ws, L.n_seg);
+    return LORA_OK;
+}
+
+lora_status_t lora_build_segments(const int32_t *ids, int32_t T, int32_t n_slots, int32_t max_rank,
+                                  void *ws, size_t ws_bytes, lora_stream_t stream) {
+    if (T < 0 || n_slots < 1) return LORA_ERR_INVALID_ARGUMENT;
+    if (n_slots > kMaxSlots) return LORA_ERR_UNSUPPORTED;
+    if (T > 0 && !ids) return LORA_ERR_INVALID_ARGUMENT;
+    ws_layout L;
+    lora_status_t st = check_ws(ws, ws_bytes, T, n_slots, max_rank, &L);
+    if (st != LORA_OK) return st;
+    if (T == 0) return LORA_OK;
+    return launch_segments(ids, T, n_slots, L, ws, hs(stream));
+}
+
+lora_status_t lora_shrink(const void *x, int32_t T, const lora_pool_t *pool, const int32_t *ids,
+                          lora_mode_t mode, float *v, void *ws, size_t ws_bytes,
+                          lora_stream_t stream) {
+    if (!valid_pool(pool) || T < 0 || !valid_mode(mode)) return LORA_ERR_INVALID_ARGUMENT;
+    if (T > 0 && (!x || !ids || !v || !aligned16(x) || !aligned16(v))) return LORA_ERR_INVALID_ARGUMENT;
+    ws_layout L;
+    lora_status_t st = check_ws(ws, ws_bytes, T, pool->n_slots, pool->max_rank, &L);
+    if (st != LORA_OK) return st;
+    if (T == 0) return LORA_OK;
+    return launch_shrink(x, T, *pool, ids, mode == LORA_MODE_SGMV, v, L, ws, hs(stream));
+}
+
+lora_status_t lora_expand(const float *v, int32_t T, const lora_pool_t *pool, const int32_t *ids,
+                          lora_mode_t mode, void *y, void *ws, size_t ws_bytes,
+                          lora_stream_t stream) {
+    if (!valid_pool(pool) || T < 0 || !valid_mode(mode)) return LORA_ERR_INVALID_ARGUMENT;
+    if (T > 0 && (!v || !ids || !y || !aligned16(y))) return LORA_ERR_INVALID_ARGUMENT;
+    ws_layout L;
+    lora_status_t st = check_ws(ws, ws_bytes, T, pool->n_slots, pool->max_rank, &L);
+    if (st != LORA_OK) return st;
+    if (T == 0) return LORA_OK;
+    return launch_expand(v, T, *pool, ids, mode == LORA_MODE_SGMV, y, L, ws, hs(stream));
+}
+
+lora_status_t lora_gemm(const void *x, const void *W, void *y, int32_t T, int32_t d_in,
+                        int32_t d_out, lora_dtype_t dtype, void * /*ws*/, size_t /*ws_bytes*/,
+                        lora_stream_t stream) {
+    if (T < 0 || !valid_dtype(dtype) || d_in <= 0 || d_out <= 0 || (d_in % 8) || (d_out % 8))
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (T > 0 && (!x || !W || !y || !aligned16(x) || !aligned16(W) || !aligned16(y)))
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (T == 0) return LORA_OK;
+    return launch_gemm(x, W, y, T, d_in, d_out, dtype, nullptr, nullptr, nullptr, nullptr, nullptr,
+                       hs(stream));
+}
+
+lora_status_t lora_linear_forward(const void *x, const void *W, void *y, int32_t T,
+                                  const lora_pool_t *pool, const int32_t *ids, lora_mode_t mode,
+                                  uint32_t flags, void *ws, size_t ws_bytes,
+                                  lora_stream_t stream) {
+    if (!valid_pool(pool) || T < 0 || !valid_mode(mode) || (flags & ~3u))
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (T > 0 && (!x || !W || !y || !ids || !aligned16(x) || !aligned16(W) || !aligned16(y)))
+        return LORA_ERR_INVALID_ARGUMENT;
+    ws_layout L;
+    lora_status_t st = check_ws(ws, ws_bytes, T, pool->n_slots, pool->max_rank, &L);
+    if (st != LORA_OK) return st;
+    if (T == 0) return LORA_OK;
+    const hipStream_t s = hs(stream);
+    const bool sgmv = use_sgmv(mode, T);
+    if (sgmv && !(flags & LORA_FLAG_SEGMENTS_READY)) {
+        st = launch_segments(ids, T, pool->n_slots, L, ws, s);
+        if (st != LORA_OK) return st;
+    }
+    float *v = ws_ptr<float>(ws, L.v);
+    st = launch_shrink(x, T, *pool, ids, sgmv, v, L, ws, s);
+    if (st != LORA_OK) return st;
+    const int32_t *perm = sgmv ? ws_ptr<int32_t>(ws, L.perm) : nullptr;
+    if (flags & LORA_FLAG_SEPARATE_EXPAND) {
+        st = launch_gemm(x, W, y, T, pool->d_in, pool->d_out, pool->dtype, nullptr, nullptr,
+                         nullptr, nullptr, nullptr, s);
+        if (st != LORA_OK) return st;
+        return launch_expand(v, T, *pool, ids, sgmv, y, L, ws, s);
+    }
+    return launch_gemm(x, W, y, T, pool->d_in, pool->d_out, pool->dtype, pool, ids, v, perm,
+                       ws_ptr<int32_t>(ws, L.header), s);
+}
+
+lora_status_t lora_get_device_error(void *ws, size_t ws_bytes, lora_stream_t stream,
+                                    int32_t *first_bad_row) {
+    if (!ws || !first_bad_row || ws_bytes < 256 || !aligned16(ws)) return LORA_ERR_INVALID_ARGUMENT;
+    int32_t h = 0;
+    const hipStream_t s = hs(stream);
+    if (hipMemcpyAsync(&h, ws, sizeof h, hipMemcpyDeviceToHost, s) != hipSuccess) return LORA_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return LORA_ERR_HIP;
+    *first_bad_row = (h == kErrNone) ? -1 : h;
+    return launch_ws_init(ws, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+// Shared device/host helpers of liblora (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lora.h"
+
+namespace lora {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32.  bf16 is the upper half of an fp32; widening is exact, and
+// narrowing rounds to nearest with ties to even (NaN stays a quiet NaN).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Element-type traits for the two storage types.
+template <int DT> struct elem;
+template <> struct elem<LORA_F32> {
+    typedef float T;
+    static constexpr int bytes = 4;
+    __device__ static float load(const T *p, int64_t i) { return p[i]; }
+    __device__ static void store(T *p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct elem<LORA_BF16> {
+    typedef uint16_t T;
+    static constexpr int bytes = 2;
+    __device__ static float load(const T *p, int64_t i) { return bf16_to_f32(p[i]); }
+    __device__ static void store(T *p, int64_t i, float v) { p[i] = (uint16_t)f32_to_bf16_bits(v); }
+};
+
+// 16-byte vector of elements: 8 bf16 or 4 fp32, widened to fp32.
+template <int DT> struct vec16;
+template <> struct vec16<LORA_BF16> {
+    static constexpr int n = 8;
+    __device__ static void widen(const uint4 &q, float *f) {
+        f[0] = bf16_lo(q.x); f[1] = bf16_hi(q.x);
+        f[2] = bf16_lo(q.y); f[3] = bf16_hi(q.y);
+        f[4] = bf16_lo(q.z); f[5] = bf16_hi(q.z);
+        f[6] = bf16_lo(q.w); f[7] = bf16_hi(q.w);
+    }
+    __device__ static uint4 narrow(const float *f) {
+        return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                          pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+    }
+};
+template <> struct vec16<LORA_F32> {
+    static constexpr int n = 4;
+    __device__ static void widen(const uint4 &q, float *f) {
+        f[0] = __uint_as_float(q.x); f[1] = __uint_as_float(q.y);
+        f[2] = __uint_as_float(q.z); f[3] = __uint_as_float(q.w);
+    }
+    __device__ static uint4 narrow(const float *f) {
+        return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                          __float_as_uint(f[2]), __float_as_uint(f[3]));
+    }
+};
+
+__device__ __forceinline__ uint4 ldg16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void stg16(void *p, const uint4 &v) { *reinterpret_cast<uint4 *>(p) = v; }
+
+// Row visited at sorted position p: identity without perm; a perm entry
+// outside [0, T) (segments not built for this batch) yields -1 = skip.
+__device__ __forceinline__ int32_t perm_row(const int32_t *perm, int32_t p, int32_t T) {
+    if (!perm) return p;
+    const int32_t t = perm[p];
+    return ((uint32_t)t < (uint32_t)T) ? t : -1;
+}
+
+// Record a bad adapter id (row index) in the workspace error word: the
+// smallest such row wins.  Vector-memory integer atomic.
+__device__ __forceinline__ void flag_bad_row(int32_t *err, int32_t row) {
+    if (err) atomicMin(err, row);
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout (host side).  Regions are 256-byte aligned.
+// ---------------------------------------------------------------------------
+constexpr int32_t kSegTile = 1024;     // rows per segment-builder tile
+constexpr int32_t kMaxKSplit = 16;     // shrink k-split factor bound
+constexpr int32_t kMaxSlots = 16000;   // slots per pool (LDS histogram bound, < 64 KiB)
+constexpr int32_t kErrNone = 0x7fffffff;
+
+struct ws_layout {
+    size_t header;      // int32[64]: [0] error word (first bad row)
+    size_t offsets;     // int32[n_slots + 2]
+    size_t seg_id;      // int32[n_slots]
+    size_t seg_start;   // int32[n_slots + 1]
+    size_t n_seg;       // int32[1]
+    size_t perm;        // int32[T]
+    size_t tile_hist;   // int32[(n_slots + 1) * n_tiles]
+    size_t v;           // fp32[T * max_rank]
+    size_t partial;     // fp32[kMaxKSplit * T * max_rank]
+    size_t total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline ws_layout make_ws_layout(int32_t T, int32_t n_slots, int32_t max_rank) {
+    ws_layout L;
+    size_t o = 0;
+    const size_t t = (size_t)(T > 0 ? T : 1);
+    const size_t n_tiles = (t + kSegTile - 1) / kSegTile;
+    L.header = o;    o = align256(o + 64 * 4);
+    L.offsets = o;   o = align256(o + 4 * (size_t)(n_slots + 2));
+    L.seg_id = o;    o = align256(o + 4 * (size_t)(n_slots + 1));
+    L.seg_start = o; o = align256(o + 4 * (size_t)(n_slots + 2));
+    L.n_seg = o;     o = align256(o + 4);
+    L.perm = o;      o = align256(o + 4 * t);
+    L.tile_hist = o; o = align256(o + 4 * (size_t)(n_slots + 1) * n_tiles);
+    L.v = o;         o = align256(o + 4 * t * (size_t)max_rank);
+    L.partial = o;   o = align256(o + 4 * (size_t)kMaxKSplit * t * (size_t)max_rank);
+    L.total = o;
+    return L;
+}
+
+template <typename T> inline T *ws_ptr(void *ws, size_t off) {
+    return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off);
+}
+
+inline lora_status_t hip_status(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_ERR_HIP; }
+
+// Launchers (one per kernel family), implemented in the matching .hip file.
+lora_status_t launch_pool_fill(void *a, size_t a_bytes, void *b, size_t b_bytes, float *scale,
+                               int32_t *rank, int32_t n_slots, hipStream_t s);
+lora_status_t launch_pool_upload(const lora_pool_t &p, int32_t slot, const void *A, int32_t lda,
+                                 const void *B, int32_t ldb, int32_t r, float alpha, hipStream_t s);
+lora_status_t launch_pool_clear(const lora_pool_t &p, int32_t slot, hipStream_t s);
+lora_status_t launch_ws_init(void *ws, hipStream_t s);
+lora_status_t launch_segments(const int32_t *ids, int32_t T, int32_t n_slots, const ws_layout &L,
+                              void *ws, hipStream_t s);
+lora_status_t launch_shrink(const void *x, int32_t T, const lora_pool_t &p, const int32_t *ids,
+                            bool sgmv, float *v, const ws_layout &L, void *ws, hipStream_t s);
+lora_status_t launch_expand(const float *v, int32_t T, const lora_pool_t &p, const int32_t *ids,
+                            bool sgmv, void *y, const ws_layout &L, void *ws, hipStream_t s);
+// y = x W (+ s v B when pool != nullptr); rows in perm order when perm != nullptr.
+lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int32_t d_in,
+                          int32_t d_out, int32_t dtype, const lora_pool_t *pool,
+                          const int32_t *ids, const float *v, const int32_t *perm,
+                          int32_t *err, hipStream_t s);
+
+}  // namespace lora

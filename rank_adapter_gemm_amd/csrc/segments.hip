@@ -1,0 +1,183 @@
+// a2 -- integer segment builder: histogram -> exclusive prefix sum -> stable
+// scatter of row indices -> compaction of non-empty adapter segments.
+//
+// It produces what the SGMV routine of "Serving multiple LoRAs: segmented
+// matrix multiplies and adapter scheduling" (section "Not merging the
+// weights, computing in batches") obtains with a stable argsort by adapter id
+// and consecutive-unique counts, and what lora_mixed_batch in "LoRAX, in
+// depth" consumes as segment boundaries plus the owner of each segment.  The
+// kernels never move x or y: later kernels index rows through `perm`, the
+// offsets-instead-of-gather idea of "Multi-LoRA Serving 与 Adapter 隔离"
+// (adapter ownership in one continuous batch).
+//
+// Key of row t: ids[t] + 1 (so "no adapter" = key 0 sorts first); ids outside
+// [-1, n_slots) count as key 0 and are flagged in the error word.
+//
+// Three launches, all integer, no floating point:
+//   1. per 1024-row tile, an LDS histogram of keys -> tile_hist[key][tile]
+//   2. one workgroup: exclusive scan of tile_hist in (key, tile) order, so
+//      entry (key, tile) becomes the first output position of that tile's rows
+//      with that key; offsets[], then the compaction of non-empty keys >= 1
+//   3. per tile, each row's rank among the earlier rows of its tile with the
+//      same key (stable), perm[base + rank] = t.
+#include "common.hpp"
+
+namespace lora {
+
+__global__ void k_ws_init(int32_t *header) {
+    const int i = threadIdx.x;
+    if (i < 64) header[i] = (i == 0) ? kErrNone : 0;
+}
+
+__device__ __forceinline__ int32_t row_key(int32_t id, int32_t n_slots) {
+    return (id >= -1 && id < n_slots) ? id + 1 : 0;
+}
+
+__global__ void __launch_bounds__(256) k_seg_hist(const int32_t *__restrict__ ids, int32_t T,
+                                                  int32_t n_slots, int32_t *__restrict__ tile_hist,
+                                                  int32_t n_tiles, int32_t *err) {
+    extern __shared__ int32_t hist[];
+    const int32_t nb = n_slots + 1, tile = blockIdx.x;
+    for (int32_t k = threadIdx.x; k < nb; k += blockDim.x) hist[k] = 0;
+    __syncthreads();
+    const int32_t t0 = tile * kSegTile;
+    const int32_t t1 = min(T, t0 + kSegTile);
+    for (int32_t t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
+        const int32_t id = ids[t];
+        if (!(id >= -1 && id < n_slots)) flag_bad_row(err, t);
+        atomicAdd(&hist[row_key(id, n_slots)], 1);
+    }
+    __syncthreads();
+    for (int32_t k = threadIdx.x; k < nb; k += blockDim.x)
+        tile_hist[(size_t)k * n_tiles + tile] = hist[k];
+}
+
+// Block-wide exclusive scan of one value per thread (1024 threads = 16
+// waves of 64).  Returns the exclusive prefix; *total gets the block sum.
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *s_wave, int32_t *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int32_t inc = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t o = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += o;
+    }
+    if (lane == 63) s_wave[wave] = inc;
+    __syncthreads();
+    if (wave == 0) {
+        const int nw = blockDim.x >> 6;
+        int32_t w = (lane < nw) ? s_wave[lane] : 0;
+        int32_t winc = w;
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) {
+            const int32_t o = __shfl_up(winc, d, 64);
+            if (lane >= d) winc += o;
+        }
+        if (lane < nw) s_wave[16 + lane] = winc - w;   // exclusive wave prefix
+        if (lane == nw - 1) s_wave[32] = winc;
+    }
+    __syncthreads();
+    const int32_t res = s_wave[16 + wave] + inc - v;
+    *total = s_wave[32];
+    __syncthreads();
+    return res;
+}
+
+constexpr int kScanItems = 4;
+
+__global__ void __launch_bounds__(1024) k_seg_scan(int32_t *__restrict__ tile_hist, int32_t n_slots,
+                                                   int32_t n_tiles, int32_t T,
+                                                   int32_t *__restrict__ offsets,
+                                                   int32_t *__restrict__ seg_id,
+                                                   int32_t *__restrict__ seg_start,
+                                                   int32_t *__restrict__ n_seg) {
+    extern __shared__ int32_t s_off[];        // [n_slots + 2]
+    __shared__ int32_t s_wave[48];
+    const int32_t nb = n_slots + 1;
+    const int64_t N = (int64_t)nb * n_tiles;
+    int32_t carry = 0;
+    const int64_t chunk = (int64_t)blockDim.x * kScanItems;
+    for (int64_t c0 = 0; c0 < N; c0 += chunk) {
+        const int64_t e0 = c0 + (int64_t)threadIdx.x * kScanItems;
+        int32_t vals[kScanItems], sum = 0;
+#pragma unroll
+        for (int q = 0; q < kScanItems; ++q) {
+            vals[q] = (e0 + q < N) ? tile_hist[e0 + q] : 0;
+            sum += vals[q];
+        }
+        int32_t tot;
+        int32_t run = block_exclusive_scan(sum, s_wave, &tot) + carry;
+#pragma unroll
+        for (int q = 0; q < kScanItems; ++q) {
+            const int64_t e = e0 + q;
+            if (e < N) {
+                tile_hist[e] = run;
+                if (e % n_tiles == 0) s_off[e / n_tiles] = run;   // first tile of key e / n_tiles
+            }
+            run += vals[q];
+        }
+        carry += tot;
+    }
+    if (threadIdx.x == 0) s_off[nb] = T;
+    __syncthreads();
+    for (int32_t k = threadIdx.x; k <= nb; k += blockDim.x) offsets[k] = s_off[k];
+
+    // Compaction of non-empty adapter keys (k >= 1) in ascending order.
+    int32_t seg_carry = 0;
+    for (int32_t k0 = 1; k0 < nb; k0 += blockDim.x) {
+        const int32_t k = k0 + threadIdx.x;
+        const int32_t nonempty = (k < nb) ? (s_off[k + 1] > s_off[k]) : 0;
+        int32_t tot;
+        const int32_t idx = block_exclusive_scan(nonempty, s_wave, &tot) + seg_carry;
+        if (nonempty) {
+            seg_id[idx] = k - 1;
+            seg_start[idx] = s_off[k];
+        }
+        seg_carry += tot;
+    }
+    if (threadIdx.x == 0) {
+        seg_start[seg_carry] = T;
+        *n_seg = seg_carry;
+    }
+}
+
+__global__ void __launch_bounds__(1024) k_seg_scatter(const int32_t *__restrict__ ids, int32_t T,
+                                                      int32_t n_slots,
+                                                      const int32_t *__restrict__ tile_hist,
+                                                      int32_t n_tiles, int32_t *__restrict__ perm) {
+    __shared__ int32_t keys[kSegTile];
+    const int32_t tile = blockIdx.x, i = threadIdx.x;
+    const int32_t t = tile * kSegTile + i;
+    const int32_t key = (t < T) ? row_key(ids[t], n_slots) : -1;
+    keys[i] = key;
+    __syncthreads();
+    if (t >= T) return;
+    // Stable rank: earlier rows of this tile with the same key.
+    int32_t rank = 0;
+    for (int32_t j = 0; j < i; ++j) rank += (keys[j] == key);
+    perm[tile_hist[(size_t)key * n_tiles + tile] + rank] = t;
+}
+
+lora_status_t launch_ws_init(void *ws, hipStream_t s) {
+    hipLaunchKernelGGL(k_ws_init, dim3(1), dim3(64), 0, s, ws_ptr<int32_t>(ws, 0));
+    return hip_status(hipGetLastError());
+}
+
+lora_status_t launch_segments(const int32_t *ids, int32_t T, int32_t n_slots, const ws_layout &L,
+                              void *ws, hipStream_t s) {
+    const int32_t n_tiles = (T + kSegTile - 1) / kSegTile;
+    int32_t *err = ws_ptr<int32_t>(ws, L.header);
+    int32_t *tile_hist = ws_ptr<int32_t>(ws, L.tile_hist);
+    const size_t lds_hist = sizeof(int32_t) * (size_t)(n_slots + 1);
+    const size_t lds_off = sizeof(int32_t) * (size_t)(n_slots + 2);
+    hipLaunchKernelGGL(k_seg_hist, dim3(n_tiles), dim3(256), lds_hist, s, ids, T, n_slots,
+                       tile_hist, n_tiles, err);
+    hipLaunchKernelGGL(k_seg_scan, dim3(1), dim3(1024), lds_off, s, tile_hist, n_slots, n_tiles, T,
+                       ws_ptr<int32_t>(ws, L.offsets), ws_ptr<int32_t>(ws, L.seg_id),
+                       ws_ptr<int32_t>(ws, L.seg_start), ws_ptr<int32_t>(ws, L.n_seg));
+    hipLaunchKernelGGL(k_seg_scatter, dim3(n_tiles), dim3(kSegTile), 0, s, ids, T, n_slots,
+                       tile_hist, n_tiles, ws_ptr<int32_t>(ws, L.perm));
+    return hip_status(hipGetLastError());
+}
+
+}  // namespace lora

@@ -1,0 +1,283 @@
+"""Python binding of liblora: the C ABI of include/lora.h, same names.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+liblora.so.  torch is used for device memory and the current stream.  There
+is no fallback: if the library cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblora.so")
+
+LORA_OK = 0
+LORA_ERR_INVALID_ARGUMENT = 1
+LORA_ERR_RANK_EXCEEDS_MAX = 2
+LORA_ERR_SLOT_OUT_OF_RANGE = 3
+LORA_ERR_WORKSPACE_TOO_SMALL = 4
+LORA_ERR_UNSUPPORTED = 5
+LORA_ERR_HIP = 6
+
+LORA_F32 = 0
+LORA_BF16 = 1
+
+LORA_MODE_AUTO = 0
+LORA_MODE_BGMV = 1
+LORA_MODE_SGMV = 2
+
+LORA_FLAG_SEGMENTS_READY = 0x1
+LORA_FLAG_SEPARATE_EXPAND = 0x2
+
+# Every symbol include/lora.h declares.
+EXPORTED = (
+    "lora_pool_bytes", "lora_pool_create", "lora_pool_upload", "lora_pool_clear",
+    "lora_workspace_bytes", "lora_workspace_init", "lora_segments_view", "lora_build_segments",
+    "lora_shrink", "lora_expand", "lora_gemm", "lora_linear_forward", "lora_get_device_error",
+    "lora_status_string", "lora_version",
+)
+
+
+class LoraError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
+
+
+class lora_pool_t(ctypes.Structure):
+    _fields_ = [("n_slots", ctypes.c_int32), ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32),
+                ("max_rank", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("a", ctypes.c_void_p), ("b", ctypes.c_void_p),
+                ("scale", ctypes.c_void_p), ("rank", ctypes.c_void_p)]
+
+
+class lora_segments_t(ctypes.Structure):
+    _fields_ = [("offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p), ("seg_id", ctypes.c_void_p),
+                ("seg_start", ctypes.c_void_p), ("n_seg", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def _check_single_hip_runtime():
+    """liblora must bind to the HIP runtime torch already loaded: two runtimes
+    in one process would not share streams or pointers."""
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64.so" in line:
+                    paths.add(line.split()[-1])
+    except OSError:
+        return
+    if len(paths) > 1:
+        raise RuntimeError("more than one HIP runtime is mapped: %s" % sorted(paths))
+
+
+def load(path: str = LIB_PATH):
+    """Load liblora.so (after torch, so its HIP runtime is the one bound)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("liblora.so is not built (%s): run `python -m rank_adapter_gemm_amd.build`"
+                           % path)
+    lib = ctypes.CDLL(path)
+    _check_single_hip_runtime()
+    c_i32, c_sz, c_vp, c_u32, c_f = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_float
+    P = ctypes.POINTER
+    sig = {
+        "lora_pool_bytes": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, P(c_sz), P(c_sz)]),
+        "lora_pool_create": (c_i32, [P(lora_pool_t), c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
+        "lora_pool_upload": (c_i32, [P(lora_pool_t), c_i32, c_vp, c_i32, c_vp, c_i32, c_i32, c_f, c_vp]),
+        "lora_pool_clear": (c_i32, [P(lora_pool_t), c_i32, c_vp]),
+        "lora_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32]),
+        "lora_workspace_init": (c_i32, [c_vp, c_sz, c_vp]),
+        "lora_segments_view": (c_i32, [c_vp, c_sz, c_i32, c_i32, c_i32, P(lora_segments_t)]),
+        "lora_build_segments": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_vp, c_sz, c_vp]),
+        "lora_shrink": (c_i32, [c_vp, c_i32, P(lora_pool_t), c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
+        "lora_expand": (c_i32, [c_vp, c_i32, P(lora_pool_t), c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
+        "lora_gemm": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_sz, c_vp]),
+        "lora_linear_forward": (c_i32, [c_vp, c_vp, c_vp, c_i32, P(lora_pool_t), c_vp, c_i32, c_u32, c_vp, c_sz, c_vp]),
+        "lora_get_device_error": (c_i32, [c_vp, c_sz, c_vp, P(c_i32)]),
+        "lora_status_string": (ctypes.c_char_p, [c_i32]),
+        "lora_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().lora_status_string(int(status)).decode()
+
+
+def _ok(status: int, where: str):
+    if status != LORA_OK:
+        raise LoraError(status, where)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return LORA_F32
+    if dt == torch.bfloat16:
+        return LORA_BF16
+    raise TypeError("liblora supports float32 and bfloat16, not %s" % dt)
+
+
+# ---- a1: pool ---------------------------------------------------------------
+def lora_pool_bytes(n_slots, d_in, d_out, max_rank, dtype):
+    a = ctypes.c_size_t()
+    b = ctypes.c_size_t()
+    _ok(load().lora_pool_bytes(n_slots, d_in, d_out, max_rank, dtype, ctypes.byref(a), ctypes.byref(b)),
+        "lora_pool_bytes")
+    return a.value, b.value
+
+
+def lora_pool_create(n_slots, d_in, d_out, max_rank, dtype, a, b, scale, rank, stream=None):
+    pool = lora_pool_t()
+    _ok(load().lora_pool_create(ctypes.byref(pool), n_slots, d_in, d_out, max_rank, dtype, _ptr(a),
+                                _ptr(b), _ptr(scale), _ptr(rank), _stream(stream)), "lora_pool_create")
+    return pool
+
+
+def lora_pool_upload(pool, slot, A, B, r, alpha, lda=None, ldb=None, stream=None):
+    lda = r if lda is None else lda
+    ldb = pool.d_out if ldb is None else ldb
+    _ok(load().lora_pool_upload(ctypes.byref(pool), slot, _ptr(A), lda, _ptr(B), ldb, r, float(alpha),
+                                _stream(stream)), "lora_pool_upload")
+
+
+def lora_pool_clear(pool, slot, stream=None):
+    _ok(load().lora_pool_clear(ctypes.byref(pool), slot, _stream(stream)), "lora_pool_clear")
+
+
+# ---- workspace / segments -----------------------------------------------------
+def lora_workspace_bytes(T, n_slots, max_rank) -> int:
+    return int(load().lora_workspace_bytes(T, n_slots, max_rank))
+
+
+def lora_workspace_init(ws, stream=None):
+    _ok(load().lora_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+        "lora_workspace_init")
+
+
+def lora_segments_view(ws, T, n_slots, max_rank):
+    seg = lora_segments_t()
+    _ok(load().lora_segments_view(_ptr(ws), ws.numel() * ws.element_size(), T, n_slots, max_rank,
+                                  ctypes.byref(seg)), "lora_segments_view")
+    return seg
+
+
+def lora_build_segments(ids, T, n_slots, max_rank, ws, stream=None):
+    _ok(load().lora_build_segments(_ptr(ids), T, n_slots, max_rank, _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)), "lora_build_segments")
+
+
+# ---- a4 / a5 / a3 / whole layer ---------------------------------------------------
+def lora_shrink(x, T, pool, ids, mode, v, ws, stream=None):
+    _ok(load().lora_shrink(_ptr(x), T, ctypes.byref(pool), _ptr(ids), mode, _ptr(v), _ptr(ws),
+                           ws.numel() * ws.element_size(), _stream(stream)), "lora_shrink")
+
+
+def lora_expand(v, T, pool, ids, mode, y, ws, stream=None):
+    _ok(load().lora_expand(_ptr(v), T, ctypes.byref(pool), _ptr(ids), mode, _ptr(y), _ptr(ws),
+                           ws.numel() * ws.element_size(), _stream(stream)), "lora_expand")
+
+
+def lora_gemm(x, W, y, T, d_in, d_out, dtype, stream=None):
+    _ok(load().lora_gemm(_ptr(x), _ptr(W), _ptr(y), T, d_in, d_out, dtype, None, 0, _stream(stream)),
+        "lora_gemm")
+
+
+def lora_linear_forward(x, W, y, T, pool, ids, mode, flags, ws, stream=None):
+    _ok(load().lora_linear_forward(_ptr(x), _ptr(W), _ptr(y), T, ctypes.byref(pool), _ptr(ids), mode,
+                                   flags, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+        "lora_linear_forward")
+
+
+def lora_get_device_error(ws, stream=None) -> int:
+    row = ctypes.c_int32()
+    _ok(load().lora_get_device_error(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream),
+                                     ctypes.byref(row)), "lora_get_device_error")
+    return row.value
+
+
+def lora_version() -> str:
+    return load().lora_version().decode()
+
+
+# ---- plumbing: device buffers held by torch ------------------------------------------
+class AdapterPool:
+    """Owns the torch device buffers of one pool and its lora_pool_t."""
+
+    def __init__(self, n_slots, d_in, d_out, max_rank, dtype: torch.dtype, device="cuda", stream=None):
+        code = dtype_code(dtype)
+        a_bytes, b_bytes = lora_pool_bytes(n_slots, d_in, d_out, max_rank, code)
+        self.a = torch.empty(a_bytes, dtype=torch.uint8, device=device)
+        self.b = torch.empty(b_bytes, dtype=torch.uint8, device=device)
+        self.scale = torch.empty(n_slots, dtype=torch.float32, device=device)
+        self.rank = torch.empty(n_slots, dtype=torch.int32, device=device)
+        self.dtype = dtype
+        self.pool = lora_pool_create(n_slots, d_in, d_out, max_rank, code, self.a, self.b,
+                                     self.scale, self.rank, stream)
+
+    def upload(self, slot, A, B, r, alpha, lda=None, ldb=None, stream=None):
+        lora_pool_upload(self.pool, slot, A, B, r, alpha, lda, ldb, stream)
+
+    def clear(self, slot, stream=None):
+        lora_pool_clear(self.pool, slot, stream)
+
+    @property
+    def nbytes(self):
+        return self.a.numel() + self.b.numel() + 8 * self.scale.numel()
+
+
+class Workspace:
+    """A device workspace sized for (T, n_slots, max_rank), initialised."""
+
+    def __init__(self, T, n_slots, max_rank, device="cuda", stream=None):
+        n = lora_workspace_bytes(T, n_slots, max_rank)
+        if n == 0:
+            raise LoraError(LORA_ERR_INVALID_ARGUMENT, "lora_workspace_bytes")
+        self.T, self.n_slots, self.max_rank = T, n_slots, max_rank
+        self.buf = torch.empty(n, dtype=torch.uint8, device=device)
+        lora_workspace_init(self.buf, stream)
+
+    def segments(self, T=None):
+        """int32 tensor views of the segment metadata inside the workspace."""
+        T = self.T if T is None else T
+        seg = lora_segments_view(self.buf, T, self.n_slots, self.max_rank)
+        base = self.buf.data_ptr()
+
+        def view(ptr, n):
+            off = ptr - base
+            return self.buf[off:off + 4 * n].view(torch.int32)
+
+        return {"offsets": view(seg.offsets, self.n_slots + 2), "perm": view(seg.perm, T),
+                "seg_id": view(seg.seg_id, self.n_slots), "seg_start": view(seg.seg_start, self.n_slots + 1),
+                "n_seg": view(seg.n_seg, 1)}

@@ -1,0 +1,122 @@
+"""CPU checks of the C-ABI library: it loads, exports every function that
+include/lora.h declares, and its host-side validation and size arithmetic
+behave as documented.  No GPU work is launched here (every call below
+returns before anything is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rank_adapter_gemm_amd import lora as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "lora.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lora_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) >= 15
+    assert sorted(L.EXPORTED) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert "gfx950" in L.lora_version()
+    for code in range(7):
+        assert L.status_string(code) and L.status_string(code) != "unknown status"
+    assert L.status_string(99) == "unknown status"
+
+
+def test_pool_bytes():
+    a, b = L.lora_pool_bytes(128, 4096, 4096, 16, L.LORA_BF16)
+    assert a == 128 * 16 * 4096 * 2 and b == 128 * 16 * 4096 * 2
+    a, b = L.lora_pool_bytes(4, 256, 256, 8, L.LORA_F32)
+    assert a == b == 4 * 8 * 256 * 4
+    for bad in [(0, 64, 64, 8), (4, 60, 64, 8), (4, 64, 60, 8), (4, 64, 64, 12), (4, 64, 64, 136),
+                (4, 64, 64, 0)]:
+        with pytest.raises(L.LoraError) as e:
+            L.lora_pool_bytes(*bad, L.LORA_BF16)
+        assert e.value.status == L.LORA_ERR_INVALID_ARGUMENT
+    with pytest.raises(L.LoraError) as e:
+        L.lora_pool_bytes(16001, 64, 64, 8, L.LORA_BF16)
+    assert e.value.status == L.LORA_ERR_UNSUPPORTED
+    with pytest.raises(L.LoraError):
+        L.lora_pool_bytes(4, 64, 64, 8, 7)
+
+
+def test_workspace_bytes():
+    assert L.lora_workspace_bytes(-1, 4, 8) == 0
+    assert L.lora_workspace_bytes(10, 0, 8) == 0
+    assert L.lora_workspace_bytes(10, 4, 7) == 0
+    n0 = L.lora_workspace_bytes(0, 4, 8)
+    n1 = L.lora_workspace_bytes(1000, 4, 8)
+    n2 = L.lora_workspace_bytes(100000, 4, 8)
+    assert 0 < n0 < n1 < n2
+    # holds at least v [T, max_rank] fp32, perm [T] and the k-split partials
+    assert n2 >= 100000 * (8 * 4 + 4 + 16 * 8 * 4)
+    assert n2 % 256 == 0
+
+
+def test_validation_returns_before_launch(lib):
+    pool = L.lora_pool_t()
+    # a null pool descriptor / zeroed descriptor is rejected
+    assert lib.lora_pool_upload(None, 0, None, 1, None, 1, 1, 1.0, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert lib.lora_pool_upload(ctypes.byref(pool), 0, None, 1, None, 1, 1, 1.0, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert lib.lora_pool_clear(ctypes.byref(pool), 0, None) == L.LORA_ERR_INVALID_ARGUMENT
+    # fake, aligned, never-dereferenced device addresses: validation only
+    fake = 1 << 40
+    ok = L.lora_pool_t(4, 64, 64, 8, L.LORA_BF16, fake, fake, fake, fake)
+    assert lib.lora_pool_upload(ctypes.byref(ok), 4, fake, 8, fake, 64, 8, 1.0, None) == L.LORA_ERR_SLOT_OUT_OF_RANGE
+    assert lib.lora_pool_upload(ctypes.byref(ok), -1, fake, 8, fake, 64, 8, 1.0, None) == L.LORA_ERR_SLOT_OUT_OF_RANGE
+    assert lib.lora_pool_upload(ctypes.byref(ok), 0, fake, 9, fake, 64, 9, 1.0, None) == L.LORA_ERR_RANK_EXCEEDS_MAX
+    assert lib.lora_pool_upload(ctypes.byref(ok), 0, fake, 2, fake, 64, 0, 1.0, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert lib.lora_pool_upload(ctypes.byref(ok), 0, fake, 2, fake, 63, 2, 1.0, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert lib.lora_pool_upload(ctypes.byref(ok), 0, fake, 1, fake, 64, 2, 1.0, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert lib.lora_pool_clear(ctypes.byref(ok), 4, None) == L.LORA_ERR_SLOT_OUT_OF_RANGE
+    ws_need = L.lora_workspace_bytes(16, 4, 8)
+    f = lib.lora_linear_forward
+    assert f(fake, fake, fake, 16, ctypes.byref(ok), fake, 0, 0, fake, ws_need - 1, None) == L.LORA_ERR_WORKSPACE_TOO_SMALL
+    assert f(fake, fake, fake, -1, ctypes.byref(ok), fake, 0, 0, fake, ws_need, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert f(fake + 2, fake, fake, 16, ctypes.byref(ok), fake, 0, 0, fake, ws_need, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert f(fake, fake, fake, 16, ctypes.byref(ok), None, 0, 0, fake, ws_need, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert f(fake, fake, fake, 16, ctypes.byref(ok), fake, 3, 0, fake, ws_need, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert f(fake, fake, fake, 16, ctypes.byref(ok), fake, 0, 4, fake, ws_need, None) == L.LORA_ERR_INVALID_ARGUMENT
+    # T == 0 is a no-op that returns OK without touching anything
+    assert f(None, None, None, 0, ctypes.byref(ok), None, 0, 0, fake, ws_need, None) == L.LORA_OK
+    assert lib.lora_shrink(None, 0, ctypes.byref(ok), None, 0, None, fake, ws_need, None) == L.LORA_OK
+    assert lib.lora_expand(None, 0, ctypes.byref(ok), None, 0, None, fake, ws_need, None) == L.LORA_OK
+    assert lib.lora_build_segments(None, 0, 4, 8, fake, ws_need, None) == L.LORA_OK
+    assert lib.lora_build_segments(fake, 16, 16001, 8, fake, ws_need, None) == L.LORA_ERR_UNSUPPORTED
+    g = lib.lora_gemm
+    assert g(fake, fake, fake, 4, 60, 64, L.LORA_BF16, None, 0, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert g(fake, fake, fake, 4, 64, 64, 5, None, 0, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert g(None, None, None, 0, 64, 64, L.LORA_BF16, None, 0, None) == L.LORA_OK
+    row = ctypes.c_int32()
+    assert lib.lora_get_device_error(None, 256, None, ctypes.byref(row)) == L.LORA_ERR_INVALID_ARGUMENT
+
+
+def test_segments_view_is_pointer_arithmetic(lib):
+    fake = 1 << 40
+    need = L.lora_workspace_bytes(100, 10, 8)
+    seg = L.lora_segments_t()
+    assert lib.lora_segments_view(fake, need, 100, 10, 8, ctypes.byref(seg)) == L.LORA_OK
+    ptrs = [seg.offsets, seg.perm, seg.seg_id, seg.seg_start, seg.n_seg]
+    assert all(fake <= p < fake + need for p in ptrs)
+    assert len(set(ptrs)) == 5 and all(p % 16 == 0 for p in ptrs)
+    # segment regions do not depend on max_rank (reuse across pools)
+    seg2 = L.lora_segments_t()
+    assert lib.lora_segments_view(fake, L.lora_workspace_bytes(100, 10, 64), 100, 10, 64,
+                                  ctypes.byref(seg2)) == L.LORA_OK
+    assert seg2.perm == seg.perm and seg2.offsets == seg.offsets

@@ -1,0 +1,155 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs, element by element.
+
+Small cases cover every row; the full-size workloads are checked on a
+bounded, seeded row sample (every adapter run's first and last row, rows per
+adapter, base rows, random rows) in the launch configuration the benchmark
+times.  Segment metadata is compared bit for bit at every size."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle_segments
+from rank_adapter_gemm_amd import lora as L
+from rank_adapter_gemm_amd.workloads import make_workload, sample_rows
+
+from helpers import DELTA_TOL, assert_parity, build_pool, forward, oracle_for, rel_err
+
+pytestmark = pytest.mark.gpu
+
+MODES = {"bgmv": L.LORA_MODE_BGMV, "sgmv": L.LORA_MODE_SGMV, "auto": L.LORA_MODE_AUTO}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.load()
+
+
+def _seg_check(ids_np, n_slots, max_rank=16):
+    T = len(ids_np)
+    ws = L.Workspace(max(T, 1), n_slots, max_rank)
+    ids = torch.as_tensor(np.asarray(ids_np, np.int32), device="cuda")
+    L.lora_build_segments(ids, T, n_slots, max_rank, ws.buf)
+    got = ws.segments(T)
+    ref = oracle_segments(ids_np, n_slots)
+    n = int(got["n_seg"].cpu()[0])
+    assert n == ref["n_seg"]
+    assert np.array_equal(got["offsets"].cpu().numpy(), ref["offsets"])
+    assert np.array_equal(got["perm"].cpu().numpy(), ref["perm"])
+    assert np.array_equal(got["seg_id"].cpu().numpy()[:n], ref["seg_id"])
+    assert np.array_equal(got["seg_start"].cpu().numpy()[: n + 1], ref["seg_start"])
+    bad = [i for i, v in enumerate(ids_np) if not (-1 <= v < n_slots)]
+    assert L.lora_get_device_error(ws.buf) == (min(bad) if bad else -1)
+
+
+def test_segments_examples_and_random():
+    # the BGMV/SGMV example's mixed batch and the grouped experiment's batch
+    lengths, adapters = [1, 1, 37, 1, 12, 1], [3, 5, 3, 0, 7, 5]
+    _seg_check([a for a, n in zip(adapters, lengths) for _ in range(n)], 8)
+    _seg_check([1, -1, 0, 1, 0, -1], 2)
+    rng = np.random.default_rng(0)
+    for T, n_slots in [(1, 1), (7, 3), (1023, 5), (1024, 5), (1025, 5), (3000, 1000),
+                       (5000, 16000), (70000, 32), (2240, 1000)]:
+        ids = rng.integers(-1, n_slots, size=T).astype(np.int32)
+        _seg_check(ids, n_slots)
+    _seg_check(np.full(2000, -1, np.int32), 7)
+    _seg_check(np.full(2000, 3, np.int32), 7)
+    ids = rng.integers(-1, 10, size=3000).astype(np.int32)
+    ids[[5, 17, 2999]] = [-3, 10, 99]
+    _seg_check(ids, 10)
+
+
+def test_tiny_fp32_every_mode():
+    wl = make_workload("tiny_fp32", device="cuda")
+    proj = wl.projections[0]
+    pool = build_pool(wl, proj)
+    ids = torch.as_tensor(wl.ids, device="cuda")
+    rows = np.arange(wl.T)
+    ref = oracle_for(wl, proj, rows, want_u=True, want_delta=True)
+    for mname, mode in MODES.items():
+        for flags in (0, L.LORA_FLAG_SEPARATE_EXPAND):
+            y, ws = forward(wl, proj, pool, ids, mode, flags)
+            torch.cuda.synchronize()
+            assert_parity(y, ref["y"], wl.dtype, "tiny_fp32 %s flags=%d" % (mname, flags))
+            assert L.lora_get_device_error(ws.buf) == -1
+    _check_shrink_expand(wl, proj, pool, ids, rows, ref)
+
+
+def _check_shrink_expand(wl, proj, pool, ids, rows, ref):
+    """v against the oracle's u, and the low-rank term alone against the
+    oracle's s * delta (the delta-sensitive check)."""
+    x = wl.x_for(proj)
+    scales = np.asarray([a / r if r else 0.0 for a, r in zip(wl.alphas, wl.ranks)])
+    sref = np.asarray([scales[wl.ids[t]] if wl.ids[t] >= 0 else 0.0 for t in rows])[:, None]
+    dref = ref["delta"] * sref
+    for mname in ("bgmv", "sgmv"):
+        ws = L.Workspace(wl.T, wl.n_slots, wl.max_rank)
+        if mname == "sgmv":
+            L.lora_build_segments(ids, wl.T, wl.n_slots, wl.max_rank, ws.buf)
+        v = torch.full((wl.T, wl.max_rank), float("nan"), dtype=torch.float32, device="cuda")
+        L.lora_shrink(x, wl.T, pool.pool, ids, MODES[mname], v, ws.buf)
+        y = torch.zeros(wl.T, proj.d_out, dtype=wl.dtype, device="cuda")
+        L.lora_expand(v, wl.T, pool.pool, ids, MODES[mname], y, ws.buf)
+        torch.cuda.synchronize()
+        vg = v.cpu().double().numpy()[rows]
+        u = ref["u"]
+        assert np.isfinite(vg).all()
+        ev = np.max(np.abs(vg - u)) / (1.0 + np.max(np.abs(u)))
+        assert ev <= 1e-4, "shrink %s: %.3e" % (mname, ev)
+        yg = y.float().cpu().double().numpy()[rows]
+        ed = np.max(np.abs(yg - dref))
+        bound = DELTA_TOL[wl.dtype] * max(np.max(np.abs(dref)), 1e-30)
+        assert ed <= bound, "expand %s: %.3e > %.3e" % (mname, ed, bound)
+
+
+def test_decode_bgmv_every_row():
+    wl = make_workload("decode_bgmv", device="cuda")
+    proj = wl.projections[0]
+    pool = build_pool(wl, proj)
+    ids = torch.as_tensor(wl.ids, device="cuda")
+    rows = np.arange(wl.T)
+    ref = oracle_for(wl, proj, rows, want_u=True, want_delta=True)
+    outs = {}
+    for mname, mode in MODES.items():
+        for flags in (0, L.LORA_FLAG_SEPARATE_EXPAND):
+            y, _ = forward(wl, proj, pool, ids, mode, flags)
+            torch.cuda.synchronize()
+            assert_parity(y, ref["y"], wl.dtype, "decode_bgmv %s flags=%d" % (mname, flags))
+            outs[(mname, flags)] = y
+    _check_shrink_expand(wl, proj, pool, ids, rows, ref)
+
+
+def test_prefill_sgmv_sampled():
+    wl = make_workload("prefill_sgmv", device="cuda")
+    proj = wl.projections[0]
+    pool = build_pool(wl, proj)
+    ids = torch.as_tensor(wl.ids, device="cuda")
+    _seg_check(wl.ids, wl.n_slots, wl.max_rank)
+    rows = sample_rows(wl, max_rows=160)
+    ref = oracle_for(wl, proj, rows)
+    for flags in (0, L.LORA_FLAG_SEPARATE_EXPAND):
+        y, _ = forward(wl, proj, pool, ids, L.LORA_MODE_AUTO, flags)
+        torch.cuda.synchronize()
+        assert_parity(y[torch.as_tensor(rows, device="cuda")], ref["y"], wl.dtype,
+                      "prefill_sgmv flags=%d" % flags)
+
+
+@pytest.mark.parametrize("name,max_rows", [("layer_8b", 160), ("stress_70b", 80)])
+def test_layer_sets_sampled(name, max_rows):
+    """Every projection of the layer set, segments built once and reused."""
+    wl = make_workload(name, device="cuda")
+    ids = torch.as_tensor(wl.ids, device="cuda")
+    rows = sample_rows(wl, max_rows=max_rows)
+    ws = L.Workspace(wl.T, wl.n_slots, wl.max_rank)
+    rows_dev = torch.as_tensor(rows, device="cuda")
+    for k, proj in enumerate(wl.projections):
+        pool = build_pool(wl, proj)
+        flags = L.LORA_FLAG_SEGMENTS_READY if k > 0 else 0
+        y, _ = forward(wl, proj, pool, ids, L.LORA_MODE_AUTO, flags, ws=ws)
+        torch.cuda.synchronize()
+        ref = oracle_for(wl, proj, rows)
+        assert_parity(y[rows_dev], ref["y"], wl.dtype, "%s %s" % (name, proj.name))
+        del pool
+    assert L.lora_get_device_error(ws.buf) == -1
