@@ -1,0 +1,382 @@
+"""Benchmark of the mixed-adapter LoRA layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_bgmv]
+
+One step = one pass of the whole layer over one batch: every projection of
+the workload through lora_linear_forward (segments built once per batch and
+reused across projections in SGMV mode).  The timed region holds exactly K
+steps bracketed by device synchronisations; inputs are resident in HBM.
+Workloads whose working set fits in the 256 MB Infinity Cache rotate through
+several copies of (x, W, pool, y) so every step reads HBM.
+
+Prints ONE JSON line: tokens/s of the whole step, plus
+  roofline:     the dominant kernel's algorithmic bytes (or flops) per launch
+                over its average duration, measured with HIP events on the
+                stream it runs on, against the MI355X peak;
+  cpu_baseline: the fp64 CPU oracle on a bounded row sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("mixed-adapter LoRA-layer tokens/s; shrink/expand HBM GB/s and base-GEMM MFMA % of peak")
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16 MFMA
+FP32_VALU_PEAK_TFS = 157.3     # fp32 vector
+RIDGE = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
+MALL_BYTES = 256 * 2 ** 20
+CSRC = os.path.join(ROOT, "rank_adapter_gemm_amd", "csrc")
+KERNEL_SOURCE = {"gemm_expand": "gemm.hip", "shrink": "shrink.hip", "segments": "segments.hip",
+                 "expand": "expand.hip"}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode_bgmv")
+    ap.add_argument("--mode", default="auto", choices=["auto", "bgmv", "sgmv"])
+    ap.add_argument("--separate-expand", action="store_true")
+    ap.add_argument("--cold-sets", type=int, default=None, help="copies of the working set to rotate")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU work of the oracle sample")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain fp32 copy kernel of known size (for counter scaling)")
+    return ap.parse_args()
+
+
+def source_sha(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCE[kernel], "common.hpp"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer is built and measured on a single "
+              "MI355X (rows are independent; see the sharding notes in the design document). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from rank_adapter_gemm_amd import lora as L
+    from rank_adapter_gemm_amd.workloads import make_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    L.load()
+    dev = "cuda"
+    wl = make_workload(args.workload, device=dev)
+    mode = {"auto": L.LORA_MODE_AUTO, "bgmv": L.LORA_MODE_BGMV, "sgmv": L.LORA_MODE_SGMV}[args.mode]
+    sgmv = mode == L.LORA_MODE_SGMV or (mode == L.LORA_MODE_AUTO and wl.T >= 1024)
+    eb = 4 if wl.dtype == torch.float32 else 2
+    T, R = wl.T, wl.max_rank
+    ids = torch.as_tensor(wl.ids, device=dev)
+
+    # ---- pools (one per projection) ----
+    pools = []
+    for pr in wl.projections:
+        pool = L.AdapterPool(wl.n_slots, pr.d_in, pr.d_out, R, wl.dtype, device=dev)
+        for s in range(wl.n_slots):
+            r = int(wl.ranks[s])
+            if r > 0:
+                pool.upload(s, pr.A[s], pr.B[s], r, float(wl.alphas[s]), lda=R, ldb=pr.d_out)
+        pools.append(pool)
+    torch.cuda.synchronize()
+    for pr in wl.projections:          # the host-side sources are no longer needed
+        pr.A = pr.B = None
+
+    # ---- working-set copies for cache-cold timing ----
+    set_bytes = sum(p.W.numel() * eb + pl.nbytes + T * p.d_out * eb for p, pl in zip(wl.projections, pools))
+    set_bytes += sum(x.numel() * eb for x in wl.xs.values())
+    n_sets = args.cold_sets
+    if n_sets is None:
+        n_sets = 1 if set_bytes >= 2 * MALL_BYTES else min(16, math.ceil(2 * MALL_BYTES / set_bytes))
+    sets = []
+    for k in range(n_sets):
+        if k == 0:
+            xs = wl.xs
+            Ws = [p.W for p in wl.projections]
+            ps = [pl.pool for pl in pools]
+            keep = []
+        else:
+            xs = {g: x.clone() for g, x in wl.xs.items()}
+            Ws = [p.W.clone() for p in wl.projections]
+            ps, keep = [], []
+            for pl in pools:
+                a, b, sc, rk = pl.a.clone(), pl.b.clone(), pl.scale.clone(), pl.rank.clone()
+                keep += [a, b, sc, rk]
+                q = L.lora_pool_t(pl.pool.n_slots, pl.pool.d_in, pl.pool.d_out, pl.pool.max_rank,
+                                  pl.pool.dtype, a.data_ptr(), b.data_ptr(), sc.data_ptr(), rk.data_ptr())
+                ps.append(q)
+        ys = [torch.empty(T, p.d_out, dtype=wl.dtype, device=dev) for p in wl.projections]
+        sets.append(dict(xs=xs, Ws=Ws, pools=ps, ys=ys, keep=keep))
+    ws = L.Workspace(T, wl.n_slots, R, device=dev)
+    v = torch.empty(T, R, dtype=torch.float32, device=dev)
+    flags0 = L.LORA_FLAG_SEPARATE_EXPAND if args.separate_expand else 0
+    torch.cuda.synchronize()
+
+    def step(i):
+        s = sets[i % n_sets]
+        for k, pr in enumerate(wl.projections):
+            fl = flags0 | (L.LORA_FLAG_SEGMENTS_READY if (sgmv and k > 0) else 0)
+            L.lora_linear_forward(s["xs"][pr.x_group], s["Ws"][k], s["ys"][k], T, s["pools"][k], ids,
+                                  mode, fl, ws.buf)
+
+    # default step counts: about 2 s of timed work
+    t0 = time.perf_counter()
+    step(0)
+    torch.cuda.synchronize()
+    est = max(time.perf_counter() - t0, 1e-5)
+    steps = args.steps if args.steps is not None else int(min(2000, max(10, 2.0 / est)))
+    warmup = args.warmup if args.warmup is not None else int(min(100, max(3, steps // 10)))
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / steps
+    value = T * steps / elapsed
+    assert L.lora_get_device_error(ws.buf) == -1
+
+    # ---- per-kernel durations: the same step decomposed, HIP events between calls ----
+    # (events are recorded on torch's current stream, the stream the kernels run on)
+    names = (["segments"] if sgmv else []) + ["shrink", "gemm_expand"]
+    if args.separate_expand:
+        names = (["segments"] if sgmv else []) + ["shrink", "gemm", "expand"]
+    k_steps = max(5, min(steps, 200))
+    per = {n: [] for n in names}
+    st = torch.cuda.current_stream()
+
+    def decomposed(i, record):
+        s = sets[i % n_sets]
+        marks = []
+        ev = lambda: (torch.cuda.Event(enable_timing=True) if record else None)
+        e = ev()
+        if record:
+            e.record(st)
+        for k, pr in enumerate(wl.projections):
+            x, W, y, pool = s["xs"][pr.x_group], s["Ws"][k], s["ys"][k], s["pools"][k]
+            calls = []
+            if sgmv and k == 0:
+                calls.append(("segments", lambda: L.lora_build_segments(ids, T, wl.n_slots, R, ws.buf)))
+            calls.append(("shrink", lambda: L.lora_shrink(x, T, pool, ids,
+                                                          L.LORA_MODE_SGMV if sgmv else L.LORA_MODE_BGMV,
+                                                          v, ws.buf)))
+            if args.separate_expand:
+                calls.append(("gemm", lambda: L.lora_gemm(x, W, y, T, pr.d_in, pr.d_out, L.dtype_code(wl.dtype))))
+                calls.append(("expand", lambda: L.lora_expand(v, T, pool, ids,
+                                                              L.LORA_MODE_SGMV if sgmv else L.LORA_MODE_BGMV,
+                                                              y, ws.buf)))
+            else:
+                calls.append(("gemm_expand", lambda: L.lora_gemm_expand(x, W, y, T, pool, ids, v,
+                                                                        L.LORA_MODE_SGMV if sgmv else L.LORA_MODE_BGMV,
+                                                                        ws.buf)))
+            for name, fn in calls:
+                fn()
+                e2 = ev()
+                if record:
+                    e2.record(st)
+                    marks.append((name, k, e, e2))
+                e = e2
+        return marks
+
+    for i in range(3):
+        decomposed(i, False)
+    torch.cuda.synchronize()
+    all_marks = []
+    for i in range(k_steps):
+        all_marks += decomposed(i, True)
+    torch.cuda.synchronize()
+    per_launch = {}          # (name, proj) -> list of ms
+    for name, k, a, b in all_marks:
+        per_launch.setdefault((name, k), []).append(a.elapsed_time(b))
+    kernel_ms = {}           # name -> average ms per step (summed over projections)
+    for (name, k), lst in per_launch.items():
+        kernel_ms[name] = kernel_ms.get(name, 0.0) + sum(lst) / len(lst)
+
+    # ---- algorithmic bytes / flops per launch ----
+    ids_np = wl.ids
+    used = np.unique(ids_np[(ids_np >= 0) & (ids_np < wl.n_slots)])
+    sum_r = int(sum(int(wl.ranks[a]) for a in used))
+    t_a = int(((ids_np >= 0) & (ids_np < wl.n_slots)).sum())
+    r_row = np.where((ids_np >= 0) & (ids_np < wl.n_slots), wl.ranks[np.clip(ids_np, 0, None)], 0)
+    sum_row_r = int(r_row.sum())
+
+    def work(name, pr):
+        d_in, d_out = pr.d_in, pr.d_out
+        if name == "segments":
+            return 3 * T * 4, 0
+        if name == "shrink":
+            return T * d_in * eb + sum_r * d_in * eb + T * R * 4, 2 * sum_row_r * d_in
+        if name == "gemm":
+            return (T * d_in + d_in * d_out + T * d_out) * eb, 2 * T * d_in * d_out
+        if name == "expand":
+            return T * R * 4 + sum_r * d_out * eb + 2 * T * d_out * eb, 2 * sum_row_r * d_out
+        if name == "gemm_expand":
+            by = (T * d_in + d_in * d_out + T * d_out) * eb + T * R * 4 + sum_r * d_out * eb
+            return by, 2 * T * d_in * d_out + 2 * sum_row_r * d_out
+        raise KeyError(name)
+
+    breakdown = {}
+    for name in names:
+        tot_b = tot_f = 0
+        tot_ms = 0.0
+        for k, pr in enumerate(wl.projections):
+            if (name, k) not in per_launch:
+                continue
+            b_, f_ = work(name, pr)
+            ms = sum(per_launch[(name, k)]) / len(per_launch[(name, k)])
+            tot_b += b_
+            tot_f += f_
+            tot_ms += ms
+        breakdown[name] = dict(us_per_step=round(1e3 * tot_ms, 3), bytes=tot_b, flops=tot_f,
+                               gbs=round(tot_b / (tot_ms * 1e-3) / 1e9, 1) if tot_ms else None,
+                               tflops=round(tot_f / (tot_ms * 1e-3) / 1e12, 2) if tot_ms else None)
+    dom = max(names, key=lambda n: breakdown[n]["us_per_step"])
+    launches = len([1 for (n, k) in per_launch if n == dom])
+    bd = breakdown[dom]
+    ai = bd["flops"] / bd["bytes"] if bd["bytes"] else 0.0
+    if wl.dtype == torch.float32 and dom in ("gemm", "gemm_expand"):
+        roof = dict(bound="alu", achieved=bd["tflops"], peak=FP32_VALU_PEAK_TFS, unit="TFLOP/s")
+    elif ai >= RIDGE:
+        roof = dict(bound="mfma", achieved=bd["tflops"], peak=MFMA_BF16_PEAK_TFS, unit="TFLOP/s")
+    else:
+        roof = dict(bound="hbm", achieved=bd["gbs"], peak=HBM_PEAK_GBS, unit="GB/s")
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = dom
+    roof["launches_per_step"] = launches
+    roof["avg_launch_us"] = round(bd["us_per_step"] / max(launches, 1), 3)
+    roof["algorithmic_bytes_per_launch"] = int(bd["bytes"] / max(launches, 1))
+    roof["algorithmic_flops_per_launch"] = int(bd["flops"] / max(launches, 1))
+    roof["traffic"] = stored_traffic(dom, args.workload)
+
+    # ---- calibration copy kernel (counter scaling runs) ----
+    if args.calib_copy:
+        n = 256 * 2 ** 20 // 4 * 4                # 1 GiB of fp32 in, 1 GiB out
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        print("calib-copy bytes_read=%d bytes_written=%d" % (a.numel() * 4, b.numel() * 4), file=sys.stderr)
+
+    # ---- CPU baseline: the fp64 oracle on a bounded sample of this batch ----
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wl.dtype == torch.float32 else "bf16",
+        "data": "synthetic (seeded; random-init adapters and weights)",
+        "config": {
+            "workload": wl.name, "T": T, "projections": [[p.name, p.d_in, p.d_out] for p in wl.projections],
+            "n_slots": wl.n_slots, "max_rank": R, "distinct_adapters": int(used.size),
+            "mode": ("sgmv" if sgmv else "bgmv") + ("" if args.mode != "auto" else " (auto)"),
+            "expand": "separate" if args.separate_expand else "fused in GEMM epilogue",
+            "cold_sets": n_sets, "working_set_MB": round(set_bytes / 1e6, 1),
+        },
+        "roofline": roof,
+        "breakdown": breakdown,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except ValueError:
+        return None
+    ent = data.get("%s/%s" % (workload, kernel))
+    if not ent or ent.get("source_sha") != source_sha(kernel):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, target_s):
+    import numpy as np
+    import torch
+
+    from oracle import BF16, F32, lora_scale, oracle_rows
+
+    def host(t):
+        t = t.detach().contiguous().cpu()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    code = F32 if wl.dtype == torch.float32 else BF16
+    # The adapters were released after upload: redraw them the same way (same seed) on the host side
+    from rank_adapter_gemm_amd.workloads import make_workload
+    wl2 = make_workload(wl.name, device="cuda")
+    xs = {g: host(x) for g, x in wl2.xs.items()}
+    rng = np.random.default_rng(12345)
+    order = rng.permutation(wl.T)
+    scales = [lora_scale(float(a), int(r)) for a, r in zip(wl2.alphas, wl2.ranks)]
+    rows_done, elapsed, n = 0, 0.0, 8
+    per_proj = []
+    for pr in wl2.projections:
+        per_proj.append(dict(W=host(pr.W), A=pr.A, B=pr.B, x=xs[pr.x_group]))
+    while rows_done < wl.T and elapsed < target_s:
+        take = order[rows_done: rows_done + n]
+        used = sorted({int(wl.ids[t]) for t in take if 0 <= wl.ids[t] < wl.n_slots})
+        for pp in per_proj:
+            A = [None] * wl.n_slots
+            B = [None] * wl.n_slots
+            for s in used:
+                r = int(wl2.ranks[s])
+                A[s] = host(pp["A"][s, :, :r])
+                B[s] = host(pp["B"][s, :r, :])
+            t0 = time.perf_counter()
+            oracle_rows(code, pp["x"], pp["W"], wl.ids, A, B, [int(r) for r in wl2.ranks], scales,
+                        rows=take, n_threads=cores)
+            elapsed += time.perf_counter() - t0
+        rows_done += len(take)
+        n = min(2 * n, 4096)
+    return {"value": round(rows_done / elapsed, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of %d token rows of %s, all %d projection(s), fp64 C oracle, %.1f s"
+                      % (rows_done, wl.T, wl.name, len(wl2.projections), elapsed)}
+
+
+if __name__ == "__main__":
+    main()

@@ -202,6 +202,17 @@ lora_status_t lora_gemm(const void *x, const void *W, void *y, int32_t T, int32_
                         int32_t d_out, lora_dtype_t dtype, void *ws, size_t ws_bytes,
                         lora_stream_t stream);
 
+/* ---- a3 + a5 fused ------------------------------------------------------------ */
+
+/* y = x W + s_a v[t, 0:r_a] B_a per row (the expand inside the GEMM
+ * epilogue, one rounding), with v from lora_shrink on the same ids.  In SGMV
+ * mode the GEMM visits rows in segment order (lora_build_segments on the same
+ * ids and ws first); BGMV and AUTO keep the original row order.  Shapes and
+ * dtypes as for lora_linear_forward; v DEVICE fp32 [T, max_rank]. */
+lora_status_t lora_gemm_expand(const void *x, const void *W, void *y, int32_t T,
+                               const lora_pool_t *pool, const int32_t *ids, const float *v,
+                               lora_mode_t mode, void *ws, size_t ws_bytes, lora_stream_t stream);
+
 /* ---- a3-a8: the whole layer -------------------------------------------------- */
 
 /* y = x W + s_a (x A_a) B_a per row (a = ids[t], -1 = none).

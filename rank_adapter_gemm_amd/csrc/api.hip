@@ -186,6 +186,21 @@ lora_status_t lora_gemm(const void *x, const void *W, void *y, int32_t T, int32_
                        hs(stream));
 }
 
+lora_status_t lora_gemm_expand(const void *x, const void *W, void *y, int32_t T,
+                               const lora_pool_t *pool, const int32_t *ids, const float *v,
+                               lora_mode_t mode, void *ws, size_t ws_bytes, lora_stream_t stream) {
+    if (!valid_pool(pool) || T < 0 || !valid_mode(mode)) return LORA_ERR_INVALID_ARGUMENT;
+    if (T > 0 && (!x || !W || !y || !ids || !v || !aligned16(x) || !aligned16(W) || !aligned16(y)))
+        return LORA_ERR_INVALID_ARGUMENT;
+    ws_layout L;
+    lora_status_t st = check_ws(ws, ws_bytes, T, pool->n_slots, pool->max_rank, &L);
+    if (st != LORA_OK) return st;
+    if (T == 0) return LORA_OK;
+    const int32_t *perm = (mode == LORA_MODE_SGMV) ? ws_ptr<int32_t>(ws, L.perm) : nullptr;
+    return launch_gemm(x, W, y, T, pool->d_in, pool->d_out, pool->dtype, pool, ids, v, perm,
+                       ws_ptr<int32_t>(ws, L.header), hs(stream));
+}
+
 lora_status_t lora_linear_forward(const void *x, const void *W, void *y, int32_t T,
                                   const lora_pool_t *pool, const int32_t *ids, lora_mode_t mode,
                                   uint32_t flags, void *ws, size_t ws_bytes,

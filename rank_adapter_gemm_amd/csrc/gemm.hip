@@ -144,76 +144,116 @@ __global__ void __launch_bounds__(512) k_gemm_bf16(gemm_args g) {
     }
 
     // ---- epilogue ----
-    float *sv = reinterpret_cast<float *>(smem);             // [256][max_rank]
-    int32_t *s_t = reinterpret_cast<int32_t *>(sv + (LORA ? GBM * g.max_rank : 0));
+    // Each wavefront moves one 32 x 64 block of its accumulators at a time
+    // through its own LDS area; a lane then owns 8 consecutive columns of 4
+    // rows, adds s * sum_j v[t][j] B[j][n] for rows with an adapter (B read in
+    // rank octets, reused across the lane's rows when they share the slot) and
+    // writes 16-byte rows of y after one rounding.
+    constexpr int SLD = 68;                                       // staged row stride (floats)
+    float *stage = reinterpret_cast<float *>(smem) + w * 32 * SLD;
+    int32_t *s_t = reinterpret_cast<int32_t *>(reinterpret_cast<float *>(smem) + 8 * 32 * SLD);
     int32_t *s_id = s_t + GBM;
-    int32_t *s_r = s_id + GBM;
-    float *s_s = reinterpret_cast<float *>(s_r + GBM);
-    if (LORA) {
-        for (int i = tid; i < GBM; i += 512) {
-            const int p = m0 + i;
-            int32_t t = -1, id = -1, r = 0;
-            float s = 0.0f;
-            if (p < T) t = perm_row(g.perm, p, T);
-            if (t >= 0) {
-                const int32_t raw = g.ids[t];
-                if (raw >= 0 && raw < g.n_slots) {
-                    r = g.rank[raw];
-                    if (r > 0) {
-                        id = raw;
-                        s = g.scale[raw];
-                    } else {
-                        r = 0;
-                    }
-                }
-            }
-            s_t[i] = t;
-            s_id[i] = id;
-            s_r[i] = r;
-            s_s[i] = s;
-        }
-        __syncthreads();
-        for (int e = tid; e < GBM * g.max_rank; e += 512) {
-            const int i = e / g.max_rank, j = e - i * g.max_rank;
-            sv[e] = (s_id[i] >= 0) ? g.v[(int64_t)s_t[i] * g.max_rank + j] : 0.0f;
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-        const int c = wn * 64 + cb * 32 + (lane & 31);
-        const int n = n0 + c;
-        if (n >= N) continue;
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int i = wm * 128 + rb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                const int p = m0 + i;
-                if (p >= T) continue;
-                float val = acc[rb][cb][e];
-                int64_t t;
-                if (LORA) {
-                    t = s_t[i];
-                    const int32_t id = s_id[i];
-                    if (id >= 0) {
-                        const int G = (s_r[i] + 7) >> 3;
-                        const uint16_t *bq = g.b + ((int64_t)id * g.max_rank * N + (int64_t)n * 8);
-                        const float *vi = sv + i * g.max_rank;
-                        float d = 0.0f;
-                        for (int gg = 0; gg < G; ++gg) {
-                            float bf[8];
-                            vec16<LORA_BF16>::widen(ldg16(bq + (int64_t)gg * N * 8), bf);
-#pragma unroll
-                            for (int q = 0; q < 8; ++q) d = fmaf(vi[gg * 8 + q], bf[q], d);
-                        }
-                        val = fmaf(s_s[i], d, val);
-                    }
+    int32_t *s_gq = s_id + GBM;
+    float *s_sc = reinterpret_cast<float *>(s_gq + GBM);
+    for (int i = tid; i < GBM; i += 512) {
+        const int p = m0 + i;
+        const int32_t t = (p < T) ? perm_row(g.perm, p, T) : -1;
+        int32_t id = -1, r = 0;
+        float sc = 0.0f;
+        if (LORA && t >= 0) {
+            const int32_t raw = g.ids[t];
+            if (raw >= 0 && raw < g.n_slots) {
+                r = g.rank[raw];
+                if (r > 0) {
+                    id = raw;
+                    sc = g.scale[raw];
                 } else {
-                    t = perm_row(g.perm, p, T);
+                    r = 0;
                 }
-                if (t >= 0) g.y[t * N + n] = (uint16_t)f32_to_bf16_bits(val);
             }
+        }
+        s_t[i] = t;
+        s_id[i] = id;
+        s_gq[i] = (r + 7) >> 3;
+        s_sc[i] = sc;
+    }
+    const int q = lane & 7, rr = lane >> 3;
+    const int n = n0 + wn * 64 + 8 * q;
+    const int R = g.max_rank;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        __syncthreads();
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                stage[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * SLD + cb * 32 + (lane & 31)] =
+                    acc[rb][cb][e];
+        __syncthreads();
+        int32_t tk[4], idk[4], gk[4];
+        float sk[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = wm * 128 + rb * 32 + rr + 8 * k;
+            tk[k] = s_t[i];
+            idk[k] = s_id[i];
+            gk[k] = s_gq[i];
+            sk[k] = s_sc[i];
+        }
+        float d[4][8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) d[k][c] = 0.0f;
+        if (LORA && n < N) {
+            const bool same = idk[0] >= 0 && idk[1] == idk[0] && idk[2] == idk[0] && idk[3] == idk[0];
+            int G = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) G = (idk[k] >= 0 && gk[k] > G) ? gk[k] : G;
+            for (int gg = 0; gg < G; ++gg) {
+                uint4 bq[8];
+                if (same) {
+                    const uint16_t *bp = g.b + ((int64_t)idk[0] * R * N + ((int64_t)gg * N + n) * 8);
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) bq[c] = ldg16(bp + c * 8);
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    if (idk[k] < 0 || gg >= gk[k]) continue;
+                    if (!same) {
+                        const uint16_t *bp = g.b + ((int64_t)idk[k] * R * N + ((int64_t)gg * N + n) * 8);
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) bq[c] = ldg16(bp + c * 8);
+                    }
+                    const float *vp = g.v + (int64_t)tk[k] * R + gg * 8;
+                    const float4 v0 = *reinterpret_cast<const float4 *>(vp);
+                    const float4 v1 = *reinterpret_cast<const float4 *>(vp + 4);
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        float bf[8];
+                        vec16<LORA_BF16>::widen(bq[c], bf);
+                        float a = d[k][c];
+                        a = fmaf(v0.x, bf[0], a); a = fmaf(v0.y, bf[1], a);
+                        a = fmaf(v0.z, bf[2], a); a = fmaf(v0.w, bf[3], a);
+                        a = fmaf(v1.x, bf[4], a); a = fmaf(v1.y, bf[5], a);
+                        a = fmaf(v1.z, bf[6], a); a = fmaf(v1.w, bf[7], a);
+                        d[k][c] = a;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (tk[k] < 0 || n >= N) continue;
+            const float *src = stage + (rr + 8 * k) * SLD + 8 * q;
+            const float4 o0 = *reinterpret_cast<const float4 *>(src);
+            const float4 o1 = *reinterpret_cast<const float4 *>(src + 4);
+            float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+            if (LORA && idk[k] >= 0) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) o[c] = fmaf(sk[k], d[k][c], o[c]);
+            }
+            stg16(g.y + (int64_t)tk[k] * N + n, vec16<LORA_BF16>::narrow(o));
         }
     }
 }

@@ -36,7 +36,8 @@ LORA_FLAG_SEPARATE_EXPAND = 0x2
 EXPORTED = (
     "lora_pool_bytes", "lora_pool_create", "lora_pool_upload", "lora_pool_clear",
     "lora_workspace_bytes", "lora_workspace_init", "lora_segments_view", "lora_build_segments",
-    "lora_shrink", "lora_expand", "lora_gemm", "lora_linear_forward", "lora_get_device_error",
+    "lora_shrink", "lora_expand", "lora_gemm", "lora_gemm_expand", "lora_linear_forward",
+    "lora_get_device_error",
     "lora_status_string", "lora_version",
 )
 
@@ -101,6 +102,7 @@ def load(path: str = LIB_PATH):
         "lora_shrink": (c_i32, [c_vp, c_i32, P(lora_pool_t), c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
         "lora_expand": (c_i32, [c_vp, c_i32, P(lora_pool_t), c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
         "lora_gemm": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_sz, c_vp]),
+        "lora_gemm_expand": (c_i32, [c_vp, c_vp, c_vp, c_i32, P(lora_pool_t), c_vp, c_vp, c_i32, c_vp, c_sz, c_vp]),
         "lora_linear_forward": (c_i32, [c_vp, c_vp, c_vp, c_i32, P(lora_pool_t), c_vp, c_i32, c_u32, c_vp, c_sz, c_vp]),
         "lora_get_device_error": (c_i32, [c_vp, c_sz, c_vp, P(c_i32)]),
         "lora_status_string": (ctypes.c_char_p, [c_i32]),
@@ -212,6 +214,12 @@ def lora_expand(v, T, pool, ids, mode, y, ws, stream=None):
 def lora_gemm(x, W, y, T, d_in, d_out, dtype, stream=None):
     _ok(load().lora_gemm(_ptr(x), _ptr(W), _ptr(y), T, d_in, d_out, dtype, None, 0, _stream(stream)),
         "lora_gemm")
+
+
+def lora_gemm_expand(x, W, y, T, pool, ids, v, mode, ws, stream=None):
+    _ok(load().lora_gemm_expand(_ptr(x), _ptr(W), _ptr(y), T, ctypes.byref(pool), _ptr(ids), _ptr(v),
+                                mode, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+        "lora_gemm_expand")
 
 
 def lora_linear_forward(x, W, y, T, pool, ids, mode, flags, ws, stream=None):
