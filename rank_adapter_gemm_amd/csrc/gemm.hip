@@ -27,7 +27,9 @@
 
 namespace lora {
 
-constexpr int GBM = 256, GBN = 256, GBK = 64, GLD = GBK + 8;
+constexpr int GBM = 256, GBN = 256;
+// K step and number of LDS stages of the bf16 kernel (2 x 64 KB).
+constexpr int kGemmBK = 64, kGemmNS = 2;
 
 struct gemm_args {
     const uint16_t *x;
@@ -41,121 +43,248 @@ struct gemm_args {
     int32_t n_slots, max_rank;
     const int32_t *ids;
     const float *v;
-    int32_t n_tiles_n;
+    int32_t n_tiles_m, n_tiles_n;
 };
 
-template <bool LORA>
-__global__ void __launch_bounds__(512) k_gemm_bf16(gemm_args g) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * GBM * GLD];
+// Tile order: workgroups are dispatched round-robin over the 8 XCDs (each
+// with its own L2), so workgroup b runs on XCD b % 8.  Give each XCD a
+// contiguous range of tiles, walked in groups of GROUP_M row tiles (down M
+// first, then across N) so the tiles resident on one XCD share x rows and W
+// columns in its L2.
+constexpr int kXcds = 8, kGroupM = 8;
+
+__device__ __forceinline__ void tile_of(int b, int total, int n_tiles_m, int n_tiles_n, int &tm, int &tn) {
+    const int q = total / kXcds, r = total % kXcds;
+    const int x = b % kXcds, slot = b / kXcds;
+    const int v = x * q + min(x, r) + slot;
+    const int per_group = kGroupM * n_tiles_n;
+    const int grp = v / per_group;
+    const int first_m = grp * kGroupM;
+    const int gm = min(kGroupM, n_tiles_m - first_m);
+    const int in = v - grp * per_group;
+    tm = first_m + in % gm;
+    tn = in / gm;
+}
+
+// A 16-byte zero vector in global memory: the source of the DMA loads of
+// masked lanes (rows past T, k past K, columns past N), so those LDS slots
+// hold zeros.
+__device__ __attribute__((aligned(16))) uint4 g_zero16[1];
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+
+// One 16-byte-per-lane DMA load from global memory straight into LDS: lane
+// l's bytes land at lds_wave_base + 16 l (gfx950 global_load_lds_dwordx4).
+// Issued as inline assembly so the compiler does not add its own
+// conservative vmcnt waits before later LDS reads; the kernel orders these
+// loads itself with explicit s_waitcnt vmcnt before each barrier.
+__device__ __forceinline__ void dma16(const void *gptr, const void *lds_wave_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_wave_base)));
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0)
+                 : "memory", "m0");
+}
+
+// XOR swizzles of the 16-byte chunk index inside an LDS row (see the tile
+// layouts below): conflict-free fragment reads for 32 and for 64 LDS banks.
+template <int BK> __device__ __forceinline__ int swz_x(int r) {
+    return BK == 64 ? ((r ^ (r >> 3)) & 7) : (((r >> 2) ^ (r >> 1)) & 3);
+}
+__device__ __forceinline__ int swz_w(int k) {
+    return (0xCA60 >> (4 * (k & 3))) & 0xF;            // 0, 6, 10, 12 for k % 4 = 0..3
+}
+
+// LDS tiles per stage (no padding; rows written by DMA 1 KB at a time):
+//   x: [256 rows][BK] bf16, row chunk c (8 k) stored at slot c ^ swz_x(row)
+//   W: [BK rows (k)][256 n] bf16, row chunk c (8 n) stored at slot c ^ swz_w(k)
+// MFMA A fragments: ds_read_b128 of 8 consecutive k of one x row.
+// MFMA B fragments: two ds_read_b64_tr_b16 per lane, each returning 4
+// consecutive k of one W column from a 4 x 16 block read by 16 lanes.
+template <bool LORA, int BK, int NS>
+__global__ void __launch_bounds__(256, 1) k_gemm_bf16(gemm_args g) {
+    constexpr int XCH = BK / 8;                         // 16-byte chunks per x row
+    constexpr int XSTAGE = GBM * BK, WSTAGE = BK * GBN; // elements per stage
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * (XSTAGE + WSTAGE) > 4 * 32 * 132 * 2 + 4 * GBM * 2
+                                                                  ? NS * (XSTAGE + WSTAGE)
+                                                                  : 4 * 32 * 132 * 2 + 4 * GBM * 2];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 2, wn = w & 3;
-    const int tm = blockIdx.x / g.n_tiles_n, tn = blockIdx.x % g.n_tiles_n;
+    const int wm = w >> 1, wn = w & 1;                  // 2 x 2 wavefronts, 128 x 128 each
+    int tm, tn;
+    tile_of(blockIdx.x, gridDim.x, g.n_tiles_m, g.n_tiles_n, tm, tn);
     const int m0 = tm * GBM, n0 = tn * GBN;
     const int K = g.K, N = g.N, T = g.T;
 
-    // this thread's four x rows
-    int64_t xoff[4];
+    // DMA plan.  x: the stage is 256 * XCH chunks; wave w issues XI = 256*XCH/256
+    // instructions of 64 chunks, chunk index c = (w * XI + j) * 64 + lane.
+    constexpr int XI = GBM * XCH / 256, WI = BK * 32 / 256;
+    int64_t xrow[XI];
+    int xcol[XI];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int p = m0 + (tid >> 3) + 64 * i;
+    for (int j = 0; j < XI; ++j) {
+        const int c = (w * XI + j) * 64 + lane;
+        const int r = c / XCH, slot = c % XCH;
+        const int p = m0 + r;
         const int32_t t = (p < T) ? perm_row(g.perm, p, T) : -1;
-        xoff[i] = (t >= 0) ? (int64_t)t * K : -1;
+        xrow[j] = (t >= 0) ? (int64_t)t * K : -1;
+        xcol[j] = 8 * (slot ^ swz_x<BK>(r));
     }
-    const int xk = (tid & 7) * 8;
-    // this thread's 4 x 8 block of W
-    const int kb = lane & 15, nb = (lane >> 4) + 4 * w;
-    const int wk = 4 * kb, wnn = 8 * nb;
-    const bool wcol_ok = (n0 + wnn) < N;
-
-    uint4 xr[4], wr[4];
-    auto gload = [&](int k0) {
+    // W: the stage is BK rows * 32 chunks; chunk index c = (w * WI + j) * 64 + lane
+    int wrow[WI], wcol[WI];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            xr[i] = make_uint4(0, 0, 0, 0);
-            if (xoff[i] >= 0 && k0 + xk < K) xr[i] = ldg16(g.x + xoff[i] + k0 + xk);
+    for (int j = 0; j < WI; ++j) {
+        const int c = (w * WI + j) * 64 + lane;
+        const int k = c >> 5, slot = c & 31;
+        wrow[j] = k;
+        wcol[j] = n0 + 8 * (slot ^ swz_w(k));
+    }
+    auto dma_stage = [&](int kt, int buf) {
+        uint16_t *xs = smem + buf * (XSTAGE + WSTAGE);
+        uint16_t *wsm = xs + XSTAGE;
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int j = 0; j < XI; ++j) {
+            const int kk = k0 + xcol[j];
+            const void *src = (xrow[j] >= 0 && kk < K) ? (const void *)(g.x + xrow[j] + kk) : (const void *)g_zero16;
+            dma16(src, xs + (w * XI + j) * 64 * 8);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int k = k0 + wk + i;
-            wr[i] = make_uint4(0, 0, 0, 0);
-            if (wcol_ok && k < K) wr[i] = ldg16(g.W + (int64_t)k * N + n0 + wnn);
-        }
-    };
-    auto sstore = [&](int buf) {
-        uint16_t *As = smem + buf * GBM * GLD;
-        uint16_t *Bs = smem + 2 * GBM * GLD + buf * GBN * GLD;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint4 *>(As + ((tid >> 3) + 64 * i) * GLD + xk) = xr[i];
-        const uint32_t in0[4] = {wr[0].x, wr[0].y, wr[0].z, wr[0].w};
-        const uint32_t in1[4] = {wr[1].x, wr[1].y, wr[1].z, wr[1].w};
-        const uint32_t in2[4] = {wr[2].x, wr[2].y, wr[2].z, wr[2].w};
-        const uint32_t in3[4] = {wr[3].x, wr[3].y, wr[3].z, wr[3].w};
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            // column 2d: low halves; column 2d+1: high halves
-            const uint2 lo = make_uint2((in0[d] & 0xffffu) | (in1[d] << 16),
-                                        (in2[d] & 0xffffu) | (in3[d] << 16));
-            const uint2 hi = make_uint2((in0[d] >> 16) | (in1[d] & 0xffff0000u),
-                                        (in2[d] >> 16) | (in3[d] & 0xffff0000u));
-            *reinterpret_cast<uint2 *>(Bs + (wnn + 2 * d) * GLD + wk) = lo;
-            *reinterpret_cast<uint2 *>(Bs + (wnn + 2 * d + 1) * GLD + wk) = hi;
+        for (int j = 0; j < WI; ++j) {
+            const int k = k0 + wrow[j];
+            const void *src = (k < K && wcol[j] < N) ? (const void *)(g.W + (int64_t)k * N + wcol[j]) : (const void *)g_zero16;
+            dma16(src, wsm + (w * WI + j) * 64 * 8);
         }
     };
 
-    f32x16_t acc[4][2];
+    f32x16_t acc[4][4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[rb][cb][e] = 0.0f;
 
-    const int nk = (K + GBK - 1) / GBK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    const int frag_row = lane & 31, frag_k = (lane >> 5) * 8;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * GBK);
-        const uint16_t *As = smem + buf * GBM * GLD;
-        const uint16_t *Bs = smem + 2 * GBM * GLD + buf * GBN * GLD;
+    // fragment addressing
+    const int fr = lane & 31, fk = lane >> 5;           // A: row within block, k-group
+    const int grp = lane >> 4, s16 = lane & 15;         // B: 16-lane group, lane in group
+    const int b_kofs = 8 * (grp >> 1) + (s16 >> 2);     // + 16 ks + 4 inst
+    const int b_col = 16 * (grp & 1) + 4 * (s16 & 3);   // + wn*128 + cb*32
+    constexpr int KS = BK / 16;                         // MFMA k-substeps per stage
+    bf16x8_t af[2][4], bfr[2][4];
+    auto load_frags = [&](int buf, int ks, bf16x8_t *a, bf16x8_t *b) {
+        const uint16_t *xs = smem + buf * (XSTAGE + WSTAGE);
+        const uint16_t *wsm = xs + XSTAGE;
 #pragma unroll
-        for (int ks = 0; ks < GBK / 16; ++ks) {
-            bf16x8_t af[4], bfr[2];
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-                af[rb] = *reinterpret_cast<const bf16x8_t *>(
-                    As + (wm * 128 + rb * 32 + frag_row) * GLD + ks * 16 + frag_k);
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-                bfr[cb] = *reinterpret_cast<const bf16x8_t *>(
-                    Bs + (wn * 64 + cb * 32 + frag_row) * GLD + ks * 16 + frag_k);
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb)
-                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb], bfr[cb],
-                                                                          acc[rb][cb], 0, 0, 0);
+        for (int rb = 0; rb < 4; ++rb) {
+            const int r = wm * 128 + rb * 32 + fr;
+            const int c = (2 * ks + fk) ^ swz_x<BK>(r);
+            a[rb] = *reinterpret_cast<const bf16x8_t *>(xs + r * BK + 8 * c);
         }
-        if (kt + 1 < nk) sstore(buf ^ 1);
-        __syncthreads();
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const int col = wn * 128 + cb * 32 + b_col;          // multiple of 4
+            short4_t h[2];
+#pragma unroll
+            for (int inst = 0; inst < 2; ++inst) {
+                const int k = 16 * ks + 4 * inst + b_kofs;
+                const int chunk = (col >> 3) ^ swz_w(k);
+                const uint16_t *addr = wsm + k * GBN + 8 * chunk + (col & 7);
+                h[inst] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_short4_t *)(reinterpret_cast<uintptr_t>(addr)));
+            }
+            typedef short short8_t __attribute__((ext_vector_type(8)));
+            const short8_t hv = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+            b[cb] = __builtin_bit_cast(bf16x8_t, hv);
+        }
+    };
+    auto mfmas = [&](const bf16x8_t *a, const bf16x8_t *b, int rb0, int rb1) {
+#pragma unroll
+        for (int rb = rb0; rb < rb1; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+                acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
+    };
+    // Scheduling patterns (sched_group_barrier masks: 0x008 MFMA, 0x100 LDS read).
+    auto interleave_16_12 = [&]() {          // 16 MFMAs; the 12 reads of the next fragments early
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
+    };
+    auto interleave_8_12 = [&]() {           // 8 MFMAs; 12 reads early
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    };
+
+    const int nk = (K + BK - 1) / BK;
+    constexpr int PER = XI + WI;                          // DMA instructions per stage per wave
+    auto wait_stage = [&](int ahead) {                    // later stages still in flight
+        if (ahead >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PER) : "memory");
+        else if (ahead == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory");
+        else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+        if (st < nk) dma_stage(st, st);
+    wait_stage(min(NS - 1, nk - 1));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    load_frags(0, 0, af[0], bfr[0]);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt % NS;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int cur = ks & 1, nxt = cur ^ 1;
+            if (ks + 1 < KS) {
+                load_frags(buf, ks + 1, af[nxt], bfr[nxt]);
+                mfmas(af[cur], bfr[cur], 0, 4);
+                interleave_16_12();
+            } else {
+                // Stage hand-off, between the two halves of the last MFMAs of
+                // this stage: every wave has finished reading this stage from
+                // LDS (lgkmcnt), stage kt+1 has landed for all waves after the
+                // barrier, this stage's buffer is refilled with stage kt+NS,
+                // and the first fragments of stage kt+1 are read under the
+                // second half of the MFMAs (after the last stage they are read
+                // and not used).
+                mfmas(af[cur], bfr[cur], 0, 2);
+                __builtin_amdgcn_sched_barrier(0);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                wait_stage(min(NS - 2, nk - 2 - kt));
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                if (kt + NS < nk) dma_stage(kt + NS, buf);
+                __builtin_amdgcn_sched_barrier(0);
+                load_frags((kt + 1) % NS, 0, af[nxt], bfr[nxt]);
+                mfmas(af[cur], bfr[cur], 2, 4);
+                interleave_8_12();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
 
     // ---- epilogue ----
-    // Each wavefront moves one 32 x 64 block of its accumulators at a time
-    // through its own LDS area; a lane then owns 8 consecutive columns of 4
+    // Each wavefront moves one 32 x 128 block of its accumulators at a time
+    // through its own LDS area; a lane then owns 8 consecutive columns of 8
     // rows, adds s * sum_j v[t][j] B[j][n] for rows with an adapter (B read in
-    // rank octets, reused across the lane's rows when they share the slot) and
-    // writes 16-byte rows of y after one rounding.
-    constexpr int SLD = 68;                                       // staged row stride (floats)
+    // rank octets, reused across the lane's rows while they share the slot)
+    // and writes 16-byte rows of y after one rounding.
+    constexpr int SLD = 132;                                      // staged row stride (floats)
     float *stage = reinterpret_cast<float *>(smem) + w * 32 * SLD;
-    int32_t *s_t = reinterpret_cast<int32_t *>(reinterpret_cast<float *>(smem) + 8 * 32 * SLD);
+    int32_t *s_t = reinterpret_cast<int32_t *>(reinterpret_cast<float *>(smem) + 4 * 32 * SLD);
     int32_t *s_id = s_t + GBM;
     int32_t *s_gq = s_id + GBM;
     float *s_sc = reinterpret_cast<float *>(s_gq + GBM);
-    for (int i = tid; i < GBM; i += 512) {
+    for (int i = tid; i < GBM; i += 256) {
         const int p = m0 + i;
         const int32_t t = (p < T) ? perm_row(g.perm, p, T) : -1;
         int32_t id = -1, r = 0;
@@ -177,83 +306,86 @@ __global__ void __launch_bounds__(512) k_gemm_bf16(gemm_args g) {
         s_gq[i] = (r + 7) >> 3;
         s_sc[i] = sc;
     }
-    const int q = lane & 7, rr = lane >> 3;
-    const int n = n0 + wn * 64 + 8 * q;
+    const int q = lane & 15, rr = lane >> 4;
+    const int n = n0 + wn * 128 + 8 * q;
     const int R = g.max_rank;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
         __syncthreads();
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 stage[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * SLD + cb * 32 + (lane & 31)] =
                     acc[rb][cb][e];
         __syncthreads();
-        int32_t tk[4], idk[4], gk[4];
-        float sk[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int i = wm * 128 + rb * 32 + rr + 8 * k;
-            tk[k] = s_t[i];
-            idk[k] = s_id[i];
-            gk[k] = s_gq[i];
-            sk[k] = s_sc[i];
-        }
-        float d[4][8];
+        for (int half = 0; half < 2; ++half) {
+            int32_t tk[4], idk[4], gk[4];
+            float sk[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+            for (int k = 0; k < 4; ++k) {
+                const int i = wm * 128 + rb * 32 + rr + 4 * (k + 4 * half);
+                tk[k] = s_t[i];
+                idk[k] = s_id[i];
+                gk[k] = s_gq[i];
+                sk[k] = s_sc[i];
+            }
+            float d[4][8];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) d[k][c] = 0.0f;
-        if (LORA && n < N) {
-            const bool same = idk[0] >= 0 && idk[1] == idk[0] && idk[2] == idk[0] && idk[3] == idk[0];
-            int G = 0;
+            for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) G = (idk[k] >= 0 && gk[k] > G) ? gk[k] : G;
-            for (int gg = 0; gg < G; ++gg) {
-                uint4 bq[8];
-                if (same) {
-                    const uint16_t *bp = g.b + ((int64_t)idk[0] * R * N + ((int64_t)gg * N + n) * 8);
+                for (int c = 0; c < 8; ++c) d[k][c] = 0.0f;
+            if (LORA && n < N) {
+                const bool same = idk[0] >= 0 && idk[1] == idk[0] && idk[2] == idk[0] && idk[3] == idk[0];
+                int G = 0;
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) bq[c] = ldg16(bp + c * 8);
-                }
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    if (idk[k] < 0 || gg >= gk[k]) continue;
-                    if (!same) {
-                        const uint16_t *bp = g.b + ((int64_t)idk[k] * R * N + ((int64_t)gg * N + n) * 8);
+                for (int k = 0; k < 4; ++k) G = (idk[k] >= 0 && gk[k] > G) ? gk[k] : G;
+                for (int gg = 0; gg < G; ++gg) {
+                    uint4 bq[8];
+                    if (same) {
+                        const uint16_t *bp = g.b + ((int64_t)idk[0] * R * N + ((int64_t)gg * N + n) * 8);
 #pragma unroll
                         for (int c = 0; c < 8; ++c) bq[c] = ldg16(bp + c * 8);
                     }
-                    const float *vp = g.v + (int64_t)tk[k] * R + gg * 8;
-                    const float4 v0 = *reinterpret_cast<const float4 *>(vp);
-                    const float4 v1 = *reinterpret_cast<const float4 *>(vp + 4);
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) {
-                        float bf[8];
-                        vec16<LORA_BF16>::widen(bq[c], bf);
-                        float a = d[k][c];
-                        a = fmaf(v0.x, bf[0], a); a = fmaf(v0.y, bf[1], a);
-                        a = fmaf(v0.z, bf[2], a); a = fmaf(v0.w, bf[3], a);
-                        a = fmaf(v1.x, bf[4], a); a = fmaf(v1.y, bf[5], a);
-                        a = fmaf(v1.z, bf[6], a); a = fmaf(v1.w, bf[7], a);
-                        d[k][c] = a;
+                    for (int k = 0; k < 4; ++k) {
+                        if (idk[k] < 0 || gg >= gk[k]) continue;
+                        if (!same) {
+                            const uint16_t *bp = g.b + ((int64_t)idk[k] * R * N + ((int64_t)gg * N + n) * 8);
+#pragma unroll
+                            for (int c = 0; c < 8; ++c) bq[c] = ldg16(bp + c * 8);
+                        }
+                        const float *vp = g.v + (int64_t)tk[k] * R + gg * 8;
+                        const float4 v0 = *reinterpret_cast<const float4 *>(vp);
+                        const float4 v1 = *reinterpret_cast<const float4 *>(vp + 4);
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) {
+                            float bf[8];
+                            vec16<LORA_BF16>::widen(bq[c], bf);
+                            float a = d[k][c];
+                            a = fmaf(v0.x, bf[0], a); a = fmaf(v0.y, bf[1], a);
+                            a = fmaf(v0.z, bf[2], a); a = fmaf(v0.w, bf[3], a);
+                            a = fmaf(v1.x, bf[4], a); a = fmaf(v1.y, bf[5], a);
+                            a = fmaf(v1.z, bf[6], a); a = fmaf(v1.w, bf[7], a);
+                            d[k][c] = a;
+                        }
                     }
                 }
             }
-        }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if (tk[k] < 0 || n >= N) continue;
-            const float *src = stage + (rr + 8 * k) * SLD + 8 * q;
-            const float4 o0 = *reinterpret_cast<const float4 *>(src);
-            const float4 o1 = *reinterpret_cast<const float4 *>(src + 4);
-            float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-            if (LORA && idk[k] >= 0) {
+            for (int k = 0; k < 4; ++k) {
+                if (tk[k] < 0 || n >= N) continue;
+                const float *src = stage + (rr + 4 * (k + 4 * half)) * SLD + 8 * q;
+                const float4 o0 = *reinterpret_cast<const float4 *>(src);
+                const float4 o1 = *reinterpret_cast<const float4 *>(src + 4);
+                float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+                if (LORA && idk[k] >= 0) {
 #pragma unroll
-                for (int c = 0; c < 8; ++c) o[c] = fmaf(sk[k], d[k][c], o[c]);
+                    for (int c = 0; c < 8; ++c) o[c] = fmaf(sk[k], d[k][c], o[c]);
+                }
+                stg16(g.y + (int64_t)tk[k] * N + n, vec16<LORA_BF16>::narrow(o));
             }
-            stg16(g.y + (int64_t)tk[k] * N + n, vec16<LORA_BF16>::narrow(o));
         }
     }
 }
@@ -371,11 +503,12 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
         g.ids = ids;
         g.v = v;
         g.n_tiles_n = (d_out + GBN - 1) / GBN;
-        const int tiles = ((T + GBM - 1) / GBM) * g.n_tiles_n;
+        g.n_tiles_m = (T + GBM - 1) / GBM;
+        const int tiles = g.n_tiles_m * g.n_tiles_n;
         if (pool)
-            hipLaunchKernelGGL(k_gemm_bf16<true>, dim3(tiles), dim3(512), 0, s, g);
+            hipLaunchKernelGGL((k_gemm_bf16<true, kGemmBK, kGemmNS>), dim3(tiles), dim3(256), 0, s, g);
         else
-            hipLaunchKernelGGL(k_gemm_bf16<false>, dim3(tiles), dim3(512), 0, s, g);
+            hipLaunchKernelGGL((k_gemm_bf16<false, kGemmBK, kGemmNS>), dim3(tiles), dim3(256), 0, s, g);
     } else {
         gemm_f32_args g;
         g.x = (const float *)x;
