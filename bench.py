@@ -128,7 +128,7 @@ def main():
                 ps.append(q)
         ys = [torch.empty(T, p.d_out, dtype=wl.dtype, device=dev) for p in wl.projections]
         sets.append(dict(xs=xs, Ws=Ws, pools=ps, ys=ys, keep=keep))
-    ws = L.Workspace(T, wl.n_slots, R, device=dev)
+    ws = L.Workspace(T, wl.n_slots, R, max(p.d_out for p in wl.projections), device=dev)
     v = torch.empty(T, R, dtype=torch.float32, device=dev)
     flags0 = L.LORA_FLAG_SEPARATE_EXPAND if args.separate_expand else 0
     torch.cuda.synchronize()
@@ -185,7 +185,8 @@ def main():
                                                           L.LORA_MODE_SGMV if sgmv else L.LORA_MODE_BGMV,
                                                           v, ws.buf)))
             if args.separate_expand:
-                calls.append(("gemm", lambda: L.lora_gemm(x, W, y, T, pr.d_in, pr.d_out, L.dtype_code(wl.dtype))))
+                calls.append(("gemm", lambda: L.lora_gemm(x, W, y, T, pr.d_in, pr.d_out, L.dtype_code(wl.dtype),
+                                                          ws=ws.buf)))
                 calls.append(("expand", lambda: L.lora_expand(v, T, pool, ids,
                                                               L.LORA_MODE_SGMV if sgmv else L.LORA_MODE_BGMV,
                                                               y, ws.buf)))

@@ -148,10 +148,13 @@ lora_status_t lora_pool_clear(const lora_pool_t *pool, int32_t slot, lora_stream
 
 /* ---- workspace ------------------------------------------------------------- */
 
-/* Bytes of workspace needed for batches of up to T rows against a pool of
- * n_slots slots and max_rank, for every entry point below.  Returns 0 on
- * bad arguments. */
-size_t lora_workspace_bytes(int32_t T, int32_t n_slots, int32_t max_rank);
+/* Bytes of workspace for batches of up to T rows against a pool of n_slots
+ * slots and max_rank, for every entry point below.  d_out is the widest
+ * output the workspace serves (0: none): with it the workspace also holds the
+ * fp32 partial sums that let small batches (T <= 4096) split the GEMM over K;
+ * without it those batches run unsplit (the two differ only in fp32 summation
+ * order).  Returns 0 on bad arguments. */
+size_t lora_workspace_bytes(int32_t T, int32_t n_slots, int32_t max_rank, int32_t d_out);
 
 /* Prepare a freshly allocated DEVICE workspace: clears the error word and
  * the internal counters.  Call once after allocation (it is kept valid by
@@ -197,7 +200,8 @@ lora_status_t lora_expand(const float *v, int32_t T, const lora_pool_t *pool, co
 
 /* y = x W (no adapters): x DEVICE [T, d_in], W DEVICE [d_in, d_out],
  * y DEVICE [T, d_out], all of `dtype`; fp32 accumulation, one rounding.
- * ws may be NULL when ws_bytes is 0. */
+ * ws (DEVICE, may be NULL) is scratch for a K split of small batches, used
+ * only if ws_bytes holds the fp32 partials. */
 lora_status_t lora_gemm(const void *x, const void *W, void *y, int32_t T, int32_t d_in,
                         int32_t d_out, lora_dtype_t dtype, void *ws, size_t ws_bytes,
                         lora_stream_t stream);

@@ -28,7 +28,7 @@ inline bool valid_pool(const lora_pool_t *p) {
 inline lora_status_t check_ws(const void *ws, size_t ws_bytes, int32_t T, int32_t n_slots,
                               int32_t max_rank, ws_layout *L) {
     if (!ws || !aligned16(ws)) return LORA_ERR_INVALID_ARGUMENT;
-    *L = make_ws_layout(T, n_slots, max_rank);
+    *L = make_ws_layout(T, n_slots, max_rank, 0);
     if (ws_bytes < L->total) return LORA_ERR_WORKSPACE_TOO_SMALL;
     return LORA_OK;
 }
@@ -112,11 +112,11 @@ lora_status_t lora_pool_clear(const lora_pool_t *pool, int32_t slot, lora_stream
     return launch_pool_clear(*pool, slot, hs(stream));
 }
 
-size_t lora_workspace_bytes(int32_t T, int32_t n_slots, int32_t max_rank) {
+size_t lora_workspace_bytes(int32_t T, int32_t n_slots, int32_t max_rank, int32_t d_out) {
     if (T < 0 || n_slots < 1 || n_slots > kMaxSlots || max_rank < 8 || max_rank > 128 ||
-        (max_rank % 8) != 0)
+        (max_rank % 8) != 0 || d_out < 0 || (d_out % 8) != 0)
         return 0;
-    return make_ws_layout(T, n_slots, max_rank).total;
+    return make_ws_layout(T, n_slots, max_rank, d_out).total;
 }
 
 lora_status_t lora_workspace_init(void *ws, size_t ws_bytes, lora_stream_t stream) {
@@ -175,15 +175,16 @@ lora_status_t lora_expand(const float *v, int32_t T, const lora_pool_t *pool, co
 }
 
 lora_status_t lora_gemm(const void *x, const void *W, void *y, int32_t T, int32_t d_in,
-                        int32_t d_out, lora_dtype_t dtype, void * /*ws*/, size_t /*ws_bytes*/,
+                        int32_t d_out, lora_dtype_t dtype, void *ws, size_t ws_bytes,
                         lora_stream_t stream) {
     if (T < 0 || !valid_dtype(dtype) || d_in <= 0 || d_out <= 0 || (d_in % 8) || (d_out % 8))
         return LORA_ERR_INVALID_ARGUMENT;
     if (T > 0 && (!x || !W || !y || !aligned16(x) || !aligned16(W) || !aligned16(y)))
         return LORA_ERR_INVALID_ARGUMENT;
+    if (ws && !aligned16(ws)) return LORA_ERR_INVALID_ARGUMENT;
     if (T == 0) return LORA_OK;
-    return launch_gemm(x, W, y, T, d_in, d_out, dtype, nullptr, nullptr, nullptr, nullptr, nullptr,
-                       hs(stream));
+    return launch_gemm(x, W, y, T, d_in, d_out, dtype, nullptr, nullptr, nullptr, nullptr,
+                       ws ? static_cast<float *>(ws) : nullptr, ws ? ws_bytes : 0, hs(stream));
 }
 
 lora_status_t lora_gemm_expand(const void *x, const void *W, void *y, int32_t T,
@@ -198,7 +199,7 @@ lora_status_t lora_gemm_expand(const void *x, const void *W, void *y, int32_t T,
     if (T == 0) return LORA_OK;
     const int32_t *perm = (mode == LORA_MODE_SGMV) ? ws_ptr<int32_t>(ws, L.perm) : nullptr;
     return launch_gemm(x, W, y, T, pool->d_in, pool->d_out, pool->dtype, pool, ids, v, perm,
-                       ws_ptr<int32_t>(ws, L.header), hs(stream));
+                       ws_ptr<float>(ws, L.gemm_partial), ws_bytes - L.gemm_partial, hs(stream));
 }
 
 lora_status_t lora_linear_forward(const void *x, const void *W, void *y, int32_t T,
@@ -225,12 +226,13 @@ lora_status_t lora_linear_forward(const void *x, const void *W, void *y, int32_t
     const int32_t *perm = sgmv ? ws_ptr<int32_t>(ws, L.perm) : nullptr;
     if (flags & LORA_FLAG_SEPARATE_EXPAND) {
         st = launch_gemm(x, W, y, T, pool->d_in, pool->d_out, pool->dtype, nullptr, nullptr,
-                         nullptr, nullptr, nullptr, s);
+                         nullptr, nullptr, ws_ptr<float>(ws, L.gemm_partial),
+                         ws_bytes - L.gemm_partial, s);
         if (st != LORA_OK) return st;
         return launch_expand(v, T, *pool, ids, sgmv, y, L, ws, s);
     }
     return launch_gemm(x, W, y, T, pool->d_in, pool->d_out, pool->dtype, pool, ids, v, perm,
-                       ws_ptr<int32_t>(ws, L.header), s);
+                       ws_ptr<float>(ws, L.gemm_partial), ws_bytes - L.gemm_partial, s);
 }
 
 lora_status_t lora_get_device_error(void *ws, size_t ws_bytes, lora_stream_t stream,

@@ -96,6 +96,8 @@ constexpr int32_t kSegTile = 1024;     // rows per segment-builder tile
 constexpr int32_t kMaxKSplit = 16;     // shrink k-split factor bound
 constexpr int32_t kMaxSlots = 16000;   // slots per pool (LDS histogram bound, < 64 KiB)
 constexpr int32_t kErrNone = 0x7fffffff;
+constexpr int32_t kMaxGemmSplit = 16;   // split-K GEMM partial copies
+constexpr int32_t kMaxSplitRows = 4096; // batches up to this many rows get split-K scratch
 
 struct ws_layout {
     size_t header;      // int32[64]: [0] error word (first bad row)
@@ -107,12 +109,13 @@ struct ws_layout {
     size_t tile_hist;   // int32[(n_slots + 1) * n_tiles]
     size_t v;           // fp32[T * max_rank]
     size_t partial;     // fp32[kMaxKSplit * T * max_rank]
+    size_t gemm_partial;  // fp32[kMaxGemmSplit * T * d_out] (split-K GEMM), may be empty
     size_t total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-inline ws_layout make_ws_layout(int32_t T, int32_t n_slots, int32_t max_rank) {
+inline ws_layout make_ws_layout(int32_t T, int32_t n_slots, int32_t max_rank, int32_t d_out) {
     ws_layout L;
     size_t o = 0;
     const size_t t = (size_t)(T > 0 ? T : 1);
@@ -126,6 +129,8 @@ inline ws_layout make_ws_layout(int32_t T, int32_t n_slots, int32_t max_rank) {
     L.tile_hist = o; o = align256(o + 4 * (size_t)(n_slots + 1) * n_tiles);
     L.v = o;         o = align256(o + 4 * t * (size_t)max_rank);
     L.partial = o;   o = align256(o + 4 * (size_t)kMaxKSplit * t * (size_t)max_rank);
+    L.gemm_partial = o;
+    if (d_out > 0 && T > 0 && T <= kMaxSplitRows) o = align256(o + 4 * (size_t)kMaxGemmSplit * t * (size_t)d_out);
     L.total = o;
     return L;
 }
@@ -153,6 +158,6 @@ lora_status_t launch_expand(const float *v, int32_t T, const lora_pool_t &p, con
 lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int32_t d_in,
                           int32_t d_out, int32_t dtype, const lora_pool_t *pool,
                           const int32_t *ids, const float *v, const int32_t *perm,
-                          int32_t *err, hipStream_t s);
+                          float *partial, size_t partial_bytes, hipStream_t s);
 
 }  // namespace lora

@@ -7,29 +7,25 @@
 // that mixes adapters"; "Serving LoRA adapters ...", Step 4: the base layer
 // runs first, then the LoRA output is added).
 //
-// bf16 kernel (gfx950 MFMA, fp32 accumulate):
-//   * 256 x 256 output tile, K step 64, 512 threads = 8 wavefronts in a 2 x 4
-//     grid, 128 x 64 outputs per wavefront = 4 x 2 blocks of
-//     v_mfma_f32_32x32x16_bf16.
-//   * x tile [256][64] and W tile staged in LDS, double-buffered (one barrier
-//     per K step); LDS rows padded to 72 elements so the fragment reads of 32
-//     rows at one column hit distinct banks.
-//   * Both MFMA operands need 8 consecutive k per lane.  x rows already are
-//     k-contiguous; W [d_in][d_out] is n-contiguous, so each thread loads a
-//     4 (k) x 8 (n) block with four 16-byte loads and transposes it in
-//     registers (byte permutes) into 8 columns of 4 k, written to LDS as W^T.
+// bf16 kernel (gfx950, v_mfma_f32_32x32x16_bf16, fp32 accumulate):
+//   * BM x BN output tile (256x256, 256x128, 128x128 or 128x64), 4 wavefronts
+//     in a 2 x 2 grid, each owning (BM/2) x (BN/2) outputs.
+//   * K step BK, NS LDS stages.  Both tiles are loaded with DMA
+//     (global_load_lds: global memory straight into LDS, no registers), stored
+//     unpadded with XOR-swizzled 16-byte chunks; A fragments are ds_read_b128
+//     of x rows, B fragments ds_read_b64_tr_b16 (transposing reads) of the
+//     n-contiguous W tile.
 //   * Rows may be visited through `perm` (segment order), gathering x rows on
 //     load and scattering y rows on store; nothing is materialised.
 //   * Epilogue: fp32 accumulator (+ s_a * sum_j v[t][j] B_a[j][n] for rows
-//     with an adapter; v staged in LDS, B read in rank octets), one rounding
-//     to bf16 (nearest even).
+//     with an adapter, B read in rank octets), one rounding to bf16 (nearest
+//     even), 16-byte stores.
+//   * Split-K (small grids): each workgroup sums a K range and writes fp32
+//     partials in sorted-row order; k_splitk_reduce adds them in split order
+//     (deterministic, no atomics) and applies the same epilogue.
 #include "common.hpp"
 
 namespace lora {
-
-constexpr int GBM = 256, GBN = 256;
-// K step and number of LDS stages of the bf16 kernel (2 x 64 KB).
-constexpr int kGemmBK = 64, kGemmNS = 2;
 
 struct gemm_args {
     const uint16_t *x;
@@ -44,19 +40,25 @@ struct gemm_args {
     const int32_t *ids;
     const float *v;
     int32_t n_tiles_m, n_tiles_n;
+    int32_t splits, k_chunk;       // split-K: number of K ranges and their length
+    float *partial;                // split-K: fp32 [splits][T][N], sorted-row order
 };
 
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs (each
 // with its own L2), so workgroup b runs on XCD b % 8.  Give each XCD a
-// contiguous range of tiles, walked in groups of GROUP_M row tiles (down M
-// first, then across N) so the tiles resident on one XCD share x rows and W
-// columns in its L2.
+// contiguous range of work items, walked in groups of GROUP_M row tiles (down
+// M first, then across N) so the tiles resident on one XCD share x rows and W
+// columns in its L2.  With split-K the split index varies slowest.
 constexpr int kXcds = 8, kGroupM = 8;
 
-__device__ __forceinline__ void tile_of(int b, int total, int n_tiles_m, int n_tiles_n, int &tm, int &tn) {
+__device__ __forceinline__ void tile_of(int b, int total, int n_tiles_m, int n_tiles_n, int &tm,
+                                        int &tn, int &split) {
     const int q = total / kXcds, r = total % kXcds;
     const int x = b % kXcds, slot = b / kXcds;
-    const int v = x * q + min(x, r) + slot;
+    int v = x * q + min(x, r) + slot;
+    const int tiles = n_tiles_m * n_tiles_n;
+    split = v / tiles;
+    v -= split * tiles;
     const int per_group = kGroupM * n_tiles_n;
     const int grp = v / per_group;
     const int first_m = grp * kGroupM;
@@ -72,6 +74,7 @@ __device__ __forceinline__ void tile_of(int b, int total, int n_tiles_m, int n_t
 __device__ __attribute__((aligned(16))) uint4 g_zero16[1];
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
 // One 16-byte-per-lane DMA load from global memory straight into LDS: lane
@@ -86,38 +89,82 @@ __device__ __forceinline__ void dma16(const void *gptr, const void *lds_wave_bas
                  : "memory", "m0");
 }
 
-// XOR swizzles of the 16-byte chunk index inside an LDS row (see the tile
-// layouts below): conflict-free fragment reads for 32 and for 64 LDS banks.
+// XOR swizzles of the 16-byte chunk index inside an LDS row: conflict-free
+// fragment reads for 32 and for 64 LDS banks.
+//   x rows (BK bf16): ds_read_b128 of 16 consecutive rows at one chunk.
+//   W rows (BN bf16): ds_read_b64_tr_b16 of 4 rows x 64 bytes per half-wave.
 template <int BK> __device__ __forceinline__ int swz_x(int r) {
     return BK == 64 ? ((r ^ (r >> 3)) & 7) : (((r >> 2) ^ (r >> 1)) & 3);
 }
-__device__ __forceinline__ int swz_w(int k) {
-    return (0xCA60 >> (4 * (k & 3))) & 0xF;            // 0, 6, 10, 12 for k % 4 = 0..3
+template <int BN> __device__ __forceinline__ int swz_w(int k) {
+    // rows of >= 16 chunks: 0, 6, 10, 12 for k % 4 = 0..3; rows of 8 chunks: 0, 2, 4, 6
+    return BN >= 128 ? ((0xCA60 >> (4 * (k & 3))) & 0xF) : 2 * (k & 3);
 }
 
-// LDS tiles per stage (no padding; rows written by DMA 1 KB at a time):
-//   x: [256 rows][BK] bf16, row chunk c (8 k) stored at slot c ^ swz_x(row)
-//   W: [BK rows (k)][256 n] bf16, row chunk c (8 n) stored at slot c ^ swz_w(k)
-// MFMA A fragments: ds_read_b128 of 8 consecutive k of one x row.
-// MFMA B fragments: two ds_read_b64_tr_b16 per lane, each returning 4
-// consecutive k of one W column from a 4 x 16 block read by 16 lanes.
-template <bool LORA, int BK, int NS>
-__global__ void __launch_bounds__(256, 1) k_gemm_bf16(gemm_args g) {
-    constexpr int XCH = BK / 8;                         // 16-byte chunks per x row
-    constexpr int XSTAGE = GBM * BK, WSTAGE = BK * GBN; // elements per stage
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * (XSTAGE + WSTAGE) > 4 * 32 * 132 * 2 + 4 * GBM * 2
-                                                                  ? NS * (XSTAGE + WSTAGE)
-                                                                  : 4 * 32 * 132 * 2 + 4 * GBM * 2];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1;                  // 2 x 2 wavefronts, 128 x 128 each
-    int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, g.n_tiles_m, g.n_tiles_n, tm, tn);
-    const int m0 = tm * GBM, n0 = tn * GBN;
-    const int K = g.K, N = g.N, T = g.T;
+// s * sum_j v[j] B[j][n..n+8] for one row: G rank octets of slot `id`, 8
+// consecutive columns starting at n (B in rank octets [R/8][N][8]).
+__device__ __forceinline__ void lora_delta8(const uint16_t *b, int32_t id, int32_t R, int32_t N,
+                                            int32_t n, int32_t G, const float *vrow, float *d) {
+    for (int gg = 0; gg < G; ++gg) {
+        const uint16_t *bp = b + ((int64_t)id * R * N + ((int64_t)gg * N + n) * 8);
+        const float4 v0 = *reinterpret_cast<const float4 *>(vrow + gg * 8);
+        const float4 v1 = *reinterpret_cast<const float4 *>(vrow + gg * 8 + 4);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float bf[8];
+            vec16<LORA_BF16>::widen(ldg16(bp + c * 8), bf);
+            float a = d[c];
+            a = fmaf(v0.x, bf[0], a); a = fmaf(v0.y, bf[1], a);
+            a = fmaf(v0.z, bf[2], a); a = fmaf(v0.w, bf[3], a);
+            a = fmaf(v1.x, bf[4], a); a = fmaf(v1.y, bf[5], a);
+            a = fmaf(v1.z, bf[6], a); a = fmaf(v1.w, bf[7], a);
+            d[c] = a;
+        }
+    }
+}
 
-    // DMA plan.  x: the stage is 256 * XCH chunks; wave w issues XI = 256*XCH/256
-    // instructions of 64 chunks, chunk index c = (w * XI + j) * 64 + lane.
-    constexpr int XI = GBM * XCH / 256, WI = BK * 32 / 256;
+// Scheduling pattern for one group of NMFMA MFMAs and the NREAD LDS reads of
+// the next fragments (sched_group_barrier masks: 0x100 LDS read, 0x008 MFMA):
+// the reads go out early, at least two per MFMA.
+template <int NREAD, int NMFMA> __device__ __forceinline__ void sched_interleave() {
+    constexpr int per = (NREAD + NMFMA - 1) / NMFMA > 2 ? (NREAD + NMFMA - 1) / NMFMA : 2;
+#pragma unroll
+    for (int i = 0; i < NMFMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+}
+
+template <int BM, int BN, int BK, int NS> struct gemm_cfg {
+    static constexpr int WM = BM / 2, WN = BN / 2;          // per-wavefront tile
+    static constexpr int RB = WM / 32, CB = WN / 32;        // 32x32 MFMA blocks per wavefront
+    static constexpr int XCH = BK / 8, WCH = BN / 8;        // 16-byte chunks per LDS row
+    static constexpr int XSTAGE = BM * BK, WSTAGE = BK * BN;
+    static constexpr int XI = BM * XCH / 256, WI = BK * WCH / 256;   // DMA instructions per wave
+    static constexpr int SLD = WN + 4;                      // epilogue staging row stride (floats)
+    static constexpr int EPI = 4 * 32 * SLD * 4 + 4 * BM * 4;   // epilogue LDS bytes
+    static constexpr int LDS = NS * (XSTAGE + WSTAGE) * 2 > EPI ? NS * (XSTAGE + WSTAGE) * 2 : EPI;
+};
+
+template <bool LORA, int BM, int BN, int BK, int NS, bool SPLIT>
+__global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
+    typedef gemm_cfg<BM, BN, BK, NS> C;
+    constexpr int WM = C::WM, WN = C::WN, RB = C::RB, CB = C::CB;
+    constexpr int XCH = C::XCH, WCH = C::WCH, XSTAGE = C::XSTAGE, WSTAGE = C::WSTAGE;
+    constexpr int XI = C::XI, WI = C::WI;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[C::LDS / 2];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    int tm, tn, split;
+    tile_of(blockIdx.x, gridDim.x, g.n_tiles_m, g.n_tiles_n, tm, tn, split);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int K = g.K, N = g.N, T = g.T;
+    const int k_begin = SPLIT ? split * g.k_chunk : 0;
+    const int k_end = SPLIT ? min(K, k_begin + g.k_chunk) : K;
+
+    // DMA plan.  x stage: BM rows x XCH chunks; wave w issues XI instructions of
+    // 64 chunks, chunk c = (w * XI + j) * 64 + lane at row c / XCH, slot c % XCH,
+    // holding the row's chunk slot ^ swz_x(row).
     int64_t xrow[XI];
     int xcol[XI];
 #pragma unroll
@@ -129,38 +176,41 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16(gemm_args g) {
         xrow[j] = (t >= 0) ? (int64_t)t * K : -1;
         xcol[j] = 8 * (slot ^ swz_x<BK>(r));
     }
-    // W: the stage is BK rows * 32 chunks; chunk index c = (w * WI + j) * 64 + lane
+    // W stage: BK rows x WCH chunks, chunk c at row c / WCH, slot c % WCH,
+    // holding the row's chunk slot ^ swz_w(row).
     int wrow[WI], wcol[WI];
 #pragma unroll
     for (int j = 0; j < WI; ++j) {
         const int c = (w * WI + j) * 64 + lane;
-        const int k = c >> 5, slot = c & 31;
+        const int k = c / WCH, slot = c % WCH;
         wrow[j] = k;
-        wcol[j] = n0 + 8 * (slot ^ swz_w(k));
+        wcol[j] = n0 + 8 * (slot ^ swz_w<BN>(k));
     }
     auto dma_stage = [&](int kt, int buf) {
         uint16_t *xs = smem + buf * (XSTAGE + WSTAGE);
         uint16_t *wsm = xs + XSTAGE;
-        const int k0 = kt * BK;
+        const int k0 = k_begin + kt * BK;
 #pragma unroll
         for (int j = 0; j < XI; ++j) {
             const int kk = k0 + xcol[j];
-            const void *src = (xrow[j] >= 0 && kk < K) ? (const void *)(g.x + xrow[j] + kk) : (const void *)g_zero16;
+            const void *src = (xrow[j] >= 0 && kk < k_end) ? (const void *)(g.x + xrow[j] + kk)
+                                                             : (const void *)g_zero16;
             dma16(src, xs + (w * XI + j) * 64 * 8);
         }
 #pragma unroll
         for (int j = 0; j < WI; ++j) {
             const int k = k0 + wrow[j];
-            const void *src = (k < K && wcol[j] < N) ? (const void *)(g.W + (int64_t)k * N + wcol[j]) : (const void *)g_zero16;
+            const void *src = (k < k_end && wcol[j] < N) ? (const void *)(g.W + (int64_t)k * N + wcol[j])
+                                                          : (const void *)g_zero16;
             dma16(src, wsm + (w * WI + j) * 64 * 8);
         }
     };
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[RB][CB];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[rb][cb][e] = 0.0f;
 
@@ -168,31 +218,30 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16(gemm_args g) {
     const int fr = lane & 31, fk = lane >> 5;           // A: row within block, k-group
     const int grp = lane >> 4, s16 = lane & 15;         // B: 16-lane group, lane in group
     const int b_kofs = 8 * (grp >> 1) + (s16 >> 2);     // + 16 ks + 4 inst
-    const int b_col = 16 * (grp & 1) + 4 * (s16 & 3);   // + wn*128 + cb*32
+    const int b_col = 16 * (grp & 1) + 4 * (s16 & 3);   // + wn*WN + cb*32
     constexpr int KS = BK / 16;                         // MFMA k-substeps per stage
-    bf16x8_t af[2][4], bfr[2][4];
+    bf16x8_t af[2][RB], bfr[2][CB];
     auto load_frags = [&](int buf, int ks, bf16x8_t *a, bf16x8_t *b) {
         const uint16_t *xs = smem + buf * (XSTAGE + WSTAGE);
         const uint16_t *wsm = xs + XSTAGE;
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            const int r = wm * 128 + rb * 32 + fr;
+        for (int rb = 0; rb < RB; ++rb) {
+            const int r = wm * WM + rb * 32 + fr;
             const int c = (2 * ks + fk) ^ swz_x<BK>(r);
             a[rb] = *reinterpret_cast<const bf16x8_t *>(xs + r * BK + 8 * c);
         }
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            const int col = wn * 128 + cb * 32 + b_col;          // multiple of 4
+        for (int cb = 0; cb < CB; ++cb) {
+            const int col = wn * WN + cb * 32 + b_col;          // multiple of 4
             short4_t h[2];
 #pragma unroll
             for (int inst = 0; inst < 2; ++inst) {
                 const int k = 16 * ks + 4 * inst + b_kofs;
-                const int chunk = (col >> 3) ^ swz_w(k);
-                const uint16_t *addr = wsm + k * GBN + 8 * chunk + (col & 7);
+                const int chunk = (col >> 3) ^ swz_w<BN>(k);
+                const uint16_t *addr = wsm + k * BN + 8 * chunk + (col & 7);
                 h[inst] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_short4_t *)(reinterpret_cast<uintptr_t>(addr)));
             }
-            typedef short short8_t __attribute__((ext_vector_type(8)));
             const short8_t hv = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
             b[cb] = __builtin_bit_cast(bf16x8_t, hv);
         }
@@ -201,28 +250,12 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16(gemm_args g) {
 #pragma unroll
         for (int rb = rb0; rb < rb1; ++rb)
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb)
+            for (int cb = 0; cb < CB; ++cb)
                 acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
     };
-    // Scheduling patterns (sched_group_barrier masks: 0x008 MFMA, 0x100 LDS read).
-    auto interleave_16_12 = [&]() {          // 16 MFMAs; the 12 reads of the next fragments early
-#pragma unroll
-        for (int i = 0; i < 6; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
-    };
-    auto interleave_8_12 = [&]() {           // 8 MFMAs; 12 reads early
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    };
+    constexpr int NREAD = RB + 2 * CB;                  // LDS reads per k-substep
 
-    const int nk = (K + BK - 1) / BK;
+    const int nk = (k_end - k_begin + BK - 1) / BK;
     constexpr int PER = XI + WI;                          // DMA instructions per stage per wave
     auto wait_stage = [&](int ahead) {                    // later stages still in flight
         if (ahead >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PER) : "memory");
@@ -244,8 +277,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16(gemm_args g) {
             const int cur = ks & 1, nxt = cur ^ 1;
             if (ks + 1 < KS) {
                 load_frags(buf, ks + 1, af[nxt], bfr[nxt]);
-                mfmas(af[cur], bfr[cur], 0, 4);
-                interleave_16_12();
+                mfmas(af[cur], bfr[cur], 0, RB);
+                sched_interleave<NREAD, RB * CB>();
             } else {
                 // Stage hand-off, between the two halves of the last MFMAs of
                 // this stage: every wave has finished reading this stage from
@@ -254,7 +287,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16(gemm_args g) {
                 // and the first fragments of stage kt+1 are read under the
                 // second half of the MFMAs (after the last stage they are read
                 // and not used).
-                mfmas(af[cur], bfr[cur], 0, 2);
+                mfmas(af[cur], bfr[cur], 0, RB / 2);
                 __builtin_amdgcn_sched_barrier(0);
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 wait_stage(min(NS - 2, nk - 2 - kt));
@@ -263,8 +296,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16(gemm_args g) {
                 if (kt + NS < nk) dma_stage(kt + NS, buf);
                 __builtin_amdgcn_sched_barrier(0);
                 load_frags((kt + 1) % NS, 0, af[nxt], bfr[nxt]);
-                mfmas(af[cur], bfr[cur], 2, 4);
-                interleave_8_12();
+                mfmas(af[cur], bfr[cur], RB / 2, RB);
+                sched_interleave<NREAD, RB / 2 * CB>();
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -273,23 +306,25 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16(gemm_args g) {
     __syncthreads();
 
     // ---- epilogue ----
-    // Each wavefront moves one 32 x 128 block of its accumulators at a time
-    // through its own LDS area; a lane then owns 8 consecutive columns of 8
-    // rows, adds s * sum_j v[t][j] B[j][n] for rows with an adapter (B read in
-    // rank octets, reused across the lane's rows while they share the slot)
-    // and writes 16-byte rows of y after one rounding.
-    constexpr int SLD = 132;                                      // staged row stride (floats)
+    // Each wavefront moves one 32 x WN block of its accumulators at a time
+    // through its own LDS area; a lane then owns 8 consecutive columns of
+    // several rows and writes them with 16-byte stores after one rounding,
+    // adding s * sum_j v[t][j] B[j][n] for rows with an adapter (B read in
+    // rank octets, reused across a lane's rows while they share the slot).
+    // In split-K mode the staged fp32 rows go to the partial buffer instead.
+    constexpr int SLD = C::SLD;
+    constexpr int QN = WN / 8, RPP = 64 / QN, PASSES = 32 / RPP;
     float *stage = reinterpret_cast<float *>(smem) + w * 32 * SLD;
     int32_t *s_t = reinterpret_cast<int32_t *>(reinterpret_cast<float *>(smem) + 4 * 32 * SLD);
-    int32_t *s_id = s_t + GBM;
-    int32_t *s_gq = s_id + GBM;
-    float *s_sc = reinterpret_cast<float *>(s_gq + GBM);
-    for (int i = tid; i < GBM; i += 256) {
+    int32_t *s_id = s_t + BM;
+    int32_t *s_gq = s_id + BM;
+    float *s_sc = reinterpret_cast<float *>(s_gq + BM);
+    for (int i = tid; i < BM; i += 256) {
         const int p = m0 + i;
         const int32_t t = (p < T) ? perm_row(g.perm, p, T) : -1;
         int32_t id = -1, r = 0;
         float sc = 0.0f;
-        if (LORA && t >= 0) {
+        if (LORA && !SPLIT && t >= 0) {
             const int32_t raw = g.ids[t];
             if (raw >= 0 && raw < g.n_slots) {
                 r = g.rank[raw];
@@ -301,46 +336,49 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16(gemm_args g) {
                 }
             }
         }
-        s_t[i] = t;
+        s_t[i] = SPLIT ? (p < T ? p : -1) : t;
         s_id[i] = id;
         s_gq[i] = (r + 7) >> 3;
         s_sc[i] = sc;
     }
-    const int q = lane & 15, rr = lane >> 4;
-    const int n = n0 + wn * 128 + 8 * q;
+    const int q = lane % QN, rr = lane / QN;
+    const int n = n0 + wn * WN + 8 * q;
     const int R = g.max_rank;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
         __syncthreads();
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 stage[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * SLD + cb * 32 + (lane & 31)] =
                     acc[rb][cb][e];
         __syncthreads();
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            int32_t tk[4], idk[4], gk[4];
-            float sk[4];
+        for (int half = 0; half < (PASSES + 3) / 4; ++half) {
+            constexpr int KR = PASSES < 4 ? PASSES : 4;
+            int32_t tk[KR], idk[KR], gk[KR];
+            float sk[KR];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int i = wm * 128 + rb * 32 + rr + 4 * (k + 4 * half);
+            for (int k = 0; k < KR; ++k) {
+                const int i = wm * WM + rb * 32 + rr + RPP * (k + 4 * half);
                 tk[k] = s_t[i];
                 idk[k] = s_id[i];
                 gk[k] = s_gq[i];
                 sk[k] = s_sc[i];
             }
-            float d[4][8];
+            float d[KR][8];
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
+            for (int k = 0; k < KR; ++k)
 #pragma unroll
                 for (int c = 0; c < 8; ++c) d[k][c] = 0.0f;
-            if (LORA && n < N) {
-                const bool same = idk[0] >= 0 && idk[1] == idk[0] && idk[2] == idk[0] && idk[3] == idk[0];
+            if (LORA && !SPLIT && n < N) {
+                bool same = idk[0] >= 0;
+#pragma unroll
+                for (int k = 1; k < KR; ++k) same = same && idk[k] == idk[0];
                 int G = 0;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) G = (idk[k] >= 0 && gk[k] > G) ? gk[k] : G;
+                for (int k = 0; k < KR; ++k) G = (idk[k] >= 0 && gk[k] > G) ? gk[k] : G;
                 for (int gg = 0; gg < G; ++gg) {
                     uint4 bq[8];
                     if (same) {
@@ -349,7 +387,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16(gemm_args g) {
                         for (int c = 0; c < 8; ++c) bq[c] = ldg16(bp + c * 8);
                     }
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
+                    for (int k = 0; k < KR; ++k) {
                         if (idk[k] < 0 || gg >= gk[k]) continue;
                         if (!same) {
                             const uint16_t *bp = g.b + ((int64_t)idk[k] * R * N + ((int64_t)gg * N + n) * 8);
@@ -374,11 +412,17 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16(gemm_args g) {
                 }
             }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
+            for (int k = 0; k < KR; ++k) {
                 if (tk[k] < 0 || n >= N) continue;
-                const float *src = stage + (rr + 4 * (k + 4 * half)) * SLD + 8 * q;
+                const float *src = stage + (rr + RPP * (k + 4 * half)) * SLD + 8 * q;
                 const float4 o0 = *reinterpret_cast<const float4 *>(src);
                 const float4 o1 = *reinterpret_cast<const float4 *>(src + 4);
+                if (SPLIT) {
+                    float *dst = g.partial + ((int64_t)split * T + tk[k]) * N + n;
+                    *reinterpret_cast<float4 *>(dst) = o0;
+                    *reinterpret_cast<float4 *>(dst + 4) = o1;
+                    continue;
+                }
                 float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
                 if (LORA && idk[k] >= 0) {
 #pragma unroll
@@ -390,10 +434,41 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16(gemm_args g) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// fp32 kernel (plain FMA, no reduced-precision path): 64 x 64 tile, K step
-// 16, 256 threads with 4 x 4 outputs each, same epilogue semantics.
-// ---------------------------------------------------------------------------
+// Split-K reduction: y[t][n..n+8] = bf16( sum_s partial[s][p][n..n+8]
+//                                         (+ s_a * sum_j v[t][j] B_a[j][n..]) ).
+// One thread per (sorted row p, 8 columns); partials are summed in split order.
+template <bool LORA>
+__global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g) {
+    const int p = blockIdx.y;
+    const int n = (blockIdx.x * 256 + threadIdx.x) * 8;
+    if (n >= g.N) return;
+    const int T = g.T, N = g.N;
+    const int32_t t = perm_row(g.perm, p, T);
+    if (t < 0) return;
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int sidx = 0; sidx < g.splits; ++sidx) {
+        const float *src = g.partial + ((int64_t)sidx * T + p) * N + n;
+        const float4 a = *reinterpret_cast<const float4 *>(src);
+        const float4 b = *reinterpret_cast<const float4 *>(src + 4);
+        o[0] += a.x; o[1] += a.y; o[2] += a.z; o[3] += a.w;
+        o[4] += b.x; o[5] += b.y; o[6] += b.z; o[7] += b.w;
+    }
+    if (LORA) {
+        const int32_t raw = g.ids[t];
+        if (raw >= 0 && raw < g.n_slots) {
+            const int32_t r = g.rank[raw];
+            if (r > 0) {
+                float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                lora_delta8(g.b, raw, g.max_rank, N, n, (r + 7) >> 3, g.v + (int64_t)t * g.max_rank, d);
+                const float sc = g.scale[raw];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) o[c] = fmaf(sc, d[c], o[c]);
+            }
+        }
+    }
+    stg16(g.y + (int64_t)t * N + n, vec16<LORA_BF16>::narrow(o));
+}
+
 struct gemm_f32_args {
     const float *x;
     const float *W;
@@ -482,10 +557,61 @@ __global__ void __launch_bounds__(256) k_gemm_f32(gemm_f32_args g) {
     }
 }
 
+// Tile configuration and K split for one bf16 GEMM shape.
+struct gemm_plan {
+    int bm, bn, splits, k_chunk;
+};
+
+static int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Largest tile that still gives close to one workgroup per CU; for grids that
+// stay small (few token rows), split K so that about 256 workgroups run, if
+// the workspace holds the fp32 partials.
+static gemm_plan plan_gemm(int T, int K, int N, size_t partial_bytes) {
+    static const int cfg[4][2] = {{256, 256}, {256, 128}, {128, 128}, {128, 64}};
+    for (int c = 0; c < 4; ++c) {
+        const int tiles = ceil_div(T, cfg[c][0]) * ceil_div(N, cfg[c][1]);
+        if (tiles >= 224) return {cfg[c][0], cfg[c][1], 1, K};
+    }
+    // small grid: 256x128 tiles (decode-sized T) or 128x128, split over K
+    const int bm = T <= 256 ? 256 : 128, bn = 128;
+    const int tiles = ceil_div(T, bm) * ceil_div(N, bn);
+    int splits = ceil_div(256, tiles);
+    const int max_by_k = K / 256 > 0 ? K / 256 : 1;
+    if (splits > max_by_k) splits = max_by_k;
+    if (splits > 16) splits = 16;
+    while (splits > 1 && (size_t)splits * T * N * 4 > partial_bytes) --splits;
+    if (splits <= 1) {
+        const int t2 = ceil_div(T, 128) * ceil_div(N, 64);
+        return t2 > tiles ? gemm_plan{128, 64, 1, K} : gemm_plan{bm, bn, 1, K};
+    }
+    int k_chunk = ceil_div(ceil_div(K, splits), 64) * 64;
+    splits = ceil_div(K, k_chunk);
+    return {bm, bn, splits, k_chunk};
+}
+
+template <int BM, int BN>
+static void launch_cfg(const gemm_args &g, bool lora, bool split, hipStream_t s) {
+    constexpr int BK = 64, NS = 2;
+    const int grid = g.n_tiles_m * g.n_tiles_n * (split ? g.splits : 1);
+    if (split) {
+        hipLaunchKernelGGL((k_gemm_bf16<false, BM, BN, BK, NS, true>), dim3(grid), dim3(256), 0, s, g);
+        const dim3 rgrid((g.N + 2047) / 2048, g.T);
+        if (lora)
+            hipLaunchKernelGGL(k_splitk_reduce<true>, rgrid, dim3(256), 0, s, g);
+        else
+            hipLaunchKernelGGL(k_splitk_reduce<false>, rgrid, dim3(256), 0, s, g);
+    } else if (lora) {
+        hipLaunchKernelGGL((k_gemm_bf16<true, BM, BN, BK, NS, false>), dim3(grid), dim3(256), 0, s, g);
+    } else {
+        hipLaunchKernelGGL((k_gemm_bf16<false, BM, BN, BK, NS, false>), dim3(grid), dim3(256), 0, s, g);
+    }
+}
+
 lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int32_t d_in,
                           int32_t d_out, int32_t dtype, const lora_pool_t *pool,
                           const int32_t *ids, const float *v, const int32_t *perm,
-                          int32_t * /*err*/, hipStream_t s) {
+                          float *partial, size_t partial_bytes, hipStream_t s) {
     if (dtype == LORA_BF16) {
         gemm_args g;
         g.x = (const uint16_t *)x;
@@ -502,13 +628,17 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
         g.max_rank = pool ? pool->max_rank : 0;
         g.ids = ids;
         g.v = v;
-        g.n_tiles_n = (d_out + GBN - 1) / GBN;
-        g.n_tiles_m = (T + GBM - 1) / GBM;
-        const int tiles = g.n_tiles_m * g.n_tiles_n;
-        if (pool)
-            hipLaunchKernelGGL((k_gemm_bf16<true, kGemmBK, kGemmNS>), dim3(tiles), dim3(256), 0, s, g);
-        else
-            hipLaunchKernelGGL((k_gemm_bf16<false, kGemmBK, kGemmNS>), dim3(tiles), dim3(256), 0, s, g);
+        const gemm_plan pl = plan_gemm(T, d_in, d_out, partial ? partial_bytes : 0);
+        g.n_tiles_m = ceil_div(T, pl.bm);
+        g.n_tiles_n = ceil_div(d_out, pl.bn);
+        g.splits = pl.splits;
+        g.k_chunk = pl.k_chunk;
+        g.partial = partial;
+        const bool split = pl.splits > 1;
+        if (pl.bm == 256 && pl.bn == 256) launch_cfg<256, 256>(g, pool != nullptr, split, s);
+        else if (pl.bm == 256) launch_cfg<256, 128>(g, pool != nullptr, split, s);
+        else if (pl.bn == 128) launch_cfg<128, 128>(g, pool != nullptr, split, s);
+        else launch_cfg<128, 64>(g, pool != nullptr, split, s);
     } else {
         gemm_f32_args g;
         g.x = (const float *)x;

@@ -95,7 +95,7 @@ def load(path: str = LIB_PATH):
         "lora_pool_create": (c_i32, [P(lora_pool_t), c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
         "lora_pool_upload": (c_i32, [P(lora_pool_t), c_i32, c_vp, c_i32, c_vp, c_i32, c_i32, c_f, c_vp]),
         "lora_pool_clear": (c_i32, [P(lora_pool_t), c_i32, c_vp]),
-        "lora_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32]),
+        "lora_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32]),
         "lora_workspace_init": (c_i32, [c_vp, c_sz, c_vp]),
         "lora_segments_view": (c_i32, [c_vp, c_sz, c_i32, c_i32, c_i32, P(lora_segments_t)]),
         "lora_build_segments": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_vp, c_sz, c_vp]),
@@ -179,8 +179,8 @@ def lora_pool_clear(pool, slot, stream=None):
 
 
 # ---- workspace / segments -----------------------------------------------------
-def lora_workspace_bytes(T, n_slots, max_rank) -> int:
-    return int(load().lora_workspace_bytes(T, n_slots, max_rank))
+def lora_workspace_bytes(T, n_slots, max_rank, d_out=0) -> int:
+    return int(load().lora_workspace_bytes(T, n_slots, max_rank, d_out))
 
 
 def lora_workspace_init(ws, stream=None):
@@ -211,9 +211,10 @@ def lora_expand(v, T, pool, ids, mode, y, ws, stream=None):
                            ws.numel() * ws.element_size(), _stream(stream)), "lora_expand")
 
 
-def lora_gemm(x, W, y, T, d_in, d_out, dtype, stream=None):
-    _ok(load().lora_gemm(_ptr(x), _ptr(W), _ptr(y), T, d_in, d_out, dtype, None, 0, _stream(stream)),
-        "lora_gemm")
+def lora_gemm(x, W, y, T, d_in, d_out, dtype, ws=None, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _ok(load().lora_gemm(_ptr(x), _ptr(W), _ptr(y), T, d_in, d_out, dtype, _ptr(ws), nbytes,
+                         _stream(stream)), "lora_gemm")
 
 
 def lora_gemm_expand(x, W, y, T, pool, ids, v, mode, ws, stream=None):
@@ -266,10 +267,10 @@ class AdapterPool:
 
 
 class Workspace:
-    """A device workspace sized for (T, n_slots, max_rank), initialised."""
+    """A device workspace sized for (T, n_slots, max_rank, d_out), initialised."""
 
-    def __init__(self, T, n_slots, max_rank, device="cuda", stream=None):
-        n = lora_workspace_bytes(T, n_slots, max_rank)
+    def __init__(self, T, n_slots, max_rank, d_out=0, device="cuda", stream=None):
+        n = lora_workspace_bytes(T, n_slots, max_rank, d_out)
         if n == 0:
             raise LoraError(LORA_ERR_INVALID_ARGUMENT, "lora_workspace_bytes")
         self.T, self.n_slots, self.max_rank = T, n_slots, max_rank

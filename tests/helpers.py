@@ -70,7 +70,7 @@ def assert_parity(y_gpu: torch.Tensor, y_ref: np.ndarray, dtype: torch.dtype, wh
 def forward(wl, proj, pool, ids_dev, mode, flags=0, ws=None, y=None):
     x = wl.x_for(proj)
     if ws is None:
-        ws = L.Workspace(wl.T, wl.n_slots, wl.max_rank)
+        ws = L.Workspace(wl.T, wl.n_slots, wl.max_rank, max(p.d_out for p in wl.projections))
     if y is None:
         y = torch.empty(wl.T, proj.d_out, dtype=wl.dtype, device=x.device)
     L.lora_linear_forward(x, proj.W, y, wl.T, pool.pool, ids_dev, mode, flags, ws.buf)

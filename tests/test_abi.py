@@ -60,6 +60,7 @@ def test_workspace_bytes():
     assert L.lora_workspace_bytes(-1, 4, 8) == 0
     assert L.lora_workspace_bytes(10, 0, 8) == 0
     assert L.lora_workspace_bytes(10, 4, 7) == 0
+    assert L.lora_workspace_bytes(10, 4, 8, 12) == 0
     n0 = L.lora_workspace_bytes(0, 4, 8)
     n1 = L.lora_workspace_bytes(1000, 4, 8)
     n2 = L.lora_workspace_bytes(100000, 4, 8)
@@ -67,6 +68,9 @@ def test_workspace_bytes():
     # holds at least v [T, max_rank] fp32, perm [T] and the k-split partials
     assert n2 >= 100000 * (8 * 4 + 4 + 16 * 8 * 4)
     assert n2 % 256 == 0
+    # with d_out: room for 16 fp32 partial copies of a small batch's output
+    assert L.lora_workspace_bytes(256, 4, 8, 4096) >= L.lora_workspace_bytes(256, 4, 8) + 16 * 256 * 4096 * 4
+    assert L.lora_workspace_bytes(100000, 4, 8, 4096) == n2
 
 
 def test_validation_returns_before_launch(lib):

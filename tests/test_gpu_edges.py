@@ -48,9 +48,9 @@ class Case:
                 self.pool.upload(s, self.A[s], self.B[s], r, self.alphas[s])
         self.ids_dev = torch.as_tensor(self.ids, device="cuda")
 
-    def run(self, mode=L.LORA_MODE_AUTO, flags=0, T=None):
+    def run(self, mode=L.LORA_MODE_AUTO, flags=0, T=None, split_scratch=True):
         T = self.T if T is None else T
-        ws = L.Workspace(max(T, 1), self.n_slots, self.R)
+        ws = L.Workspace(max(T, 1), self.n_slots, self.R, self.d_out if split_scratch else 0)
         y = torch.full((max(T, 1), self.d_out), 7.0, dtype=self.dtype, device="cuda")
         L.lora_linear_forward(self.x, self.W, y, T, self.pool.pool, self.ids_dev, mode, flags, ws.buf)
         torch.cuda.synchronize()
@@ -201,7 +201,7 @@ def test_modes_agree():
 
 def test_host_errors_enqueue_nothing():
     c = Case(T=16, d_in=64, d_out=64, ranks=[8], max_rank=8, dtype=torch.bfloat16, seed=11)
-    ws = L.Workspace(16, 1, 8)
+    ws = L.Workspace(16, 1, 8, 64)
     y = torch.empty(16, 64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(L.LoraError) as e:
         c.pool.upload(0, c.A[0], c.B[0], 9, 1.0)
@@ -216,3 +216,34 @@ def test_host_errors_enqueue_nothing():
     with pytest.raises(L.LoraError) as e:
         L.lora_linear_forward(c.x[:, 1:], c.W, y, 16, c.pool.pool, c.ids_dev, 0, 0, ws.buf)
     assert e.value.status == L.LORA_ERR_INVALID_ARGUMENT      # misaligned x
+
+
+@pytest.mark.parametrize("T,d_in,d_out", [(256, 4096, 4096), (64, 1032, 520), (2240, 4096, 1024),
+                                          (300, 2048, 264), (4096, 512, 256)])
+def test_split_k_and_tile_configs(T, d_in, d_out):
+    """Small batches split the GEMM over K when the workspace holds the fp32
+    partials; with and without that scratch the results agree with the oracle
+    (and with each other to fp32 summation order), for every tile shape the
+    planner picks."""
+    c = Case(T=T, d_in=d_in, d_out=d_out, ranks=[16, 8, 16, 4], max_rank=16, dtype=torch.bfloat16,
+             seed=12)
+    ref = c.oracle()
+    outs = []
+    for split_scratch in (True, False):
+        for mode in MODES:
+            for flags in FLAGS:
+                y, ws = c.run(mode, flags, split_scratch=split_scratch)
+                assert_parity(y, ref, torch.bfloat16, "T=%d split=%s mode=%d flags=%d"
+                              % (T, split_scratch, mode, flags))
+                outs.append(y.float())
+    for y in outs[1:]:
+        assert torch.max((y - outs[0]).abs() / (1 + outs[0].abs())).item() <= 2 ** -6
+    # the plain GEMM entry point, with and without scratch
+    ws = torch.empty(L.lora_workspace_bytes(T, 1, 8, d_out), dtype=torch.uint8, device="cuda")
+    y1 = torch.empty(T, d_out, dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty(T, d_out, dtype=torch.bfloat16, device="cuda")
+    L.lora_gemm(c.x, c.W, y1, T, d_in, d_out, L.LORA_BF16, ws=ws)
+    L.lora_gemm(c.x, c.W, y2, T, d_in, d_out, L.LORA_BF16)
+    base = c.oracle(ids=np.full(T, -1, np.int32))
+    assert_parity(y1, base, torch.bfloat16, "gemm split")
+    assert_parity(y2, base, torch.bfloat16, "gemm")

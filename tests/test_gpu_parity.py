@@ -85,7 +85,7 @@ def _check_shrink_expand(wl, proj, pool, ids, rows, ref):
     sref = np.asarray([scales[wl.ids[t]] if wl.ids[t] >= 0 else 0.0 for t in rows])[:, None]
     dref = ref["delta"] * sref
     for mname in ("bgmv", "sgmv"):
-        ws = L.Workspace(wl.T, wl.n_slots, wl.max_rank)
+        ws = L.Workspace(wl.T, wl.n_slots, wl.max_rank, proj.d_out)
         if mname == "sgmv":
             L.lora_build_segments(ids, wl.T, wl.n_slots, wl.max_rank, ws.buf)
         v = torch.full((wl.T, wl.max_rank), float("nan"), dtype=torch.float32, device="cuda")
@@ -142,7 +142,7 @@ def test_layer_sets_sampled(name, max_rows):
     wl = make_workload(name, device="cuda")
     ids = torch.as_tensor(wl.ids, device="cuda")
     rows = sample_rows(wl, max_rows=max_rows)
-    ws = L.Workspace(wl.T, wl.n_slots, wl.max_rank)
+    ws = L.Workspace(wl.T, wl.n_slots, wl.max_rank, max(p.d_out for p in wl.projections))
     rows_dev = torch.as_tensor(rows, device="cuda")
     for k, proj in enumerate(wl.projections):
         pool = build_pool(wl, proj)
