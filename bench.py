@@ -140,82 +140,90 @@ def main():
             L.lora_linear_forward(s["xs"][pr.x_group], s["Ws"][k], s["ys"][k], T, s["pools"][k], ids,
                                   mode, fl, ws.buf)
 
-    # default step counts: about 2 s of timed work
-    t0 = time.perf_counter()
+    # The step is captured into HIP graphs (one graph replays every working-set
+    # copy once) so host-side launch overhead is not part of the timing.
+    graph_steps = n_sets if n_sets > 1 else 4
     step(0)
     torch.cuda.synchronize()
-    est = max(time.perf_counter() - t0, 1e-5)
-    steps = args.steps if args.steps is not None else int(min(2000, max(10, 2.0 / est)))
-    warmup = args.warmup if args.warmup is not None else int(min(100, max(3, steps // 10)))
+    g_step = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_step):
+        for i in range(graph_steps):
+            step(i)
+    torch.cuda.synchronize()
 
-    for i in range(warmup):
-        step(i)
+    # default step counts: about 2 s of timed work
+    t0 = time.perf_counter()
+    g_step.replay()
+    torch.cuda.synchronize()
+    est = max((time.perf_counter() - t0) / graph_steps, 1e-6)
+    steps = args.steps if args.steps is not None else int(min(20000, max(20, 2.0 / est)))
+    steps = max(graph_steps, (steps // graph_steps) * graph_steps)
+    warmup = args.warmup if args.warmup is not None else int(min(200, max(graph_steps, steps // 10)))
+    warmup = max(graph_steps, (warmup // graph_steps) * graph_steps)
+
+    for _ in range(warmup // graph_steps):
+        g_step.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        step(i)
+    for _ in range(steps // graph_steps):
+        g_step.replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = 1e3 * elapsed / steps
     value = T * steps / elapsed
     assert L.lora_get_device_error(ws.buf) == -1
 
-    # ---- per-kernel durations: the same step decomposed, HIP events between calls ----
-    # (events are recorded on torch's current stream, the stream the kernels run on)
+    # ---- per-kernel durations ----
+    # Each entry point of the decomposed step (segments, shrink, GEMM with the
+    # fused expand) is captured alone, REPS launches in a row over the rotated
+    # working sets, and timed with HIP events around graph replays on the
+    # current stream -- the stream the kernels run on.
     names = (["segments"] if sgmv else []) + ["shrink", "gemm_expand"]
     if args.separate_expand:
         names = (["segments"] if sgmv else []) + ["shrink", "gemm", "expand"]
-    k_steps = max(5, min(steps, 200))
-    per = {n: [] for n in names}
-    st = torch.cuda.current_stream()
+    smode = L.LORA_MODE_SGMV if sgmv else L.LORA_MODE_BGMV
 
-    def decomposed(i, record):
-        s = sets[i % n_sets]
-        marks = []
-        ev = lambda: (torch.cuda.Event(enable_timing=True) if record else None)
-        e = ev()
-        if record:
-            e.record(st)
-        for k, pr in enumerate(wl.projections):
-            x, W, y, pool = s["xs"][pr.x_group], s["Ws"][k], s["ys"][k], s["pools"][k]
-            calls = []
-            if sgmv and k == 0:
-                calls.append(("segments", lambda: L.lora_build_segments(ids, T, wl.n_slots, R, ws.buf)))
-            calls.append(("shrink", lambda: L.lora_shrink(x, T, pool, ids,
-                                                          L.LORA_MODE_SGMV if sgmv else L.LORA_MODE_BGMV,
-                                                          v, ws.buf)))
-            if args.separate_expand:
-                calls.append(("gemm", lambda: L.lora_gemm(x, W, y, T, pr.d_in, pr.d_out, L.dtype_code(wl.dtype),
-                                                          ws=ws.buf)))
-                calls.append(("expand", lambda: L.lora_expand(v, T, pool, ids,
-                                                              L.LORA_MODE_SGMV if sgmv else L.LORA_MODE_BGMV,
-                                                              y, ws.buf)))
-            else:
-                calls.append(("gemm_expand", lambda: L.lora_gemm_expand(x, W, y, T, pool, ids, v,
-                                                                        L.LORA_MODE_SGMV if sgmv else L.LORA_MODE_BGMV,
-                                                                        ws.buf)))
-            for name, fn in calls:
-                fn()
-                e2 = ev()
-                if record:
-                    e2.record(st)
-                    marks.append((name, k, e, e2))
-                e = e2
-        return marks
+    def call(name, k, i):
+        s_ = sets[i % n_sets]
+        pr = wl.projections[k]
+        x, W, y, pool = s_["xs"][pr.x_group], s_["Ws"][k], s_["ys"][k], s_["pools"][k]
+        if name == "segments":
+            L.lora_build_segments(ids, T, wl.n_slots, R, ws.buf)
+        elif name == "shrink":
+            L.lora_shrink(x, T, pool, ids, smode, v, ws.buf)
+        elif name == "gemm":
+            L.lora_gemm(x, W, y, T, pr.d_in, pr.d_out, L.dtype_code(wl.dtype), ws=ws.buf)
+        elif name == "expand":
+            L.lora_expand(v, T, pool, ids, smode, y, ws.buf)
+        else:
+            L.lora_gemm_expand(x, W, y, T, pool, ids, v, smode, ws.buf)
 
-    for i in range(3):
-        decomposed(i, False)
-    torch.cuda.synchronize()
-    all_marks = []
-    for i in range(k_steps):
-        all_marks += decomposed(i, True)
-    torch.cuda.synchronize()
-    per_launch = {}          # (name, proj) -> list of ms
-    for name, k, a, b in all_marks:
-        per_launch.setdefault((name, k), []).append(a.elapsed_time(b))
-    kernel_ms = {}           # name -> average ms per step (summed over projections)
-    for (name, k), lst in per_launch.items():
-        kernel_ms[name] = kernel_ms.get(name, 0.0) + sum(lst) / len(lst)
+    if sgmv:
+        L.lora_build_segments(ids, T, wl.n_slots, R, ws.buf)
+    per_launch = {}          # (name, proj) -> average ms per launch
+    reps = max(n_sets, 8)
+    for name in names:
+        projs = [0] if name == "segments" else range(len(wl.projections))
+        for k in projs:
+            for i in range(2):
+                call(name, k, i)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(reps):
+                    call(name, k, i)
+            g.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            n_rep = max(3, int(0.2 / max(est, 1e-6) / reps))
+            e0.record()
+            for _ in range(n_rep):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            per_launch[(name, k)] = e0.elapsed_time(e1) / (n_rep * reps)
+            del g
 
     # ---- algorithmic bytes / flops per launch ----
     ids_np = wl.ids
@@ -248,10 +256,9 @@ def main():
             if (name, k) not in per_launch:
                 continue
             b_, f_ = work(name, pr)
-            ms = sum(per_launch[(name, k)]) / len(per_launch[(name, k)])
             tot_b += b_
             tot_f += f_
-            tot_ms += ms
+            tot_ms += per_launch[(name, k)]
         breakdown[name] = dict(us_per_step=round(1e3 * tot_ms, 3), bytes=tot_b, flops=tot_f,
                                gbs=round(tot_b / (tot_ms * 1e-3) / 1e9, 1) if tot_ms else None,
                                tflops=round(tot_f / (tot_ms * 1e-3) / 1e12, 2) if tot_ms else None)

@@ -93,6 +93,7 @@ __device__ __forceinline__ void flag_bad_row(int32_t *err, int32_t row) {
 // Workspace layout (host side).  Regions are 256-byte aligned.
 // ---------------------------------------------------------------------------
 constexpr int32_t kSegTile = 1024;     // rows per segment-builder tile
+constexpr int32_t kShrinkRows = 32;    // rows of one segment per grouped-shrink work block
 constexpr int32_t kMaxKSplit = 16;     // shrink k-split factor bound
 constexpr int32_t kMaxSlots = 16000;   // slots per pool (LDS histogram bound, < 64 KiB)
 constexpr int32_t kErrNone = 0x7fffffff;
@@ -105,6 +106,8 @@ struct ws_layout {
     size_t seg_id;      // int32[n_slots]
     size_t seg_start;   // int32[n_slots + 1]
     size_t n_seg;       // int32[1]
+    size_t blk_start;   // int32[n_slots + 2]: first shrink work block of each segment
+    size_t blk_seg;     // int32[ceil(T / kShrinkRows) + n_slots]: segment of each work block
     size_t perm;        // int32[T]
     size_t tile_hist;   // int32[(n_slots + 1) * n_tiles]
     size_t v;           // fp32[T * max_rank]
@@ -125,6 +128,8 @@ inline ws_layout make_ws_layout(int32_t T, int32_t n_slots, int32_t max_rank, in
     L.seg_id = o;    o = align256(o + 4 * (size_t)(n_slots + 1));
     L.seg_start = o; o = align256(o + 4 * (size_t)(n_slots + 2));
     L.n_seg = o;     o = align256(o + 4);
+    L.blk_start = o; o = align256(o + 4 * (size_t)(n_slots + 2));
+    L.blk_seg = o;   o = align256(o + 4 * ((t + kShrinkRows - 1) / kShrinkRows + (size_t)n_slots + 1));
     L.perm = o;      o = align256(o + 4 * t);
     L.tile_hist = o; o = align256(o + 4 * (size_t)(n_slots + 1) * n_tiles);
     L.v = o;         o = align256(o + 4 * t * (size_t)max_rank);

@@ -90,7 +90,9 @@ __global__ void __launch_bounds__(1024) k_seg_scan(int32_t *__restrict__ tile_hi
                                                    int32_t *__restrict__ offsets,
                                                    int32_t *__restrict__ seg_id,
                                                    int32_t *__restrict__ seg_start,
-                                                   int32_t *__restrict__ n_seg) {
+                                                   int32_t *__restrict__ n_seg,
+                                                   int32_t *__restrict__ blk_start,
+                                                   int32_t *__restrict__ blk_seg) {
     extern __shared__ int32_t s_off[];        // [n_slots + 2]
     __shared__ int32_t s_wave[48];
     const int32_t nb = n_slots + 1;
@@ -122,21 +124,30 @@ __global__ void __launch_bounds__(1024) k_seg_scan(int32_t *__restrict__ tile_hi
     __syncthreads();
     for (int32_t k = threadIdx.x; k <= nb; k += blockDim.x) offsets[k] = s_off[k];
 
-    // Compaction of non-empty adapter keys (k >= 1) in ascending order.
-    int32_t seg_carry = 0;
+    // Compaction of non-empty adapter keys (k >= 1) in ascending order, and
+    // the shrink work table: segment i covers work blocks
+    // [blk_start[i], blk_start[i+1]) of kShrinkRows rows each.
+    int32_t seg_carry = 0, blk_carry = 0;
     for (int32_t k0 = 1; k0 < nb; k0 += blockDim.x) {
         const int32_t k = k0 + threadIdx.x;
-        const int32_t nonempty = (k < nb) ? (s_off[k + 1] > s_off[k]) : 0;
-        int32_t tot;
+        const int32_t len = (k < nb) ? (s_off[k + 1] - s_off[k]) : 0;
+        const int32_t nonempty = len > 0;
+        const int32_t nblk = (len + kShrinkRows - 1) / kShrinkRows;
+        int32_t tot, btot;
         const int32_t idx = block_exclusive_scan(nonempty, s_wave, &tot) + seg_carry;
+        const int32_t bidx = block_exclusive_scan(nblk, s_wave, &btot) + blk_carry;
         if (nonempty) {
             seg_id[idx] = k - 1;
             seg_start[idx] = s_off[k];
+            blk_start[idx] = bidx;
+            for (int32_t b = 0; b < nblk; ++b) blk_seg[bidx + b] = idx;
         }
         seg_carry += tot;
+        blk_carry += btot;
     }
     if (threadIdx.x == 0) {
         seg_start[seg_carry] = T;
+        blk_start[seg_carry] = blk_carry;
         *n_seg = seg_carry;
     }
 }
@@ -174,7 +185,8 @@ lora_status_t launch_segments(const int32_t *ids, int32_t T, int32_t n_slots, co
                        tile_hist, n_tiles, err);
     hipLaunchKernelGGL(k_seg_scan, dim3(1), dim3(1024), lds_off, s, tile_hist, n_slots, n_tiles, T,
                        ws_ptr<int32_t>(ws, L.offsets), ws_ptr<int32_t>(ws, L.seg_id),
-                       ws_ptr<int32_t>(ws, L.seg_start), ws_ptr<int32_t>(ws, L.n_seg));
+                       ws_ptr<int32_t>(ws, L.seg_start), ws_ptr<int32_t>(ws, L.n_seg),
+                       ws_ptr<int32_t>(ws, L.blk_start), ws_ptr<int32_t>(ws, L.blk_seg));
     hipLaunchKernelGGL(k_seg_scatter, dim3(n_tiles), dim3(kSegTile), 0, s, ids, T, n_slots,
                        tile_hist, n_tiles, ws_ptr<int32_t>(ws, L.perm));
     return hip_status(hipGetLastError());

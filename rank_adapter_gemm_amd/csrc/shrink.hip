@@ -8,17 +8,16 @@
 // form walks adapter-contiguous segments so one read of A serves a segment.
 //
 // Two kernels:
-//  * k_shrink_rows  (BGMV): one workgroup per token row; x[t] is read once
-//    with 16-byte coalesced loads, the slot's A^T rows (only the first r)
-//    are gathered, each lane keeps per-rank partial sums, which are reduced
-//    across the wavefront with a transposing butterfly of cross-lane swaps
-//    and then across the 4 wavefronts through LDS.  fp32 or bf16 inputs.
-//  * k_shrink_sgmv  (SGMV, bf16): rows in segment order (through perm), 16
-//    rows per MFMA tile; for each adapter present in the tile, one bf16 MFMA
-//    K-loop with the tile's other rows masked to zero, so all adapters of the
-//    tile accumulate into one fp32 result.  The K dimension is split over the
-//    4 wavefronts (LDS reduction) and optionally over workgroups (partials,
-//    then a fixed-order reduction: deterministic).
+//  * k_shrink_rows  (BGMV): one 512-thread workgroup per token row; x[t] is
+//    read once with 16-byte coalesced loads, the slot's A^T rows (only the
+//    first r) are gathered in batches of independent loads, each lane keeps
+//    per-rank partial sums, which are reduced across the wavefront with a
+//    transposing butterfly of cross-lane swaps and then across the 8
+//    wavefronts through LDS.  fp32 or bf16 inputs.
+//  * k_shrink_grouped (SGMV, bf16): work blocks of up to 32 rows of one
+//    adapter segment (rows through perm), MFMA 16x16x32 with fp32 accumulate;
+//    K is split over the 4 wavefronts (LDS reduction) and optionally over
+//    workgroups (partials, then a fixed-order reduction: deterministic).
 #include "common.hpp"
 
 namespace lora {
@@ -64,7 +63,7 @@ __device__ __forceinline__ int owned_index(int lane) {
 }
 
 template <int DT, int RM>
-__global__ void __launch_bounds__(256) k_shrink_rows(const typename elem<DT>::T *__restrict__ x,
+__global__ void __launch_bounds__(512) k_shrink_rows(const typename elem<DT>::T *__restrict__ x,
                                                      int32_t T, int32_t d_in,
                                                      const typename elem<DT>::T *__restrict__ a,
                                                      const int32_t *__restrict__ rank,
@@ -74,7 +73,9 @@ __global__ void __launch_bounds__(256) k_shrink_rows(const typename elem<DT>::T 
                                                      float *__restrict__ v, int32_t *err) {
     typedef typename elem<DT>::T E;
     constexpr int VN = vec16<DT>::n;
-    __shared__ float s_red[4][RM];
+    constexpr int NW = 8;                                 // wavefronts per workgroup
+    constexpr int RC = RM < 16 ? RM : (RM > 32 ? 8 : 16); // rank rows per batch of loads
+    __shared__ float s_red[NW][RM];
     const int p = blockIdx.x;
     const int t = perm_row(perm, p, T);
     if (t < 0) return;
@@ -85,7 +86,7 @@ __global__ void __launch_bounds__(256) k_shrink_rows(const typename elem<DT>::T 
     if (tid == 0 && ((id < -1 || id >= n_slots) || (in_range && r == 0))) flag_bad_row(err, t);
     float *vt = v + (size_t)t * max_rank;
     if (r <= 0) {
-        for (int j = tid; j < max_rank; j += 256) vt[j] = 0.0f;
+        for (int j = tid; j < max_rank; j += NW * 64) vt[j] = 0.0f;
         return;
     }
     const E *xt = x + (size_t)t * d_in;
@@ -94,143 +95,209 @@ __global__ void __launch_bounds__(256) k_shrink_rows(const typename elem<DT>::T 
 #pragma unroll
     for (int j = 0; j < RM; ++j) acc[j] = 0.0f;
     const int nvec = d_in / VN;
-    for (int kv = tid; kv < nvec; kv += 256) {
+    for (int kv = tid; kv < nvec; kv += NW * 64) {
+        const uint4 xq = ldg16(xt + (size_t)kv * VN);
         float xf[VN];
-        vec16<DT>::widen(ldg16(xt + (size_t)kv * VN), xf);
 #pragma unroll
-        for (int j = 0; j < RM; ++j) {
-            if (j < r) {
-                float af[VN];
-                vec16<DT>::widen(ldg16(At + (size_t)j * d_in + (size_t)kv * VN), af);
+        for (int c = 0; c < RM; c += RC) {
+            if (c < r) {                                  // uniform: rows left in this slot
+                // RC independent loads in flight; rows past the rank re-read
+                // row r-1 (a cache hit) and are masked out below.
+                uint4 aq[RC];
 #pragma unroll
-                for (int e = 0; e < VN; ++e) acc[j] = fmaf(xf[e], af[e], acc[j]);
+                for (int j = 0; j < RC; ++j) {
+                    const int row = min(c + j, r - 1);
+                    aq[j] = ldg16(At + (size_t)row * d_in + (size_t)kv * VN);
+                }
+                if (c == 0) vec16<DT>::widen(xq, xf);
+#pragma unroll
+                for (int j = 0; j < RC; ++j) {
+                    float af[VN];
+                    vec16<DT>::widen(aq[j], af);
+                    float d = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < VN; ++e) d = fmaf(xf[e], af[e], d);
+                    acc[c + j] += (c + j < r) ? d : 0.0f;
+                }
             }
         }
     }
     constexpr int NR = RM < 64 ? RM : 64;
 #pragma unroll
     for (int c = 0; c < RM / NR; ++c) {
-        const float s = wave_reduce_transpose<NR>(acc + c * NR, lane);
-        if (lane < NR) s_red[wave][c * NR + owned_index<NR>(lane)] = s;
+        const float sum = wave_reduce_transpose<NR>(acc + c * NR, lane);
+        if (lane < NR) s_red[wave][c * NR + owned_index<NR>(lane)] = sum;
     }
     __syncthreads();
-    for (int j = tid; j < max_rank; j += 256) {
-        float s = 0.0f;
-        if (j < r) s = (s_red[0][j] + s_red[1][j]) + (s_red[2][j] + s_red[3][j]);
-        vt[j] = s;
+    for (int j = tid; j < max_rank; j += NW * 64) {
+        float sum = 0.0f;
+        if (j < r) {
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) sum += s_red[w2][j];
+        }
+        vt[j] = sum;
     }
 }
 
 // ---------------------------------------------------------------------------
-// SGMV shrink, bf16, MFMA 16x16x32 (fp32 accumulate).
-//   grid.x: 16-row tiles of sorted positions; grid.y: k-split chunks.
-//   Operand mapping per lane l (wavefront of 64): A operand = x rows,
-//   row (l % 16), 8 consecutive k of k-group (l / 16); B operand = A^T rows
-//   (one rank per column), column (l % 16) = rank within the 16-rank chunk,
-//   the same 8 k.  Output: column (l % 16), rows 4 (l / 16) + 0..3.
+// SGMV shrink, bf16: a grouped product over adapter segments.
+//   Work block w (grid.x) covers up to kShrinkRows consecutive sorted rows of
+//   ONE segment (the block table comes from the segment builder); grid.y
+//   splits K.  The 4 wavefronts take interleaved 32-wide k steps, batching the
+//   loads of U steps before the MFMAs (v_mfma_f32_16x16x32_bf16, fp32
+//   accumulate), and reduce in LDS in a fixed order.  Rows of a segment share
+//   one adapter, so its A^T rows are read once per block (L1/L2 hits across
+//   waves).  Extra workgroups past the work blocks write the zero v rows of
+//   the base-only block (and of bad ids) so every row of v is defined.
+//   Operand mapping per lane l: A operand = x row (l % 16) of a 16-row block,
+//   8 consecutive k of k-group (l / 16); B operand = A^T row (rank) (l % 16) of
+//   a 16-rank chunk, the same 8 k.  Output: rank (l % 16), rows 4 (l / 16) + q.
 // ---------------------------------------------------------------------------
-template <int RC>   // number of 16-rank column chunks
-__global__ void __launch_bounds__(256) k_shrink_sgmv(const uint16_t *__restrict__ x, int32_t T,
-                                                     int32_t d_in, const uint16_t *__restrict__ a,
-                                                     const int32_t *__restrict__ rank,
-                                                     int32_t n_slots, int32_t max_rank,
-                                                     const int32_t *__restrict__ ids,
-                                                     const int32_t *__restrict__ perm,
-                                                     int32_t k_chunk, float *__restrict__ v,
-                                                     float *__restrict__ partial, int32_t *err) {
-    __shared__ float s_acc[4][16][RC * 16 + 1];
-    __shared__ int32_t s_id[16], s_r[16], s_t[16];
+template <int RCH>   // 16-rank chunks
+__global__ void __launch_bounds__(256) k_shrink_grouped(
+    const uint16_t *__restrict__ x, int32_t T, int32_t d_in, const uint16_t *__restrict__ a,
+    const int32_t *__restrict__ rank, int32_t max_rank, const int32_t *__restrict__ perm,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ seg_id,
+    const int32_t *__restrict__ seg_start, const int32_t *__restrict__ n_seg_p,
+    const int32_t *__restrict__ blk_start, const int32_t *__restrict__ blk_seg,
+    int32_t n_work_upper, int32_t k_chunk,
+    float *__restrict__ v, float *__restrict__ partial, int32_t *err) {
+    constexpr int U = RCH <= 2 ? 4 : 2;                  // k steps per batch of loads
+    constexpr int BR = kShrinkRows;                      // 32 rows = two 16-row MFMA blocks
+    __shared__ float s_acc[4][BR][RCH * 16 + 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int p0 = blockIdx.x * 16;
-    if (tid < 16) {
-        const int p = p0 + tid;
-        int32_t t = -1, id = -1, r = 0;
-        if (p < T) t = perm_row(perm, p, T);
-        if (t >= 0) {
-            const int32_t raw = ids[t];
-            const bool in_range = raw >= 0 && raw < n_slots;
-            r = in_range ? rank[raw] : 0;
-            if (r > 0) id = raw;
-            if (blockIdx.y == 0 && ((raw < -1 || raw >= n_slots) || (in_range && r == 0)))
-                flag_bad_row(err, t);
-        }
-        s_t[tid] = t;
-        s_id[tid] = id;
-        s_r[tid] = r;
-    }
-    __syncthreads();
-
-    const int k_begin = blockIdx.y * k_chunk;
-    const int k_end = min(d_in, k_begin + k_chunk);
-    const int row = lane & 15, kg = lane >> 4;
-    const int my_t = s_t[row];
-    f32x4_t acc[RC];
-#pragma unroll
-    for (int c = 0; c < RC; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    uint32_t done = 0;                               // processed row slots (uniform)
-    for (int guard = 0; guard < 16; ++guard) {
-        int first = -1;
-        for (int i = 0; i < 16; ++i)
-            if (!((done >> i) & 1) && s_id[i] >= 0) { first = i; break; }
-        if (first < 0) break;
-        const int32_t aid = s_id[first];
-        uint32_t mask = 0;
-        for (int i = 0; i < 16; ++i)
-            if (s_id[i] == aid) mask |= 1u << i;
-        done |= mask;
-        const int32_t r = s_r[first];
-        const bool row_on = (mask >> row) & 1;
-        const uint16_t *xrow = x + (size_t)(row_on ? my_t : 0) * d_in;
-        const uint16_t *At = a + (size_t)aid * max_rank * d_in;
-        for (int k0 = k_begin + wave * 32; k0 < k_end; k0 += 4 * 32) {
-            const int kk = k0 + kg * 8;
-            uint4 xq = make_uint4(0, 0, 0, 0);
-            if (row_on && kk < k_end) xq = ldg16(xrow + kk);
-            const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, xq);
-#pragma unroll
-            for (int c = 0; c < RC; ++c) {
-                const int j = c * 16 + row;                 // rank = output column
-                uint4 aq = make_uint4(0, 0, 0, 0);
-                if (j < r && kk < k_end) aq = ldg16(At + (size_t)j * d_in + kk);
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    xa, __builtin_bit_cast(bf16x8_t, aq), acc[c], 0, 0, 0);
+    const int wid = blockIdx.x;
+    if (wid >= n_work_upper) {
+        // base-only block: sorted positions [0, offsets[1]) get v = 0
+        if (blockIdx.y != 0) return;
+        const int p0 = (wid - n_work_upper) * BR;
+        const int pend = min(offsets[1], p0 + BR);
+        for (int e = tid; e < BR * max_rank; e += 256) {
+            const int p = p0 + e / max_rank, j = e % max_rank;
+            if (p < pend) {
+                const int32_t t = perm_row(perm, p, T);
+                if (t >= 0) v[(size_t)t * max_rank + j] = 0.0f;
             }
         }
+        return;
     }
-    // cross-wave reduction of the k-subsets
+    const int nseg = *n_seg_p;
+    if (nseg <= 0 || wid >= blk_start[nseg]) return;
+    const int lo = blk_seg[wid];                         // this block's segment
+    const int32_t aid = seg_id[lo];
+    const int p0 = seg_start[lo] + (wid - blk_start[lo]) * BR;
+    const int pend = min(seg_start[lo + 1], p0 + BR);
+    const int32_t r = rank[aid];
+    const int k_begin = blockIdx.y * k_chunk;
+    const int k_end = min(d_in, k_begin + k_chunk);
+
+    const int lr = lane & 15, kg = lane >> 4;
+    // this lane's two x rows (row blocks 0 and 1); invalid rows read the
+    // block's first row and are zeroed
+    const int32_t t_first = perm_row(perm, p0, T);
+    int64_t xoff[2];
+    uint32_t xm[2];                                      // all-ones for a real row, else 0
 #pragma unroll
-    for (int c = 0; c < RC; ++c)
+    for (int rb = 0; rb < 2; ++rb) {
+        const int p = p0 + rb * 16 + lr;
+        const int32_t t = (p < pend) ? perm_row(perm, p, T) : -1;
+        xm[rb] = t >= 0 ? ~0u : 0u;
+        xoff[rb] = (int64_t)(t >= 0 ? t : (t_first >= 0 ? t_first : 0)) * d_in;
+    }
+    const uint16_t *At = a + (size_t)aid * max_rank * d_in;
+    int64_t aoff[RCH];
+    uint32_t am[RCH];                                    // all-ones for a rank below r, else 0
 #pragma unroll
-        for (int q = 0; q < 4; ++q) s_acc[wave][4 * kg + q][c * 16 + row] = acc[c][q];
+    for (int rc = 0; rc < RCH; ++rc) {
+        const int j = rc * 16 + lr;
+        am[rc] = j < r ? ~0u : 0u;
+        aoff[rc] = (int64_t)min(j, r > 0 ? r - 1 : 0) * d_in;
+    }
+    f32x4_t acc[2][RCH];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int rc = 0; rc < RCH; ++rc) acc[rb][rc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    if (r > 0) {
+        for (int kb = k_begin + wave * 32; kb < k_end; kb += 4 * 32 * U) {
+            uint4 xq[U][2], aq[U][RCH];
+            uint32_t km[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = kb + u * 128 + 8 * kg;
+                km[u] = k < k_end ? ~0u : 0u;
+                const int kc = k < k_end ? k : k_begin;
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) xq[u][rb] = ldg16(x + xoff[rb] + kc);
+#pragma unroll
+                for (int rc = 0; rc < RCH; ++rc) aq[u][rc] = ldg16(At + aoff[rc] + kc);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    const uint32_t m = km[u] & xm[rb];
+                    xq[u][rb] = make_uint4(xq[u][rb].x & m, xq[u][rb].y & m, xq[u][rb].z & m, xq[u][rb].w & m);
+                }
+#pragma unroll
+                for (int rc = 0; rc < RCH; ++rc) {
+                    const uint32_t m = km[u] & am[rc];
+                    aq[u][rc] = make_uint4(aq[u][rc].x & m, aq[u][rc].y & m, aq[u][rc].z & m, aq[u][rc].w & m);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int rc = 0; rc < RCH; ++rc)
+                        acc[rb][rc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, xq[u][rb]),
+                            __builtin_bit_cast(bf16x8_t, aq[u][rc]), acc[rb][rc], 0, 0, 0);
+        }
+    } else if (blockIdx.y == 0 && tid < BR && p0 + tid < pend) {
+        flag_bad_row(err, perm_row(perm, p0 + tid, T));     // segment of an empty slot
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int rc = 0; rc < RCH; ++rc)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) s_acc[wave][rb * 16 + 4 * kg + q][rc * 16 + lr] = acc[rb][rc][q];
     __syncthreads();
-    for (int e = tid; e < 16 * max_rank; e += 256) {
+    for (int e = tid; e < BR * max_rank; e += 256) {
         const int i = e / max_rank, j = e % max_rank;
         const int p = p0 + i;
-        if (p >= T) continue;
-        float s = 0.0f;
-        if (j < RC * 16) s = (s_acc[0][i][j] + s_acc[1][i][j]) + (s_acc[2][i][j] + s_acc[3][i][j]);
-        if (partial)
-            partial[((size_t)blockIdx.y * T + p) * max_rank + j] = s;
-        else if (s_t[i] >= 0)
-            v[(size_t)s_t[i] * max_rank + j] = s;
+        if (p >= pend) continue;
+        float sum = 0.0f;
+        if (j < RCH * 16) sum = (s_acc[0][i][j] + s_acc[1][i][j]) + (s_acc[2][i][j] + s_acc[3][i][j]);
+        if (partial) {
+            partial[((size_t)blockIdx.y * T + p) * max_rank + j] = sum;
+        } else {
+            const int32_t t = perm_row(perm, p, T);
+            if (t >= 0) v[(size_t)t * max_rank + j] = sum;
+        }
     }
 }
 
-// v[perm[p]][j] = sum over k-split chunks, in chunk order.
+// v[perm[p]][j] = sum over k-split chunks, in chunk order, for the adapter
+// rows (sorted positions from offsets[1] on).
 __global__ void __launch_bounds__(256) k_shrink_reduce(const float *__restrict__ partial,
                                                        int32_t n_split, int32_t T,
                                                        int32_t max_rank,
                                                        const int32_t *__restrict__ perm,
+                                                       const int32_t *__restrict__ offsets,
                                                        float *__restrict__ v) {
     const size_t n = (size_t)T * max_rank;
-    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n;
+    const size_t e0 = (size_t)offsets[1] * max_rank;
+    for (size_t e = e0 + blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n;
          e += (size_t)gridDim.x * blockDim.x) {
         const int p = (int)(e / max_rank), j = (int)(e % max_rank);
-        float s = 0.0f;
-        for (int c = 0; c < n_split; ++c) s += partial[(size_t)c * n + e];
+        float sum = 0.0f;
+        for (int c = 0; c < n_split; ++c) sum += partial[(size_t)c * n + e];
         const int t = perm_row(perm, p, T);
-        if (t >= 0) v[(size_t)t * max_rank + j] = s;
+        if (t >= 0) v[(size_t)t * max_rank + j] = sum;
     }
 }
 
@@ -241,7 +308,7 @@ static void launch_rows(const void *x, int32_t T, const lora_pool_t &p, const in
     const E *xe = (const E *)x;
     const E *ae = (const E *)p.a;
 #define LORA_SHRINK_ROWS(RMV)                                                                   \
-    hipLaunchKernelGGL((k_shrink_rows<DT, RMV>), dim3(T), dim3(256), 0, s, xe, T, p.d_in, ae,   \
+    hipLaunchKernelGGL((k_shrink_rows<DT, RMV>), dim3(T), dim3(512), 0, s, xe, T, p.d_in, ae,   \
                        p.rank, p.n_slots, p.max_rank, ids, perm, v, err)
     if (p.max_rank <= 8) LORA_SHRINK_ROWS(8);
     else if (p.max_rank <= 16) LORA_SHRINK_ROWS(16);
@@ -260,10 +327,13 @@ lora_status_t launch_shrink(const void *x, int32_t T, const lora_pool_t &p, cons
         else launch_rows<LORA_BF16>(x, T, p, ids, perm, v, err, s);
         return hip_status(hipGetLastError());
     }
-    // SGMV bf16: choose a k-split so that the grid has enough workgroups.
-    const int32_t tiles = (T + 15) / 16;
-    int32_t split = 1;
-    while (split < kMaxKSplit && tiles * split < 1024 && p.d_in / (split * 2) >= 256) split *= 2;
+    // SGMV bf16: grouped over segment blocks; split K so that about 512
+    // workgroups have work.
+    const int32_t row_blocks = (T + kShrinkRows - 1) / kShrinkRows;
+    const int32_t n_work_upper = row_blocks + (T < p.n_slots ? T : p.n_slots);
+    int32_t split = (512 + row_blocks) / (row_blocks + 1);
+    if (split > kMaxKSplit) split = kMaxKSplit;
+    while (split > 1 && p.d_in / split < 256) --split;
     int32_t k_chunk = (p.d_in + split - 1) / split;
     k_chunk = (k_chunk + 31) / 32 * 32;
     split = (p.d_in + k_chunk - 1) / k_chunk;
@@ -271,26 +341,31 @@ lora_status_t launch_shrink(const void *x, int32_t T, const lora_pool_t &p, cons
     const uint16_t *xe = (const uint16_t *)x;
     const uint16_t *ae = (const uint16_t *)p.a;
     const int rc = (p.max_rank + 15) / 16;
-#define LORA_SHRINK_SGMV(RCV)                                                                    \
-    hipLaunchKernelGGL((k_shrink_sgmv<RCV>), dim3(tiles, split), dim3(256), 0, s, xe, T, p.d_in, \
-                       ae, p.rank, p.n_slots, p.max_rank, ids, perm, k_chunk, v, partial, err)
+    const int32_t *offsets = ws_ptr<int32_t>(ws, L.offsets);
+    const dim3 grid(n_work_upper + row_blocks, split);
+#define LORA_SHRINK_GROUPED(RCV)                                                                  \
+    hipLaunchKernelGGL((k_shrink_grouped<RCV>), grid, dim3(256), 0, s, xe, T, p.d_in, ae, p.rank, \
+                       p.max_rank, perm, offsets, ws_ptr<int32_t>(ws, L.seg_id),                  \
+                       ws_ptr<int32_t>(ws, L.seg_start), ws_ptr<int32_t>(ws, L.n_seg),            \
+                       ws_ptr<int32_t>(ws, L.blk_start), ws_ptr<int32_t>(ws, L.blk_seg),          \
+                       n_work_upper, k_chunk, v, partial, err)
     switch (rc) {
-        case 1: LORA_SHRINK_SGMV(1); break;
-        case 2: LORA_SHRINK_SGMV(2); break;
-        case 3: LORA_SHRINK_SGMV(3); break;
-        case 4: LORA_SHRINK_SGMV(4); break;
-        case 5: LORA_SHRINK_SGMV(5); break;
-        case 6: LORA_SHRINK_SGMV(6); break;
-        case 7: LORA_SHRINK_SGMV(7); break;
-        default: LORA_SHRINK_SGMV(8); break;
+        case 1: LORA_SHRINK_GROUPED(1); break;
+        case 2: LORA_SHRINK_GROUPED(2); break;
+        case 3: LORA_SHRINK_GROUPED(3); break;
+        case 4: LORA_SHRINK_GROUPED(4); break;
+        case 5: LORA_SHRINK_GROUPED(5); break;
+        case 6: LORA_SHRINK_GROUPED(6); break;
+        case 7: LORA_SHRINK_GROUPED(7); break;
+        default: LORA_SHRINK_GROUPED(8); break;
     }
-#undef LORA_SHRINK_SGMV
+#undef LORA_SHRINK_GROUPED
     if (split > 1) {
         size_t n = (size_t)T * p.max_rank;
         int g = (int)((n + 255) / 256);
         if (g > 4096) g = 4096;
         hipLaunchKernelGGL(k_shrink_reduce, dim3(g), dim3(256), 0, s, partial, split, T,
-                           p.max_rank, perm, v);
+                           p.max_rank, perm, offsets, v);
     }
     return hip_status(hipGetLastError());
 }
