@@ -135,6 +135,74 @@ template <int NREAD, int NMFMA> __device__ __forceinline__ void sched_interleave
     }
 }
 
+// The expand on MFMA: acc[rb][cb] += (s_a v[t]) B_a for the rows of each
+// distinct adapter a among a wavefront's 32-row block (found with ballots;
+// other rows get zero operands).  v is split into bf16 high and low parts so
+// the fp32 intermediate keeps about 16 mantissa bits; B octets (8 ranks of
+// one column, 16 bytes) are exactly the MFMA B operand of one lane.
+// Operand mapping of v_mfma_f32_32x32x16_bf16 per lane l: A = row (l % 32),
+// ranks 16 ks + 8 (l / 32) + 0..7; B = column (l % 32), the same ranks.
+template <int RB, int CB>
+__device__ __forceinline__ void lora_pass_impl(const gemm_args &g, f32x16_t (&acc)[RB][CB],
+                                               const int32_t *s_t, const int32_t *s_id, int n0,
+                                               int wrow0, int wcol0, int lane) {
+    const int R = g.max_rank, RO = g.max_rank / 8, N = g.N;
+    const int half = lane >> 5;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int row = wrow0 + rb * 32 + (lane & 31);
+        const int32_t my_id = s_id[row];
+        const int32_t my_t = s_t[row];
+        uint64_t pend = __ballot(my_id >= 0) & 0xffffffffull;
+        while (pend) {
+            const int first = __ffsll((long long)pend) - 1;
+            const int32_t a = __shfl(my_id, first, 64);
+            pend &= ~(__ballot(my_id == a) & 0xffffffffull);
+            const int32_t ra = g.rank[a];
+            const float sa = g.scale[a];
+            const uint32_t vm = (my_id == a) ? ~0u : 0u;
+            const float *vrow = g.v + (int64_t)(my_id == a ? my_t : 0) * R;
+            for (int ks = 0; ks * 16 < ra; ++ks) {
+                const int j0 = 16 * ks + 8 * half;
+                const int oct = 2 * ks + half;
+                const bool j_ok = j0 < R;
+                const float *vp = vrow + (j_ok ? j0 : 0);
+                float4 v0 = *reinterpret_cast<const float4 *>(vp);
+                float4 v1 = *reinterpret_cast<const float4 *>(vp + 4);
+                uint4 bq[CB];
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    const int col = wcol0 + cb * 32 + (lane & 31);
+                    const bool ok = j_ok && col < N;
+                    bq[cb] = ldg16(g.b + ((int64_t)a * R * N + ((int64_t)(ok ? oct : 0) * N + (ok ? col : 0)) * 8));
+                    const uint32_t m = ok ? ~0u : 0u;
+                    bq[cb] = make_uint4(bq[cb].x & m, bq[cb].y & m, bq[cb].z & m, bq[cb].w & m);
+                }
+                const uint32_t m = j_ok ? vm : 0u;
+                float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float f0 = __uint_as_float(__float_as_uint(sa * vv[2 * e]) & m);
+                    const float f1 = __uint_as_float(__float_as_uint(sa * vv[2 * e + 1]) & m);
+                    const uint32_t h0 = f32_to_bf16_bits(f0), h1 = f32_to_bf16_bits(f1);
+                    hi[e] = h0 | (h1 << 16);
+                    lo[e] = f32_to_bf16_bits(f0 - __uint_as_float(h0 << 16)) |
+                            (f32_to_bf16_bits(f1 - __uint_as_float(h1 << 16)) << 16);
+                }
+                const bf16x8_t ahi = __builtin_bit_cast(bf16x8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+                const bf16x8_t alo = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    const bf16x8_t bb = __builtin_bit_cast(bf16x8_t, bq[cb]);
+                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bb, acc[rb][cb], 0, 0, 0);
+                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bb, acc[rb][cb], 0, 0, 0);
+                }
+            }
+        }
+    }
+}
+
 template <int BM, int BN, int BK, int NS> struct gemm_cfg {
     static constexpr int WM = BM / 2, WN = BN / 2;          // per-wavefront tile
     static constexpr int RB = WM / 32, CB = WN / 32;        // 32x32 MFMA blocks per wavefront
@@ -142,7 +210,7 @@ template <int BM, int BN, int BK, int NS> struct gemm_cfg {
     static constexpr int XSTAGE = BM * BK, WSTAGE = BK * BN;
     static constexpr int XI = BM * XCH / 256, WI = BK * WCH / 256;   // DMA instructions per wave
     static constexpr int SLD = WN + 4;                      // epilogue staging row stride (floats)
-    static constexpr int EPI = 4 * 32 * SLD * 4 + 4 * BM * 4;   // epilogue LDS bytes
+    static constexpr int EPI = 4 * 32 * SLD * 4;             // epilogue LDS bytes
     static constexpr int LDS = NS * (XSTAGE + WSTAGE) * 2 > EPI ? NS * (XSTAGE + WSTAGE) * 2 : EPI;
 };
 
@@ -255,6 +323,20 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
     };
     constexpr int NREAD = RB + 2 * CB;                  // LDS reads per k-substep
 
+    // Per-row metadata of the tile (token row; usable adapter slot or -1).
+    __shared__ int32_t s_meta_t[BM], s_meta_id[BM];
+    for (int i = tid; i < BM; i += 256) {
+        const int p = m0 + i;
+        const int32_t t = (p < T) ? perm_row(g.perm, p, T) : -1;
+        int32_t id = -1;
+        if (LORA && !SPLIT && t >= 0) {
+            const int32_t raw = g.ids[t];
+            if (raw >= 0 && raw < g.n_slots && g.rank[raw] > 0) id = raw;
+        }
+        s_meta_t[i] = SPLIT ? (p < T ? p : -1) : t;
+        s_meta_id[i] = id;
+    }
+
     const int nk = (k_end - k_begin + BK - 1) / BK;
     constexpr int PER = XI + WI;                          // DMA instructions per stage per wave
     auto wait_stage = [&](int ahead) {                    // later stages still in flight
@@ -266,6 +348,10 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
 #pragma unroll
     for (int st = 0; st < NS; ++st)
         if (st < nk) dma_stage(st, st);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (LORA && !SPLIT) lora_pass_impl<RB, CB>(g, acc, s_meta_t, s_meta_id, n0, wm * WM, n0 + wn * WN, lane);
     wait_stage(min(NS - 1, nk - 1));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -308,42 +394,14 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
     // ---- epilogue ----
     // Each wavefront moves one 32 x WN block of its accumulators at a time
     // through its own LDS area; a lane then owns 8 consecutive columns of
-    // several rows and writes them with 16-byte stores after one rounding,
-    // adding s * sum_j v[t][j] B[j][n] for rows with an adapter (B read in
-    // rank octets, reused across a lane's rows while they share the slot).
-    // In split-K mode the staged fp32 rows go to the partial buffer instead.
+    // several rows and writes them with 16-byte stores after one rounding (the
+    // low-rank term is already in the accumulators).  In split-K mode the
+    // staged fp32 rows go to the partial buffer instead.
     constexpr int SLD = C::SLD;
     constexpr int QN = WN / 8, RPP = 64 / QN, PASSES = 32 / RPP;
     float *stage = reinterpret_cast<float *>(smem) + w * 32 * SLD;
-    int32_t *s_t = reinterpret_cast<int32_t *>(reinterpret_cast<float *>(smem) + 4 * 32 * SLD);
-    int32_t *s_id = s_t + BM;
-    int32_t *s_gq = s_id + BM;
-    float *s_sc = reinterpret_cast<float *>(s_gq + BM);
-    for (int i = tid; i < BM; i += 256) {
-        const int p = m0 + i;
-        const int32_t t = (p < T) ? perm_row(g.perm, p, T) : -1;
-        int32_t id = -1, r = 0;
-        float sc = 0.0f;
-        if (LORA && !SPLIT && t >= 0) {
-            const int32_t raw = g.ids[t];
-            if (raw >= 0 && raw < g.n_slots) {
-                r = g.rank[raw];
-                if (r > 0) {
-                    id = raw;
-                    sc = g.scale[raw];
-                } else {
-                    r = 0;
-                }
-            }
-        }
-        s_t[i] = SPLIT ? (p < T ? p : -1) : t;
-        s_id[i] = id;
-        s_gq[i] = (r + 7) >> 3;
-        s_sc[i] = sc;
-    }
     const int q = lane % QN, rr = lane / QN;
     const int n = n0 + wn * WN + 8 * q;
-    const int R = g.max_rank;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         __syncthreads();
@@ -355,80 +413,20 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
                     acc[rb][cb][e];
         __syncthreads();
 #pragma unroll
-        for (int half = 0; half < (PASSES + 3) / 4; ++half) {
-            constexpr int KR = PASSES < 4 ? PASSES : 4;
-            int32_t tk[KR], idk[KR], gk[KR];
-            float sk[KR];
-#pragma unroll
-            for (int k = 0; k < KR; ++k) {
-                const int i = wm * WM + rb * 32 + rr + RPP * (k + 4 * half);
-                tk[k] = s_t[i];
-                idk[k] = s_id[i];
-                gk[k] = s_gq[i];
-                sk[k] = s_sc[i];
-            }
-            float d[KR][8];
-#pragma unroll
-            for (int k = 0; k < KR; ++k)
-#pragma unroll
-                for (int c = 0; c < 8; ++c) d[k][c] = 0.0f;
-            if (LORA && !SPLIT && n < N) {
-                bool same = idk[0] >= 0;
-#pragma unroll
-                for (int k = 1; k < KR; ++k) same = same && idk[k] == idk[0];
-                int G = 0;
-#pragma unroll
-                for (int k = 0; k < KR; ++k) G = (idk[k] >= 0 && gk[k] > G) ? gk[k] : G;
-                for (int gg = 0; gg < G; ++gg) {
-                    uint4 bq[8];
-                    if (same) {
-                        const uint16_t *bp = g.b + ((int64_t)idk[0] * R * N + ((int64_t)gg * N + n) * 8);
-#pragma unroll
-                        for (int c = 0; c < 8; ++c) bq[c] = ldg16(bp + c * 8);
-                    }
-#pragma unroll
-                    for (int k = 0; k < KR; ++k) {
-                        if (idk[k] < 0 || gg >= gk[k]) continue;
-                        if (!same) {
-                            const uint16_t *bp = g.b + ((int64_t)idk[k] * R * N + ((int64_t)gg * N + n) * 8);
-#pragma unroll
-                            for (int c = 0; c < 8; ++c) bq[c] = ldg16(bp + c * 8);
-                        }
-                        const float *vp = g.v + (int64_t)tk[k] * R + gg * 8;
-                        const float4 v0 = *reinterpret_cast<const float4 *>(vp);
-                        const float4 v1 = *reinterpret_cast<const float4 *>(vp + 4);
-#pragma unroll
-                        for (int c = 0; c < 8; ++c) {
-                            float bf[8];
-                            vec16<LORA_BF16>::widen(bq[c], bf);
-                            float a = d[k][c];
-                            a = fmaf(v0.x, bf[0], a); a = fmaf(v0.y, bf[1], a);
-                            a = fmaf(v0.z, bf[2], a); a = fmaf(v0.w, bf[3], a);
-                            a = fmaf(v1.x, bf[4], a); a = fmaf(v1.y, bf[5], a);
-                            a = fmaf(v1.z, bf[6], a); a = fmaf(v1.w, bf[7], a);
-                            d[k][c] = a;
-                        }
-                    }
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < KR; ++k) {
-                if (tk[k] < 0 || n >= N) continue;
-                const float *src = stage + (rr + RPP * (k + 4 * half)) * SLD + 8 * q;
-                const float4 o0 = *reinterpret_cast<const float4 *>(src);
-                const float4 o1 = *reinterpret_cast<const float4 *>(src + 4);
-                if (SPLIT) {
-                    float *dst = g.partial + ((int64_t)split * T + tk[k]) * N + n;
-                    *reinterpret_cast<float4 *>(dst) = o0;
-                    *reinterpret_cast<float4 *>(dst + 4) = o1;
-                    continue;
-                }
-                float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-                if (LORA && idk[k] >= 0) {
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) o[c] = fmaf(sk[k], d[k][c], o[c]);
-                }
-                stg16(g.y + (int64_t)tk[k] * N + n, vec16<LORA_BF16>::narrow(o));
+        for (int k = 0; k < PASSES; ++k) {
+            const int i = wm * WM + rb * 32 + rr + RPP * k;
+            const int32_t tk = s_meta_t[i];
+            if (tk < 0 || n >= N) continue;
+            const float *src = stage + (rr + RPP * k) * SLD + 8 * q;
+            const float4 o0 = *reinterpret_cast<const float4 *>(src);
+            const float4 o1 = *reinterpret_cast<const float4 *>(src + 4);
+            if (SPLIT) {
+                float *dst = g.partial + ((int64_t)split * T + tk) * N + n;
+                *reinterpret_cast<float4 *>(dst) = o0;
+                *reinterpret_cast<float4 *>(dst + 4) = o1;
+            } else {
+                const float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+                stg16(g.y + (int64_t)tk * N + n, vec16<LORA_BF16>::narrow(o));
             }
         }
     }
