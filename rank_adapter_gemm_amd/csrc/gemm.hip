@@ -101,28 +101,6 @@ template <int BN> __device__ __forceinline__ int swz_w(int k) {
     return BN >= 128 ? ((0xCA60 >> (4 * (k & 3))) & 0xF) : 2 * (k & 3);
 }
 
-// s * sum_j v[j] B[j][n..n+8] for one row: G rank octets of slot `id`, 8
-// consecutive columns starting at n (B in rank octets [R/8][N][8]).
-__device__ __forceinline__ void lora_delta8(const uint16_t *b, int32_t id, int32_t R, int32_t N,
-                                            int32_t n, int32_t G, const float *vrow, float *d) {
-    for (int gg = 0; gg < G; ++gg) {
-        const uint16_t *bp = b + ((int64_t)id * R * N + ((int64_t)gg * N + n) * 8);
-        const float4 v0 = *reinterpret_cast<const float4 *>(vrow + gg * 8);
-        const float4 v1 = *reinterpret_cast<const float4 *>(vrow + gg * 8 + 4);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            float bf[8];
-            vec16<LORA_BF16>::widen(ldg16(bp + c * 8), bf);
-            float a = d[c];
-            a = fmaf(v0.x, bf[0], a); a = fmaf(v0.y, bf[1], a);
-            a = fmaf(v0.z, bf[2], a); a = fmaf(v0.w, bf[3], a);
-            a = fmaf(v1.x, bf[4], a); a = fmaf(v1.y, bf[5], a);
-            a = fmaf(v1.z, bf[6], a); a = fmaf(v1.w, bf[7], a);
-            d[c] = a;
-        }
-    }
-}
-
 // Scheduling pattern for one group of NMFMA MFMAs and the NREAD LDS reads of
 // the next fragments (sched_group_barrier masks: 0x100 LDS read, 0x008 MFMA):
 // the reads go out early, at least two per MFMA.
@@ -329,11 +307,11 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
         const int p = m0 + i;
         const int32_t t = (p < T) ? perm_row(g.perm, p, T) : -1;
         int32_t id = -1;
-        if (LORA && !SPLIT && t >= 0) {
+        if (LORA && t >= 0) {
             const int32_t raw = g.ids[t];
             if (raw >= 0 && raw < g.n_slots && g.rank[raw] > 0) id = raw;
         }
-        s_meta_t[i] = SPLIT ? (p < T ? p : -1) : t;
+        s_meta_t[i] = t;
         s_meta_id[i] = id;
     }
 
@@ -351,7 +329,11 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (LORA && !SPLIT) lora_pass_impl<RB, CB>(g, acc, s_meta_t, s_meta_id, n0, wm * WM, n0 + wn * WN, lane);
+    // The low-rank term goes into the accumulators before the K loop, while
+    // the first stages load.  (Split-K tiles leave it to the reduction, whose
+    // one-thread-per-row-chunk layout hides the per-row loads of B.)
+    if (LORA && !SPLIT)
+        lora_pass_impl<RB, CB>(g, acc, s_meta_t, s_meta_id, n0, wm * WM, n0 + wn * WN, lane);
     wait_stage(min(NS - 1, nk - 1));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -421,7 +403,7 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
             const float4 o0 = *reinterpret_cast<const float4 *>(src);
             const float4 o1 = *reinterpret_cast<const float4 *>(src + 4);
             if (SPLIT) {
-                float *dst = g.partial + ((int64_t)split * T + tk) * N + n;
+                float *dst = g.partial + ((int64_t)split * T + m0 + i) * N + n;
                 *reinterpret_cast<float4 *>(dst) = o0;
                 *reinterpret_cast<float4 *>(dst + 4) = o1;
             } else {
@@ -432,9 +414,32 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
     }
 }
 
-// Split-K reduction: y[t][n..n+8] = bf16( sum_s partial[s][p][n..n+8]
-//                                         (+ s_a * sum_j v[t][j] B_a[j][n..]) ).
-// One thread per (sorted row p, 8 columns); partials are summed in split order.
+// s * sum_j v[j] B[j][n..n+8] for one row: G rank octets of slot `id`, 8
+// consecutive columns starting at n (B in rank octets [R/8][N][8]).
+__device__ __forceinline__ void lora_delta8(const uint16_t *b, int32_t id, int32_t R, int32_t N,
+                                            int32_t n, int32_t G, const float *vrow, float *d) {
+    for (int gg = 0; gg < G; ++gg) {
+        const uint16_t *bp = b + ((int64_t)id * R * N + ((int64_t)gg * N + n) * 8);
+        const float4 v0 = *reinterpret_cast<const float4 *>(vrow + gg * 8);
+        const float4 v1 = *reinterpret_cast<const float4 *>(vrow + gg * 8 + 4);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float bf[8];
+            vec16<LORA_BF16>::widen(ldg16(bp + c * 8), bf);
+            float a = d[c];
+            a = fmaf(v0.x, bf[0], a); a = fmaf(v0.y, bf[1], a);
+            a = fmaf(v0.z, bf[2], a); a = fmaf(v0.w, bf[3], a);
+            a = fmaf(v1.x, bf[4], a); a = fmaf(v1.y, bf[5], a);
+            a = fmaf(v1.z, bf[6], a); a = fmaf(v1.w, bf[7], a);
+            d[c] = a;
+        }
+    }
+}
+
+// Split-K reduction: y[t][n..n+8] = bf16(sum_s partial[s][p][n..n+8]
+//                                        (+ s_a * sum_j v[t][j] B_a[j][n..n+8]))
+// with t = perm[p]; the partials of one element are summed in split order, so
+// the result does not depend on scheduling.  One thread per (row, 8 columns).
 template <bool LORA>
 __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g) {
     const int p = blockIdx.y;
@@ -571,8 +576,10 @@ static gemm_plan plan_gemm(int T, int K, int N, size_t partial_bytes) {
         const int tiles = ceil_div(T, cfg[c][0]) * ceil_div(N, cfg[c][1]);
         if (tiles >= 224) return {cfg[c][0], cfg[c][1], 1, K};
     }
-    // small grid: 256x128 tiles (decode-sized T) or 128x128, split over K
-    const int bm = T <= 256 ? 256 : 128, bn = 128;
+    // Small grid (decode-sized T): split K.  One 256-row tile covers T <= 256,
+    // so W is read once; narrow 64-column tiles keep the number of fp32
+    // partial copies (written and read back) low for the same grid size.
+    const int bm = T <= 256 ? 256 : 128, bn = T <= 256 ? 64 : 128;
     const int tiles = ceil_div(T, bm) * ceil_div(N, bn);
     int splits = ceil_div(256, tiles);
     const int max_by_k = K / 256 > 0 ? K / 256 : 1;
@@ -588,9 +595,9 @@ static gemm_plan plan_gemm(int T, int K, int N, size_t partial_bytes) {
     return {bm, bn, splits, k_chunk};
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int NS = 2>
 static void launch_cfg(const gemm_args &g, bool lora, bool split, hipStream_t s) {
-    constexpr int BK = 64, NS = 2;
+    constexpr int BK = 64;
     const int grid = g.n_tiles_m * g.n_tiles_n * (split ? g.splits : 1);
     if (split) {
         hipLaunchKernelGGL((k_gemm_bf16<false, BM, BN, BK, NS, true>), dim3(grid), dim3(256), 0, s, g);
@@ -634,7 +641,8 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
         g.partial = partial;
         const bool split = pl.splits > 1;
         if (pl.bm == 256 && pl.bn == 256) launch_cfg<256, 256>(g, pool != nullptr, split, s);
-        else if (pl.bm == 256) launch_cfg<256, 128>(g, pool != nullptr, split, s);
+        else if (pl.bm == 256 && pl.bn == 128) launch_cfg<256, 128>(g, pool != nullptr, split, s);
+        else if (pl.bm == 256) launch_cfg<256, 64, 3>(g, pool != nullptr, split, s);
         else if (pl.bn == 128) launch_cfg<128, 128>(g, pool != nullptr, split, s);
         else launch_cfg<128, 64>(g, pool != nullptr, split, s);
     } else {
