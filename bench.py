@@ -36,8 +36,9 @@ FP32_VALU_PEAK_TFS = 157.3     # fp32 vector
 RIDGE = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
 MALL_BYTES = 256 * 2 ** 20
 CSRC = os.path.join(ROOT, "rank_adapter_gemm_amd", "csrc")
-KERNEL_SOURCE = {"gemm_expand": "gemm.hip", "shrink": "shrink.hip", "segments": "segments.hip",
-                 "expand": "expand.hip"}
+KERNEL_SOURCE = {"gemm_expand": ["gemm.hip"], "shrink": ["shrink.hip"], "segments": ["segments.hip"],
+                 "expand": ["expand.hip"],
+                 "forward": ["api.hip", "gemm.hip", "shrink.hip", "segments.hip", "expand.hip"]}
 
 
 def parse():
@@ -58,7 +59,7 @@ def parse():
 
 def source_sha(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCE[kernel], "common.hpp"):
+    for f in KERNEL_SOURCE[kernel] + ["common.hpp"]:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -225,6 +226,36 @@ def main():
             per_launch[(name, k)] = e0.elapsed_time(e1) / (n_rep * reps)
             del g
 
+    # The step itself calls lora_linear_forward once per projection; time each
+    # of those calls alone the same way (segments already built for k > 0).
+    fwd = {}
+    for k in range(len(wl.projections)):
+        def fcall(i, k=k):
+            s_ = sets[i % n_sets]
+            pr = wl.projections[k]
+            fl = flags0 | (L.LORA_FLAG_SEGMENTS_READY if (sgmv and k > 0) else 0)
+            L.lora_linear_forward(s_["xs"][pr.x_group], s_["Ws"][k], s_["ys"][k], T, s_["pools"][k], ids,
+                                  mode, fl, ws.buf)
+        for i in range(2):
+            fcall(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                fcall(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        n_rep = max(3, int(0.2 / max(est, 1e-6) / reps))
+        e0.record()
+        for _ in range(n_rep):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        fwd[k] = e0.elapsed_time(e1) / (n_rep * reps)
+        del g
+
     # ---- algorithmic bytes / flops per launch ----
     ids_np = wl.ids
     used = np.unique(ids_np[(ids_np >= 0) & (ids_np < wl.n_slots)])
@@ -248,6 +279,18 @@ def main():
             return by, 2 * T * d_in * d_out + 2 * sum_row_r * d_out
         raise KeyError(name)
 
+    def fwd_work(k):
+        """One forward of projection k: x read once (shrink and base product
+        share it), W, y written, the used adapters' A and B, segments."""
+        pr = wl.projections[k]
+        b_g, f_g = work("gemm", pr)
+        b_s, f_s = work("shrink", pr)
+        b_e, f_e = work("expand", pr)
+        by = b_g + (b_s - T * pr.d_in * eb - T * R * 4) + (b_e - T * R * 4 - 2 * T * pr.d_out * eb)
+        if sgmv and k == 0:
+            by += work("segments", pr)[0]
+        return by, f_g + f_s + f_e
+
     breakdown = {}
     for name in names:
         tot_b = tot_f = 0
@@ -262,23 +305,29 @@ def main():
         breakdown[name] = dict(us_per_step=round(1e3 * tot_ms, 3), bytes=tot_b, flops=tot_f,
                                gbs=round(tot_b / (tot_ms * 1e-3) / 1e9, 1) if tot_ms else None,
                                tflops=round(tot_f / (tot_ms * 1e-3) / 1e12, 2) if tot_ms else None)
-    dom = max(names, key=lambda n: breakdown[n]["us_per_step"])
-    launches = len([1 for (n, k) in per_launch if n == dom])
-    bd = breakdown[dom]
-    ai = bd["flops"] / bd["bytes"] if bd["bytes"] else 0.0
-    if wl.dtype == torch.float32 and dom in ("gemm", "gemm_expand"):
-        roof = dict(bound="alu", achieved=bd["tflops"], peak=FP32_VALU_PEAK_TFS, unit="TFLOP/s")
+    # Roofline of the step's dominant launch group: the lora_linear_forward
+    # call of the slowest projection (all the kernels that call enqueues).
+    kd = max(fwd, key=lambda k: fwd[k])
+    by_d, fl_d = fwd_work(kd)
+    t_d = fwd[kd] * 1e-3
+    ai = fl_d / by_d
+    if wl.dtype == torch.float32:
+        roof = dict(bound="alu", achieved=round(fl_d / t_d / 1e12, 2), peak=FP32_VALU_PEAK_TFS, unit="TFLOP/s")
     elif ai >= RIDGE:
-        roof = dict(bound="mfma", achieved=bd["tflops"], peak=MFMA_BF16_PEAK_TFS, unit="TFLOP/s")
+        roof = dict(bound="mfma", achieved=round(fl_d / t_d / 1e12, 2), peak=MFMA_BF16_PEAK_TFS, unit="TFLOP/s")
     else:
-        roof = dict(bound="hbm", achieved=bd["gbs"], peak=HBM_PEAK_GBS, unit="GB/s")
+        roof = dict(bound="hbm", achieved=round(by_d / t_d / 1e9, 1), peak=HBM_PEAK_GBS, unit="GB/s")
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["kernel"] = dom
-    roof["launches_per_step"] = launches
-    roof["avg_launch_us"] = round(bd["us_per_step"] / max(launches, 1), 3)
-    roof["algorithmic_bytes_per_launch"] = int(bd["bytes"] / max(launches, 1))
-    roof["algorithmic_flops_per_launch"] = int(bd["flops"] / max(launches, 1))
-    roof["traffic"] = stored_traffic(dom, args.workload)
+    roof["kernel"] = "forward"
+    roof["projection"] = wl.projections[kd].name
+    roof["launches_per_step"] = 1
+    roof["avg_launch_us"] = round(fwd[kd] * 1e3, 3)
+    roof["algorithmic_bytes_per_launch"] = int(by_d)
+    roof["algorithmic_flops_per_launch"] = int(fl_d)
+    roof["traffic"] = stored_traffic("forward", args.workload, wl.projections[kd].name)
+    breakdown["forward"] = dict(us_per_step=round(1e3 * sum(fwd.values()), 3),
+                                per_projection_us={wl.projections[k].name: round(1e3 * v, 3)
+                                                   for k, v in fwd.items()})
 
     # ---- calibration copy kernel (counter scaling runs) ----
     if args.calib_copy:
@@ -312,7 +361,7 @@ def main():
             "workload": wl.name, "T": T, "projections": [[p.name, p.d_in, p.d_out] for p in wl.projections],
             "n_slots": wl.n_slots, "max_rank": R, "distinct_adapters": int(used.size),
             "mode": ("sgmv" if sgmv else "bgmv") + ("" if args.mode != "auto" else " (auto)"),
-            "expand": "separate" if args.separate_expand else "fused in GEMM epilogue",
+            "expand": "separate" if args.separate_expand else "fused into the base GEMM",
             "cold_sets": n_sets, "working_set_MB": round(set_bytes / 1e6, 1),
         },
         "roofline": roof,
@@ -322,7 +371,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def stored_traffic(kernel: str, workload: str):
+def stored_traffic(kernel: str, workload: str, projection: str | None = None):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -332,7 +381,7 @@ def stored_traffic(kernel: str, workload: str):
         data = json.load(open(path))
     except ValueError:
         return None
-    ent = data.get("%s/%s" % (workload, kernel))
+    ent = data.get("%s/%s" % (workload, kernel) + ("/" + projection if projection else ""))
     if not ent or ent.get("source_sha") != source_sha(kernel):
         return None
     return ent.get("hbm_bytes_per_launch")

@@ -220,6 +220,13 @@ lora_status_t lora_linear_forward(const void *x, const void *W, void *y, int32_t
         st = launch_segments(ids, T, pool->n_slots, L, ws, s);
         if (st != LORA_OK) return st;
     }
+    // Decode-sized BGMV batches: the shrink runs inside the split-K GEMM,
+    // which streams x through LDS anyway (the workspace's v is not written).
+    if (!sgmv && !(flags & LORA_FLAG_SEPARATE_EXPAND) && pool->dtype == LORA_BF16 &&
+        gemm_fused_shrink_ok(T, pool->d_in, pool->d_out, pool->max_rank, ws_bytes - L.gemm_partial))
+        return launch_gemm_fused_shrink(x, W, y, T, pool, ids, ws_ptr<float>(ws, L.partial),
+                                        ws_ptr<int32_t>(ws, L.header), ws_ptr<float>(ws, L.gemm_partial),
+                                        ws_bytes - L.gemm_partial, s);
     float *v = ws_ptr<float>(ws, L.v);
     st = launch_shrink(x, T, *pool, ids, sgmv, v, L, ws, s);
     if (st != LORA_OK) return st;

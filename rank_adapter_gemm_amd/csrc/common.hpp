@@ -160,6 +160,12 @@ lora_status_t launch_shrink(const void *x, int32_t T, const lora_pool_t &p, cons
 lora_status_t launch_expand(const float *v, int32_t T, const lora_pool_t &p, const int32_t *ids,
                             bool sgmv, void *y, const ws_layout &L, void *ws, hipStream_t s);
 // y = x W (+ s v B when pool != nullptr); rows in perm order when perm != nullptr.
+bool gemm_fused_shrink_ok(int32_t T, int32_t d_in, int32_t d_out, int32_t max_rank,
+                          size_t partial_bytes);
+lora_status_t launch_gemm_fused_shrink(const void *x, const void *W, void *y, int32_t T,
+                                       const lora_pool_t *pool, const int32_t *ids, float *vpart,
+                                       int32_t *err, float *partial, size_t partial_bytes,
+                                       hipStream_t s);
 lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int32_t d_in,
                           int32_t d_out, int32_t dtype, const lora_pool_t *pool,
                           const int32_t *ids, const float *v, const int32_t *perm,

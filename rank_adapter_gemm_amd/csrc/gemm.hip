@@ -42,6 +42,9 @@ struct gemm_args {
     int32_t n_tiles_m, n_tiles_n;
     int32_t splits, k_chunk;       // split-K: number of K ranges and their length
     float *partial;                // split-K: fp32 [splits][T][N], sorted-row order
+    const uint16_t *a;             // fused shrink: the pool's A^T [n_slots][max_rank][K]
+    float *vpart;                  // fused shrink: fp32 [splits][T][max_rank] rank partials
+    int32_t *err;                  // fused shrink: the workspace error word
 };
 
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs (each
@@ -181,23 +184,28 @@ __device__ __forceinline__ void lora_pass_impl(const gemm_args &g, f32x16_t (&ac
     }
 }
 
-template <int BM, int BN, int BK, int NS> struct gemm_cfg {
+template <int BM, int BN, int BK, int NS, bool SH> struct gemm_cfg {
     static constexpr int WM = BM / 2, WN = BN / 2;          // per-wavefront tile
     static constexpr int RB = WM / 32, CB = WN / 32;        // 32x32 MFMA blocks per wavefront
     static constexpr int XCH = BK / 8, WCH = BN / 8;        // 16-byte chunks per LDS row
     static constexpr int XSTAGE = BM * BK, WSTAGE = BK * BN;
+    // fused shrink: per stage, 64/R rows x R ranks x BK k of A^T (8 BK chunks)
+    static constexpr int ACH = BK / 8, ASTAGE = SH ? 64 * BK : 0;
+    static constexpr int STAGE = XSTAGE + WSTAGE + ASTAGE;  // uint16 elements per ring stage
     static constexpr int XI = BM * XCH / 256, WI = BK * WCH / 256;   // DMA instructions per wave
+    static constexpr int AI = SH ? BK / 32 : 0;
     static constexpr int SLD = WN + 4;                      // epilogue staging row stride (floats)
     static constexpr int EPI = 4 * 32 * SLD * 4;             // epilogue LDS bytes
-    static constexpr int LDS = NS * (XSTAGE + WSTAGE) * 2 > EPI ? NS * (XSTAGE + WSTAGE) * 2 : EPI;
+    static constexpr int LDS = NS * STAGE * 2 > EPI ? NS * STAGE * 2 : EPI;
 };
 
-template <bool LORA, int BM, int BN, int BK, int NS, bool SPLIT>
+template <bool LORA, int BM, int BN, int BK, int NS, bool SPLIT, bool SH = false>
 __global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
-    typedef gemm_cfg<BM, BN, BK, NS> C;
+    static_assert(!SH || SPLIT, "the fused shrink runs in split-K mode");
+    typedef gemm_cfg<BM, BN, BK, NS, SH> C;
     constexpr int WM = C::WM, WN = C::WN, RB = C::RB, CB = C::CB;
     constexpr int XCH = C::XCH, WCH = C::WCH, XSTAGE = C::XSTAGE, WSTAGE = C::WSTAGE;
-    constexpr int XI = C::XI, WI = C::WI;
+    constexpr int XI = C::XI, WI = C::WI, AI = C::AI, ACH = C::ACH, STAGE = C::STAGE;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[C::LDS / 2];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 1, wn = w & 1;
@@ -232,9 +240,34 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
         wrow[j] = k;
         wcol[j] = n0 + 8 * (slot ^ swz_w<BN>(k));
     }
+    // Fused shrink (decode-sized batches, one M tile): this workgroup also
+    // computes the rank partials v[t][j] over its K range for the rows
+    // t = tn + i * n_tiles_n (i < 64 / R).  The A^T slices of those rows'
+    // adapters ride along in every DMA stage (chunk c: row i, rank j, 8 k),
+    // so x, already in LDS for the base product, is read from HBM once.
+    int64_t arow[AI > 0 ? AI : 1];
+    int acol[AI > 0 ? AI : 1];
+    const int R = g.max_rank;
+    if (SH) {
+#pragma unroll
+        for (int jj = 0; jj < AI; ++jj) {
+            const int c = (w * AI + jj) * 64 + lane;
+            const int i = c / (R * ACH), rem = c % (R * ACH);
+            const int j = rem / ACH, q = rem % ACH;
+            const int t = tn + i * g.n_tiles_n;
+            int64_t off = -1;
+            if (t < T) {
+                const int32_t id = g.ids[t];
+                if (id >= 0 && id < g.n_slots && j < g.rank[id]) off = ((int64_t)id * R + j) * K;
+            }
+            arow[jj] = off;
+            acol[jj] = 8 * q;
+        }
+    }
     auto dma_stage = [&](int kt, int buf) {
-        uint16_t *xs = smem + buf * (XSTAGE + WSTAGE);
+        uint16_t *xs = smem + buf * STAGE;
         uint16_t *wsm = xs + XSTAGE;
+        uint16_t *as = wsm + WSTAGE;
         const int k0 = k_begin + kt * BK;
 #pragma unroll
         for (int j = 0; j < XI; ++j) {
@@ -249,6 +282,13 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
             const void *src = (k < k_end && wcol[j] < N) ? (const void *)(g.W + (int64_t)k * N + wcol[j])
                                                           : (const void *)g_zero16;
             dma16(src, wsm + (w * WI + j) * 64 * 8);
+        }
+#pragma unroll
+        for (int jj = 0; jj < AI; ++jj) {
+            const int k = k0 + acol[jj];
+            const void *src = (arow[jj] >= 0 && k < k_end) ? (const void *)(g.a + arow[jj] + k)
+                                                            : (const void *)g_zero16;
+            dma16(src, as + (w * AI + jj) * 64 * 8);
         }
     };
 
@@ -268,7 +308,7 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
     constexpr int KS = BK / 16;                         // MFMA k-substeps per stage
     bf16x8_t af[2][RB], bfr[2][CB];
     auto load_frags = [&](int buf, int ks, bf16x8_t *a, bf16x8_t *b) {
-        const uint16_t *xs = smem + buf * (XSTAGE + WSTAGE);
+        const uint16_t *xs = smem + buf * STAGE;
         const uint16_t *wsm = xs + XSTAGE;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -316,7 +356,28 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
     }
 
     const int nk = (k_end - k_begin + BK - 1) / BK;
-    constexpr int PER = XI + WI;                          // DMA instructions per stage per wave
+    constexpr int PER = XI + WI + AI;                     // DMA instructions per stage per wave
+    // fused shrink: thread = (row slot i, rank j, 16-k group gq) of a stage
+    const int sh_i = tid / (4 * R), sh_j = (tid >> 2) % R, sh_gq = tid & 3;
+    const int sh_t = SH ? tn + sh_i * g.n_tiles_n : -1;
+    float sh_acc = 0.0f;
+    auto shrink_stage = [&](int buf) {
+        if (!SH || sh_t >= T) return;
+        const uint16_t *xs = smem + buf * STAGE;
+        const uint16_t *as = xs + XSTAGE + WSTAGE;
+        const int r = sh_t - m0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int c = 2 * sh_gq + h;
+            const uint4 xq = *reinterpret_cast<const uint4 *>(xs + r * BK + 8 * (c ^ swz_x<BK>(r)));
+            const uint4 aq = *reinterpret_cast<const uint4 *>(as + ((sh_i * R + sh_j) * ACH + c) * 8);
+            float xf[8], af[8];
+            vec16<LORA_BF16>::widen(xq, xf);
+            vec16<LORA_BF16>::widen(aq, af);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sh_acc = fmaf(xf[e], af[e], sh_acc);
+        }
+    };
     auto wait_stage = [&](int ahead) {                    // later stages still in flight
         if (ahead >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PER) : "memory");
         else if (ahead == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory");
@@ -338,6 +399,7 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     load_frags(0, 0, af[0], bfr[0]);
+    if (SH && nk > 0) shrink_stage(0);
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt % NS;
 #pragma unroll
@@ -364,6 +426,7 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
                 if (kt + NS < nk) dma_stage(kt + NS, buf);
                 __builtin_amdgcn_sched_barrier(0);
                 load_frags((kt + 1) % NS, 0, af[nxt], bfr[nxt]);
+                if (SH && kt + 1 < nk) shrink_stage((kt + 1) % NS);
                 mfmas(af[cur], bfr[cur], RB / 2, RB);
                 sched_interleave<NREAD, RB / 2 * CB>();
                 __builtin_amdgcn_sched_barrier(0);
@@ -372,6 +435,13 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (SH) {
+        // rank partial of this K range: sum the four 16-k groups (adjacent lanes)
+        float vsum = sh_acc;
+        vsum += __shfl_xor(vsum, 1, 64);
+        vsum += __shfl_xor(vsum, 2, 64);
+        if (sh_gq == 0 && sh_t < T) g.vpart[((int64_t)split * T + sh_t) * R + sh_j] = vsum;
+    }
 
     // ---- epilogue ----
     // Each wavefront moves one 32 x WN block of its accumulators at a time
@@ -440,14 +510,30 @@ __device__ __forceinline__ void lora_delta8(const uint16_t *b, int32_t id, int32
 //                                        (+ s_a * sum_j v[t][j] B_a[j][n..n+8]))
 // with t = perm[p]; the partials of one element are summed in split order, so
 // the result does not depend on scheduling.  One thread per (row, 8 columns).
-template <bool LORA>
+// With VP (fused shrink) the row's v is first summed from the K-range rank
+// partials (in range order) into LDS, and bad ids are flagged here.
+template <bool LORA, bool VP = false>
 __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g) {
     const int p = blockIdx.y;
     const int n = (blockIdx.x * 256 + threadIdx.x) * 8;
-    if (n >= g.N) return;
     const int T = g.T, N = g.N;
     const int32_t t = perm_row(g.perm, p, T);
-    if (t < 0) return;
+    __shared__ __attribute__((aligned(16))) float s_v[VP ? 128 : 1];
+    if (VP) {
+        for (int j = threadIdx.x; j < g.max_rank; j += 256) {
+            float sum = 0.0f;
+            for (int sidx = 0; sidx < g.splits; ++sidx)
+                sum += g.vpart[((int64_t)sidx * T + t) * g.max_rank + j];
+            s_v[j] = sum;
+        }
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            const int32_t raw = g.ids[t];
+            const bool ok = raw == -1 || (raw >= 0 && raw < g.n_slots && g.rank[raw] > 0);
+            if (!ok) flag_bad_row(g.err, t);
+        }
+        __syncthreads();
+    }
+    if (n >= N || t < 0) return;
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int sidx = 0; sidx < g.splits; ++sidx) {
         const float *src = g.partial + ((int64_t)sidx * T + p) * N + n;
@@ -462,7 +548,8 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g) {
             const int32_t r = g.rank[raw];
             if (r > 0) {
                 float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                lora_delta8(g.b, raw, g.max_rank, N, n, (r + 7) >> 3, g.v + (int64_t)t * g.max_rank, d);
+                lora_delta8(g.b, raw, g.max_rank, N, n, (r + 7) >> 3,
+                            VP ? s_v : g.v + (int64_t)t * g.max_rank, d);
                 const float sc = g.scale[raw];
 #pragma unroll
                 for (int c = 0; c < 8; ++c) o[c] = fmaf(sc, d[c], o[c]);
@@ -613,6 +700,53 @@ static void launch_cfg(const gemm_args &g, bool lora, bool split, hipStream_t s)
     }
 }
 
+// The fused shrink applies to the decode-sized split-K plan (one 256-row
+// tile, 64-column tiles): every row must be one of the 64 / R rows that some
+// column tile takes on.
+bool gemm_fused_shrink_ok(int32_t T, int32_t d_in, int32_t d_out, int32_t max_rank,
+                          size_t partial_bytes) {
+    if (T <= 0 || T > 256) return false;
+    if (max_rank != 8 && max_rank != 16 && max_rank != 32 && max_rank != 64) return false;
+    const gemm_plan pl = plan_gemm(T, d_in, d_out, partial_bytes);
+    if (pl.splits <= 1 || pl.bm != 256 || pl.bn != 64) return false;
+    if (pl.splits > kMaxKSplit) return false;
+    return (int64_t)ceil_div(d_out, pl.bn) * (64 / max_rank) >= T;
+}
+
+lora_status_t launch_gemm_fused_shrink(const void *x, const void *W, void *y, int32_t T,
+                                       const lora_pool_t *pool, const int32_t *ids, float *vpart,
+                                       int32_t *err, float *partial, size_t partial_bytes,
+                                       hipStream_t s) {
+    gemm_args g;
+    g.x = (const uint16_t *)x;
+    g.W = (const uint16_t *)W;
+    g.y = (uint16_t *)y;
+    g.T = T;
+    g.K = pool->d_in;
+    g.N = pool->d_out;
+    g.perm = nullptr;
+    g.b = (const uint16_t *)pool->b;
+    g.scale = pool->scale;
+    g.rank = pool->rank;
+    g.n_slots = pool->n_slots;
+    g.max_rank = pool->max_rank;
+    g.ids = ids;
+    g.v = nullptr;
+    const gemm_plan pl = plan_gemm(T, g.K, g.N, partial_bytes);
+    g.n_tiles_m = ceil_div(T, pl.bm);
+    g.n_tiles_n = ceil_div(g.N, pl.bn);
+    g.splits = pl.splits;
+    g.k_chunk = pl.k_chunk;
+    g.partial = partial;
+    g.a = (const uint16_t *)pool->a;
+    g.vpart = vpart;
+    g.err = err;
+    const int grid = g.n_tiles_m * g.n_tiles_n * g.splits;
+    hipLaunchKernelGGL((k_gemm_bf16<false, 256, 64, 64, 3, true, true>), dim3(grid), dim3(256), 0, s, g);
+    hipLaunchKernelGGL((k_splitk_reduce<true, true>), dim3((g.N + 2047) / 2048, T), dim3(256), 0, s, g);
+    return hip_status(hipGetLastError());
+}
+
 lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int32_t d_in,
                           int32_t d_out, int32_t dtype, const lora_pool_t *pool,
                           const int32_t *ids, const float *v, const int32_t *perm,
@@ -639,6 +773,9 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
         g.splits = pl.splits;
         g.k_chunk = pl.k_chunk;
         g.partial = partial;
+        g.a = nullptr;
+        g.vpart = nullptr;
+        g.err = nullptr;
         const bool split = pl.splits > 1;
         if (pl.bm == 256 && pl.bn == 256) launch_cfg<256, 256>(g, pool != nullptr, split, s);
         else if (pl.bm == 256 && pl.bn == 128) launch_cfg<256, 128>(g, pool != nullptr, split, s);
