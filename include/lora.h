@@ -150,10 +150,11 @@ lora_status_t lora_pool_clear(const lora_pool_t *pool, int32_t slot, lora_stream
 
 /* Bytes of workspace for batches of up to T rows against a pool of n_slots
  * slots and max_rank, for every entry point below.  d_out is the widest
- * output the workspace serves (0: none): with it the workspace also holds the
- * fp32 partial sums that let small batches (T <= 4096) split the GEMM over K;
- * without it those batches run unsplit (the two differ only in fp32 summation
- * order).  Returns 0 on bad arguments. */
+ * output the workspace serves (0: none): with it the workspace also holds
+ * fp32 partial tiles (at most 128 MiB) that let the GEMM split K -- for all
+ * tiles of small batches, and for the last, mostly idle round of tiles of
+ * larger ones; without it every tile runs whole (the two differ only in fp32
+ * summation order).  Returns 0 on bad arguments. */
 size_t lora_workspace_bytes(int32_t T, int32_t n_slots, int32_t max_rank, int32_t d_out);
 
 /* Prepare a freshly allocated DEVICE workspace: clears the error word and

@@ -97,8 +97,11 @@ constexpr int32_t kShrinkRows = 32;    // rows of one segment per grouped-shrink
 constexpr int32_t kMaxKSplit = 16;     // shrink k-split factor bound
 constexpr int32_t kMaxSlots = 16000;   // slots per pool (LDS histogram bound, < 64 KiB)
 constexpr int32_t kErrNone = 0x7fffffff;
-constexpr int32_t kMaxGemmSplit = 16;   // split-K GEMM partial copies
-constexpr int32_t kMaxSplitRows = 4096; // batches up to this many rows get split-K scratch
+constexpr int32_t kMaxGemmSplit = 16;   // split-K GEMM: most K ranges per tile
+// Split-K GEMM partials are fp32 tiles, [tile][split][BM][BN]; one split
+// launch has at most about two rounds of 256 workgroups of <= 256 x 256
+// tiles, so this bounds the scratch for any shape.
+constexpr size_t kGemmPartialCap = size_t(128) << 20;
 
 struct ws_layout {
     size_t header;      // int32[64]: [0] error word (first bad row)
@@ -112,7 +115,7 @@ struct ws_layout {
     size_t tile_hist;   // int32[(n_slots + 1) * n_tiles]
     size_t v;           // fp32[T * max_rank]
     size_t partial;     // fp32[kMaxKSplit * T * max_rank]
-    size_t gemm_partial;  // fp32[kMaxGemmSplit * T * d_out] (split-K GEMM), may be empty
+    size_t gemm_partial;  // split-K GEMM partials (fp32 tiles), may be empty
     size_t total;
 };
 
@@ -135,7 +138,11 @@ inline ws_layout make_ws_layout(int32_t T, int32_t n_slots, int32_t max_rank, in
     L.v = o;         o = align256(o + 4 * t * (size_t)max_rank);
     L.partial = o;   o = align256(o + 4 * (size_t)kMaxKSplit * t * (size_t)max_rank);
     L.gemm_partial = o;
-    if (d_out > 0 && T > 0 && T <= kMaxSplitRows) o = align256(o + 4 * (size_t)kMaxGemmSplit * t * (size_t)d_out);
+    if (d_out > 0 && T > 0) {
+        const size_t tp = (t + 255) / 256 * 256, np = ((size_t)d_out + 255) / 256 * 256;
+        const size_t need = 4 * (size_t)kMaxGemmSplit * tp * np;
+        o = align256(o + (need < kGemmPartialCap ? need : kGemmPartialCap));
+    }
     L.total = o;
     return L;
 }

@@ -40,8 +40,9 @@ struct gemm_args {
     const int32_t *ids;
     const float *v;
     int32_t n_tiles_m, n_tiles_n;
+    int32_t tile_base, n_tiles;    // this launch: tiles [tile_base, tile_base + n_tiles) in tile order
     int32_t splits, k_chunk;       // split-K: number of K ranges and their length
-    float *partial;                // split-K: fp32 [splits][T][N], sorted-row order
+    float *partial;                // split-K: fp32 [n_tiles][splits][BM][BN] (tile-major)
     const uint16_t *a;             // fused shrink: the pool's A^T [n_slots][max_rank][K]
     float *vpart;                  // fused shrink: fp32 [splits][T][max_rank] rank partials
     int32_t *err;                  // fused shrink: the workspace error word
@@ -54,14 +55,7 @@ struct gemm_args {
 // columns in its L2.  With split-K the split index varies slowest.
 constexpr int kXcds = 8, kGroupM = 8;
 
-__device__ __forceinline__ void tile_of(int b, int total, int n_tiles_m, int n_tiles_n, int &tm,
-                                        int &tn, int &split) {
-    const int q = total / kXcds, r = total % kXcds;
-    const int x = b % kXcds, slot = b / kXcds;
-    int v = x * q + min(x, r) + slot;
-    const int tiles = n_tiles_m * n_tiles_n;
-    split = v / tiles;
-    v -= split * tiles;
+__device__ __forceinline__ void grouped_tile(int v, int n_tiles_m, int n_tiles_n, int &tm, int &tn) {
     const int per_group = kGroupM * n_tiles_n;
     const int grp = v / per_group;
     const int first_m = grp * kGroupM;
@@ -69,6 +63,19 @@ __device__ __forceinline__ void tile_of(int b, int total, int n_tiles_m, int n_t
     const int in = v - grp * per_group;
     tm = first_m + in % gm;
     tn = in / gm;
+}
+
+// Work item of workgroup b in a launch of `total` workgroups covering
+// n_tiles tiles (from tile_base, in tile order) times the split count.
+// Returns the tile (tm, tn), the split, and the launch-local tile index.
+__device__ __forceinline__ void tile_of(int b, int total, const gemm_args &g, int &tm, int &tn,
+                                        int &split, int &tidx) {
+    const int q = total / kXcds, r = total % kXcds;
+    const int x = b % kXcds, slot = b / kXcds;
+    int v = x * q + min(x, r) + slot;
+    split = v / g.n_tiles;
+    tidx = v - split * g.n_tiles;
+    grouped_tile(g.tile_base + tidx, g.n_tiles_m, g.n_tiles_n, tm, tn);
 }
 
 // A 16-byte zero vector in global memory: the source of the DMA loads of
@@ -209,8 +216,8 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
     __shared__ __attribute__((aligned(1024))) uint16_t smem[C::LDS / 2];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 1, wn = w & 1;
-    int tm, tn, split;
-    tile_of(blockIdx.x, gridDim.x, g.n_tiles_m, g.n_tiles_n, tm, tn, split);
+    int tm, tn, split, tidx;
+    tile_of(blockIdx.x, gridDim.x, g, tm, tn, split, tidx);
     const int m0 = tm * BM, n0 = tn * BN;
     const int K = g.K, N = g.N, T = g.T;
     const int k_begin = SPLIT ? split * g.k_chunk : 0;
@@ -473,7 +480,7 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
             const float4 o0 = *reinterpret_cast<const float4 *>(src);
             const float4 o1 = *reinterpret_cast<const float4 *>(src + 4);
             if (SPLIT) {
-                float *dst = g.partial + ((int64_t)split * T + m0 + i) * N + n;
+                float *dst = g.partial + (((int64_t)tidx * g.splits + split) * BM + i) * BN + (n - n0);
                 *reinterpret_cast<float4 *>(dst) = o0;
                 *reinterpret_cast<float4 *>(dst + 4) = o1;
             } else {
@@ -506,37 +513,50 @@ __device__ __forceinline__ void lora_delta8(const uint16_t *b, int32_t id, int32
     }
 }
 
-// Split-K reduction: y[t][n..n+8] = bf16(sum_s partial[s][p][n..n+8]
-//                                        (+ s_a * sum_j v[t][j] B_a[j][n..n+8]))
-// with t = perm[p]; the partials of one element are summed in split order, so
-// the result does not depend on scheduling.  One thread per (row, 8 columns).
-// With VP (fused shrink) the row's v is first summed from the K-range rank
-// partials (in range order) into LDS, and bad ids are flagged here.
-template <bool LORA, bool VP = false>
+// Split-K reduction over the tiles of one split launch.  A workgroup takes
+// RW = 2048 / BN rows of one tile; a thread owns 8 consecutive columns of one
+// row: y[t][n..n+8] = bf16(sum_s partial[tile][s][r][c..c+8]
+//                          (+ s_a * sum_j v[t][j] B_a[j][n..n+8])), t = perm[p].
+// The partials of an element are summed in split order (deterministic).
+// With VP (fused shrink) the rows' v are first summed from the K-range rank
+// partials (in range order) into LDS, and the first column tile flags bad ids.
+template <bool LORA, bool VP, int BM, int BN>
 __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g) {
-    const int p = blockIdx.y;
-    const int n = (blockIdx.x * 256 + threadIdx.x) * 8;
-    const int T = g.T, N = g.N;
-    const int32_t t = perm_row(g.perm, p, T);
-    __shared__ __attribute__((aligned(16))) float s_v[VP ? 128 : 1];
+    constexpr int RW = 2048 / BN, CPR = BN / 8, CHUNKS = BM / RW;
+    const int tidx = blockIdx.x / CHUNKS, chunk = blockIdx.x % CHUNKS;
+    int tm, tn;
+    grouped_tile(g.tile_base + tidx, g.n_tiles_m, g.n_tiles_n, tm, tn);
+    const int T = g.T, N = g.N, R = g.max_rank;
+    const int r = chunk * RW + threadIdx.x / CPR, c = (threadIdx.x % CPR) * 8;
+    const int p = tm * BM + r, n = tn * BN + c;
+    __shared__ __attribute__((aligned(16))) float s_v[VP ? RW * 64 : 1];
     if (VP) {
-        for (int j = threadIdx.x; j < g.max_rank; j += 256) {
+        for (int e = threadIdx.x; e < RW * R; e += 256) {
+            const int rr = e / R, j = e % R;
+            const int pp = tm * BM + chunk * RW + rr;
             float sum = 0.0f;
-            for (int sidx = 0; sidx < g.splits; ++sidx)
-                sum += g.vpart[((int64_t)sidx * T + t) * g.max_rank + j];
-            s_v[j] = sum;
-        }
-        if (blockIdx.x == 0 && threadIdx.x == 0) {
-            const int32_t raw = g.ids[t];
-            const bool ok = raw == -1 || (raw >= 0 && raw < g.n_slots && g.rank[raw] > 0);
-            if (!ok) flag_bad_row(g.err, t);
+            if (pp < T) {
+                const int32_t tt = perm_row(g.perm, pp, T);
+                if (tt >= 0) {
+                    for (int sidx = 0; sidx < g.splits; ++sidx)
+                        sum += g.vpart[((int64_t)sidx * T + tt) * R + j];
+                    if (j == 0 && tn == 0) {
+                        const int32_t raw = g.ids[tt];
+                        const bool ok = raw == -1 || (raw >= 0 && raw < g.n_slots && g.rank[raw] > 0);
+                        if (!ok) flag_bad_row(g.err, tt);
+                    }
+                }
+            }
+            s_v[rr * R + j] = sum;
         }
         __syncthreads();
     }
-    if (n >= N || t < 0) return;
+    if (p >= T || n >= N) return;
+    const int32_t t = perm_row(g.perm, p, T);
+    if (t < 0) return;
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int sidx = 0; sidx < g.splits; ++sidx) {
-        const float *src = g.partial + ((int64_t)sidx * T + p) * N + n;
+        const float *src = g.partial + (((int64_t)tidx * g.splits + sidx) * BM + r) * BN + c;
         const float4 a = *reinterpret_cast<const float4 *>(src);
         const float4 b = *reinterpret_cast<const float4 *>(src + 4);
         o[0] += a.x; o[1] += a.y; o[2] += a.z; o[3] += a.w;
@@ -545,14 +565,14 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g) {
     if (LORA) {
         const int32_t raw = g.ids[t];
         if (raw >= 0 && raw < g.n_slots) {
-            const int32_t r = g.rank[raw];
-            if (r > 0) {
+            const int32_t rk = g.rank[raw];
+            if (rk > 0) {
                 float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                lora_delta8(g.b, raw, g.max_rank, N, n, (r + 7) >> 3,
-                            VP ? s_v : g.v + (int64_t)t * g.max_rank, d);
+                lora_delta8(g.b, raw, R, N, n, (rk + 7) >> 3,
+                            VP ? s_v + (r - chunk * RW) * R : g.v + (int64_t)t * R, d);
                 const float sc = g.scale[raw];
 #pragma unroll
-                for (int c = 0; c < 8; ++c) o[c] = fmaf(sc, d[c], o[c]);
+                for (int q = 0; q < 8; ++q) o[q] = fmaf(sc, d[q], o[q]);
             }
         }
     }
@@ -649,19 +669,38 @@ __global__ void __launch_bounds__(256) k_gemm_f32(gemm_f32_args g) {
 
 // Tile configuration and K split for one bf16 GEMM shape.
 struct gemm_plan {
-    int bm, bn, splits, k_chunk;
+    int bm, bn;
+    int n_dp;          // tiles computed whole (with the fused expand), from tile 0
+    int tail;          // tiles after those, computed as split-K pieces + reduction
+    int splits, k_chunk;
 };
 
 static int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-// Largest tile that still gives close to one workgroup per CU; for grids that
-// stay small (few token rows), split K so that about 256 workgroups run, if
-// the workspace holds the fp32 partials.
+// Largest tile that still gives close to one workgroup per CU.  When the last
+// round of tiles would leave most CUs idle (a tail of at most 160 of 256),
+// those tail tiles are split over K so every CU takes a share.  Grids that
+// stay small (few token rows) split K for all tiles.  Split-K needs room for
+// the fp32 partials in the workspace.
 static gemm_plan plan_gemm(int T, int K, int N, size_t partial_bytes) {
     static const int cfg[4][2] = {{256, 256}, {256, 128}, {128, 128}, {128, 64}};
     for (int c = 0; c < 4; ++c) {
-        const int tiles = ceil_div(T, cfg[c][0]) * ceil_div(N, cfg[c][1]);
-        if (tiles >= 224) return {cfg[c][0], cfg[c][1], 1, K};
+        const int bm = cfg[c][0], bn = cfg[c][1];
+        const int tiles = ceil_div(T, bm) * ceil_div(N, bn);
+        if (tiles < 224) continue;
+        gemm_plan p{bm, bn, tiles, 0, 1, K};
+        const int full = tiles / 256 * 256, rem = tiles - full;
+        if (full > 0 && rem > 0 && rem <= 160 && K >= 1024) {
+            int sp = 256 / rem;
+            if (sp > kMaxGemmSplit) sp = kMaxGemmSplit;
+            if (sp > K / 512) sp = K / 512;
+            while (sp > 1 && (size_t)sp * rem * bm * bn * 4 > partial_bytes) --sp;
+            if (sp >= 2) {
+                const int kc = ceil_div(ceil_div(K, sp), 64) * 64;
+                p = gemm_plan{bm, bn, full, rem, ceil_div(K, kc), kc};
+            }
+        }
+        return p;
     }
     // Small grid (decode-sized T): split K.  One 256-row tile covers T <= 256,
     // so W is read once; narrow 64-column tiles keep the number of fp32
@@ -671,32 +710,41 @@ static gemm_plan plan_gemm(int T, int K, int N, size_t partial_bytes) {
     int splits = ceil_div(256, tiles);
     const int max_by_k = K / 256 > 0 ? K / 256 : 1;
     if (splits > max_by_k) splits = max_by_k;
-    if (splits > 16) splits = 16;
-    while (splits > 1 && (size_t)splits * T * N * 4 > partial_bytes) --splits;
+    if (splits > kMaxGemmSplit) splits = kMaxGemmSplit;
+    while (splits > 1 && (size_t)splits * tiles * bm * bn * 4 > partial_bytes) --splits;
     if (splits <= 1) {
         const int t2 = ceil_div(T, 128) * ceil_div(N, 64);
-        return t2 > tiles ? gemm_plan{128, 64, 1, K} : gemm_plan{bm, bn, 1, K};
+        return t2 > tiles ? gemm_plan{128, 64, t2, 0, 1, K} : gemm_plan{bm, bn, tiles, 0, 1, K};
     }
-    int k_chunk = ceil_div(ceil_div(K, splits), 64) * 64;
-    splits = ceil_div(K, k_chunk);
-    return {bm, bn, splits, k_chunk};
+    const int k_chunk = ceil_div(ceil_div(K, splits), 64) * 64;
+    return {bm, bn, 0, tiles, ceil_div(K, k_chunk), k_chunk};
 }
 
 template <int BM, int BN, int NS = 2>
-static void launch_cfg(const gemm_args &g, bool lora, bool split, hipStream_t s) {
+static void launch_cfg(gemm_args g, const gemm_plan &pl, bool lora, hipStream_t s) {
     constexpr int BK = 64;
-    const int grid = g.n_tiles_m * g.n_tiles_n * (split ? g.splits : 1);
-    if (split) {
-        hipLaunchKernelGGL((k_gemm_bf16<false, BM, BN, BK, NS, true>), dim3(grid), dim3(256), 0, s, g);
-        const dim3 rgrid((g.N + 2047) / 2048, g.T);
+    if (pl.n_dp > 0) {
+        g.tile_base = 0;
+        g.n_tiles = pl.n_dp;
+        g.splits = 1;
+        g.k_chunk = g.K;
         if (lora)
-            hipLaunchKernelGGL(k_splitk_reduce<true>, rgrid, dim3(256), 0, s, g);
+            hipLaunchKernelGGL((k_gemm_bf16<true, BM, BN, BK, NS, false>), dim3(pl.n_dp), dim3(256), 0, s, g);
         else
-            hipLaunchKernelGGL(k_splitk_reduce<false>, rgrid, dim3(256), 0, s, g);
-    } else if (lora) {
-        hipLaunchKernelGGL((k_gemm_bf16<true, BM, BN, BK, NS, false>), dim3(grid), dim3(256), 0, s, g);
-    } else {
-        hipLaunchKernelGGL((k_gemm_bf16<false, BM, BN, BK, NS, false>), dim3(grid), dim3(256), 0, s, g);
+            hipLaunchKernelGGL((k_gemm_bf16<false, BM, BN, BK, NS, false>), dim3(pl.n_dp), dim3(256), 0, s, g);
+    }
+    if (pl.tail > 0) {
+        g.tile_base = pl.n_dp;
+        g.n_tiles = pl.tail;
+        g.splits = pl.splits;
+        g.k_chunk = pl.k_chunk;
+        hipLaunchKernelGGL((k_gemm_bf16<false, BM, BN, BK, NS, true>), dim3(pl.tail * pl.splits), dim3(256),
+                           0, s, g);
+        const dim3 rgrid(pl.tail * (BM / (2048 / BN)));
+        if (lora)
+            hipLaunchKernelGGL((k_splitk_reduce<true, false, BM, BN>), rgrid, dim3(256), 0, s, g);
+        else
+            hipLaunchKernelGGL((k_splitk_reduce<false, false, BM, BN>), rgrid, dim3(256), 0, s, g);
     }
 }
 
@@ -708,7 +756,7 @@ bool gemm_fused_shrink_ok(int32_t T, int32_t d_in, int32_t d_out, int32_t max_ra
     if (T <= 0 || T > 256) return false;
     if (max_rank != 8 && max_rank != 16 && max_rank != 32 && max_rank != 64) return false;
     const gemm_plan pl = plan_gemm(T, d_in, d_out, partial_bytes);
-    if (pl.splits <= 1 || pl.bm != 256 || pl.bn != 64) return false;
+    if (pl.n_dp != 0 || pl.splits <= 1 || pl.bm != 256 || pl.bn != 64) return false;
     if (pl.splits > kMaxKSplit) return false;
     return (int64_t)ceil_div(d_out, pl.bn) * (64 / max_rank) >= T;
 }
@@ -735,15 +783,17 @@ lora_status_t launch_gemm_fused_shrink(const void *x, const void *W, void *y, in
     const gemm_plan pl = plan_gemm(T, g.K, g.N, partial_bytes);
     g.n_tiles_m = ceil_div(T, pl.bm);
     g.n_tiles_n = ceil_div(g.N, pl.bn);
+    g.tile_base = 0;
+    g.n_tiles = pl.tail;
     g.splits = pl.splits;
     g.k_chunk = pl.k_chunk;
     g.partial = partial;
     g.a = (const uint16_t *)pool->a;
     g.vpart = vpart;
     g.err = err;
-    const int grid = g.n_tiles_m * g.n_tiles_n * g.splits;
-    hipLaunchKernelGGL((k_gemm_bf16<false, 256, 64, 64, 3, true, true>), dim3(grid), dim3(256), 0, s, g);
-    hipLaunchKernelGGL((k_splitk_reduce<true, true>), dim3((g.N + 2047) / 2048, T), dim3(256), 0, s, g);
+    hipLaunchKernelGGL((k_gemm_bf16<false, 256, 64, 64, 3, true, true>), dim3(pl.tail * pl.splits), dim3(256),
+                       0, s, g);
+    hipLaunchKernelGGL((k_splitk_reduce<true, true, 256, 64>), dim3(pl.tail * (256 / 32)), dim3(256), 0, s, g);
     return hip_status(hipGetLastError());
 }
 
@@ -770,18 +820,16 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
         const gemm_plan pl = plan_gemm(T, d_in, d_out, partial ? partial_bytes : 0);
         g.n_tiles_m = ceil_div(T, pl.bm);
         g.n_tiles_n = ceil_div(d_out, pl.bn);
-        g.splits = pl.splits;
-        g.k_chunk = pl.k_chunk;
         g.partial = partial;
         g.a = nullptr;
         g.vpart = nullptr;
         g.err = nullptr;
-        const bool split = pl.splits > 1;
-        if (pl.bm == 256 && pl.bn == 256) launch_cfg<256, 256>(g, pool != nullptr, split, s);
-        else if (pl.bm == 256 && pl.bn == 128) launch_cfg<256, 128>(g, pool != nullptr, split, s);
-        else if (pl.bm == 256) launch_cfg<256, 64, 3>(g, pool != nullptr, split, s);
-        else if (pl.bn == 128) launch_cfg<128, 128>(g, pool != nullptr, split, s);
-        else launch_cfg<128, 64>(g, pool != nullptr, split, s);
+        const bool lora = pool != nullptr;
+        if (pl.bm == 256 && pl.bn == 256) launch_cfg<256, 256>(g, pl, lora, s);
+        else if (pl.bm == 256 && pl.bn == 128) launch_cfg<256, 128>(g, pl, lora, s);
+        else if (pl.bm == 256) launch_cfg<256, 64, 3>(g, pl, lora, s);
+        else if (pl.bn == 128) launch_cfg<128, 128>(g, pl, lora, s);
+        else launch_cfg<128, 64>(g, pl, lora, s);
     } else {
         gemm_f32_args g;
         g.x = (const float *)x;

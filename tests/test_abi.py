@@ -68,9 +68,11 @@ def test_workspace_bytes():
     # holds at least v [T, max_rank] fp32, perm [T] and the k-split partials
     assert n2 >= 100000 * (8 * 4 + 4 + 16 * 8 * 4)
     assert n2 % 256 == 0
-    # with d_out: room for 16 fp32 partial copies of a small batch's output
+    # with d_out: room for 16 fp32 partial copies of a small batch's output,
+    # and never more than 128 MiB of partial tiles
     assert L.lora_workspace_bytes(256, 4, 8, 4096) >= L.lora_workspace_bytes(256, 4, 8) + 16 * 256 * 4096 * 4
-    assert L.lora_workspace_bytes(100000, 4, 8, 4096) == n2
+    assert L.lora_workspace_bytes(100000, 4, 8, 4096) == n2 + (128 << 20)
+    assert L.lora_workspace_bytes(2240, 1000, 16, 14336) <= L.lora_workspace_bytes(2240, 1000, 16) + (128 << 20)
 
 
 def test_validation_returns_before_launch(lib):
