@@ -162,8 +162,9 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
     const int32_t *__restrict__ blk_start, const int32_t *__restrict__ blk_seg,
     int32_t n_work_upper, int32_t k_chunk,
     float *__restrict__ v, float *__restrict__ partial, int32_t *err) {
+    constexpr int BR = kShrinkRows;                      // rows per work block
+    constexpr int RBN = BR / 16;                         // 16-row MFMA blocks
     constexpr int U = RCH <= 2 ? 4 : 2;                  // k steps per batch of loads
-    constexpr int BR = kShrinkRows;                      // 32 rows = two 16-row MFMA blocks
     __shared__ float s_acc[4][BR][RCH * 16 + 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wid = blockIdx.x;
@@ -192,13 +193,13 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
     const int k_end = min(d_in, k_begin + k_chunk);
 
     const int lr = lane & 15, kg = lane >> 4;
-    // this lane's two x rows (row blocks 0 and 1); invalid rows read the
-    // block's first row and are zeroed
+    // this lane's x row in each 16-row block; invalid rows read the block's
+    // first row and are zeroed
     const int32_t t_first = perm_row(perm, p0, T);
-    int64_t xoff[2];
-    uint32_t xm[2];                                      // all-ones for a real row, else 0
+    int64_t xoff[RBN];
+    uint32_t xm[RBN];                                    // all-ones for a real row, else 0
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RBN; ++rb) {
         const int p = p0 + rb * 16 + lr;
         const int32_t t = (p < pend) ? perm_row(perm, p, T) : -1;
         xm[rb] = t >= 0 ? ~0u : 0u;
@@ -213,15 +214,15 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
         am[rc] = j < r ? ~0u : 0u;
         aoff[rc] = (int64_t)min(j, r > 0 ? r - 1 : 0) * d_in;
     }
-    f32x4_t acc[2][RCH];
+    f32x4_t acc[RBN][RCH];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < RBN; ++rb)
 #pragma unroll
         for (int rc = 0; rc < RCH; ++rc) acc[rb][rc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     if (r > 0) {
         for (int kb = k_begin + wave * 32; kb < k_end; kb += 4 * 32 * U) {
-            uint4 xq[U][2], aq[U][RCH];
+            uint4 xq[U][RBN], aq[U][RCH];
             uint32_t km[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -229,14 +230,14 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
                 km[u] = k < k_end ? ~0u : 0u;
                 const int kc = k < k_end ? k : k_begin;
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) xq[u][rb] = ldg16(x + xoff[rb] + kc);
+                for (int rb = 0; rb < RBN; ++rb) xq[u][rb] = ldg16(x + xoff[rb] + kc);
 #pragma unroll
                 for (int rc = 0; rc < RCH; ++rc) aq[u][rc] = ldg16(At + aoff[rc] + kc);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
+                for (int rb = 0; rb < RBN; ++rb) {
                     const uint32_t m = km[u] & xm[rb];
                     xq[u][rb] = make_uint4(xq[u][rb].x & m, xq[u][rb].y & m, xq[u][rb].z & m, xq[u][rb].w & m);
                 }
@@ -249,7 +250,7 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
+                for (int rb = 0; rb < RBN; ++rb)
 #pragma unroll
                     for (int rc = 0; rc < RCH; ++rc)
                         acc[rb][rc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -260,7 +261,7 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
         flag_bad_row(err, perm_row(perm, p0 + tid, T));     // segment of an empty slot
     }
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < RBN; ++rb)
 #pragma unroll
         for (int rc = 0; rc < RCH; ++rc)
 #pragma unroll
