@@ -232,6 +232,45 @@ lora_status_t lora_linear_forward(const void *x, const void *W, void *y, int32_t
                                   uint32_t flags, void *ws, size_t ws_bytes,
                                   lora_stream_t stream);
 
+/* ---- several projections that share x (multi-slice) ------------------------- */
+
+/* Projections fed by the same input -- q, k and v of an attention block, or
+ * gate and up of an MLP -- each with its own pool, share one shrink: it
+ * reads x once and computes every slice's rank vector in one launch (the
+ * stacked per-slice buffers and output slices of "Serving LoRA adapters
+ * ...", Step 4).  The pools of one call (HOST array pools[0..n_slices)) must
+ * agree on n_slots, d_in, max_rank and dtype (d_out may differ); a slot
+ * number names the same adapter in every slice, with its own rank and scale
+ * there.  1 <= n_slices <= 4 and n_slices * max_rank <= 128, else
+ * LORA_ERR_UNSUPPORTED.  A row is flagged as bad (see lora_get_device_error)
+ * if its id is out of range or its slot is empty in any slice; each slice
+ * then computes it as a base row where its own slot is empty. */
+
+/* Workspace bytes for sliced calls (lora_workspace_bytes with v of
+ * n_slices * max_rank columns); 0 on bad arguments. */
+size_t lora_workspace_bytes_sliced(int32_t T, int32_t n_slots, int32_t max_rank, int32_t n_slices,
+                                   int32_t d_out);
+
+/* v DEVICE fp32 [T, n_slices * max_rank]: slice s in columns
+ * [s * max_rank, (s + 1) * max_rank), each as lora_shrink would write it for
+ * pools[s] (bitwise the same values). */
+lora_status_t lora_shrink_sliced(const void *x, int32_t T, const lora_pool_t *pools,
+                                 int32_t n_slices, const int32_t *ids, lora_mode_t mode, float *v,
+                                 void *ws, size_t ws_bytes, lora_stream_t stream);
+
+/* y[s] = x W[s] + s_a (x A_a^s) B_a^s for each slice s: W and y are HOST
+ * arrays of n_slices DEVICE pointers ([d_in, pools[s].d_out] and
+ * [T, pools[s].d_out]).  Same modes and flags as lora_linear_forward; the
+ * results are bitwise those of n_slices lora_linear_forward calls.
+ * Segments (SGMV) are built once, the shrink runs once for all slices, then
+ * each slice's GEMM applies its expand.  A slice that lora_linear_forward
+ * would run on its decode-sized fused path (the shrink inside the GEMM, on
+ * the x it streams anyway) runs that way here too. */
+lora_status_t lora_linear_forward_sliced(const void *x, const void *const *W, void *const *y,
+                                         int32_t T, const lora_pool_t *pools, int32_t n_slices,
+                                         const int32_t *ids, lora_mode_t mode, uint32_t flags,
+                                         void *ws, size_t ws_bytes, lora_stream_t stream);
+
 /* ---- errors ------------------------------------------------------------------- */
 
 /* Synchronise `stream`, read the workspace's error word into *first_bad_row

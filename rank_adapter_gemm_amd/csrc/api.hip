@@ -43,6 +43,39 @@ inline bool valid_mode(int32_t m) {
     return m == LORA_MODE_AUTO || m == LORA_MODE_BGMV || m == LORA_MODE_SGMV;
 }
 
+// Slices must be valid pools that agree on everything the shared shrink uses.
+inline lora_status_t check_slices(const lora_pool_t *pools, int32_t n) {
+    if (!pools || n < 1) return LORA_ERR_INVALID_ARGUMENT;
+    if (n > kMaxSlices) return LORA_ERR_UNSUPPORTED;
+    for (int i = 0; i < n; ++i) {
+        if (!valid_pool(&pools[i])) return LORA_ERR_INVALID_ARGUMENT;
+        if (pools[i].n_slots != pools[0].n_slots || pools[i].d_in != pools[0].d_in ||
+            pools[i].max_rank != pools[0].max_rank || pools[i].dtype != pools[0].dtype)
+            return LORA_ERR_INVALID_ARGUMENT;
+    }
+    if ((int64_t)n * pools[0].max_rank > kMaxSliceRanks) return LORA_ERR_UNSUPPORTED;
+    return LORA_OK;
+}
+
+// Base product plus the low-rank term from v (row stride v_stride), fused
+// into the GEMM or as a separate pass.
+lora_status_t gemm_and_expand(const void *x, const void *W, void *y, int32_t T, const lora_pool_t &p,
+                              const int32_t *ids, const float *v, int32_t v_stride, bool sgmv,
+                              uint32_t flags, const ws_layout &L, void *ws, size_t ws_bytes,
+                              hipStream_t s) {
+    const int32_t *perm = sgmv ? ws_ptr<int32_t>(ws, L.perm) : nullptr;
+    float *partial = ws_ptr<float>(ws, L.gemm_partial);
+    const size_t partial_bytes = ws_bytes - L.gemm_partial;
+    if (flags & LORA_FLAG_SEPARATE_EXPAND) {
+        lora_status_t st = launch_gemm(x, W, y, T, p.d_in, p.d_out, p.dtype, nullptr, nullptr, nullptr,
+                                       0, nullptr, partial, partial_bytes, s);
+        if (st != LORA_OK) return st;
+        return launch_expand(v, v_stride, T, p, ids, sgmv, y, L, ws, s);
+    }
+    return launch_gemm(x, W, y, T, p.d_in, p.d_out, p.dtype, &p, ids, v, v_stride, perm, partial,
+                       partial_bytes, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -159,7 +192,7 @@ lora_status_t lora_shrink(const void *x, int32_t T, const lora_pool_t *pool, con
     lora_status_t st = check_ws(ws, ws_bytes, T, pool->n_slots, pool->max_rank, &L);
     if (st != LORA_OK) return st;
     if (T == 0) return LORA_OK;
-    return launch_shrink(x, T, *pool, ids, mode == LORA_MODE_SGMV, v, L, ws, hs(stream));
+    return launch_shrink(x, T, pool, 1, ids, mode == LORA_MODE_SGMV, v, L, ws, hs(stream));
 }
 
 lora_status_t lora_expand(const float *v, int32_t T, const lora_pool_t *pool, const int32_t *ids,
@@ -171,7 +204,7 @@ lora_status_t lora_expand(const float *v, int32_t T, const lora_pool_t *pool, co
     lora_status_t st = check_ws(ws, ws_bytes, T, pool->n_slots, pool->max_rank, &L);
     if (st != LORA_OK) return st;
     if (T == 0) return LORA_OK;
-    return launch_expand(v, T, *pool, ids, mode == LORA_MODE_SGMV, y, L, ws, hs(stream));
+    return launch_expand(v, pool->max_rank, T, *pool, ids, mode == LORA_MODE_SGMV, y, L, ws, hs(stream));
 }
 
 lora_status_t lora_gemm(const void *x, const void *W, void *y, int32_t T, int32_t d_in,
@@ -183,7 +216,7 @@ lora_status_t lora_gemm(const void *x, const void *W, void *y, int32_t T, int32_
         return LORA_ERR_INVALID_ARGUMENT;
     if (ws && !aligned16(ws)) return LORA_ERR_INVALID_ARGUMENT;
     if (T == 0) return LORA_OK;
-    return launch_gemm(x, W, y, T, d_in, d_out, dtype, nullptr, nullptr, nullptr, nullptr,
+    return launch_gemm(x, W, y, T, d_in, d_out, dtype, nullptr, nullptr, nullptr, 0, nullptr,
                        ws ? static_cast<float *>(ws) : nullptr, ws ? ws_bytes : 0, hs(stream));
 }
 
@@ -198,8 +231,8 @@ lora_status_t lora_gemm_expand(const void *x, const void *W, void *y, int32_t T,
     if (st != LORA_OK) return st;
     if (T == 0) return LORA_OK;
     const int32_t *perm = (mode == LORA_MODE_SGMV) ? ws_ptr<int32_t>(ws, L.perm) : nullptr;
-    return launch_gemm(x, W, y, T, pool->d_in, pool->d_out, pool->dtype, pool, ids, v, perm,
-                       ws_ptr<float>(ws, L.gemm_partial), ws_bytes - L.gemm_partial, hs(stream));
+    return launch_gemm(x, W, y, T, pool->d_in, pool->d_out, pool->dtype, pool, ids, v, pool->max_rank,
+                       perm, ws_ptr<float>(ws, L.gemm_partial), ws_bytes - L.gemm_partial, hs(stream));
 }
 
 lora_status_t lora_linear_forward(const void *x, const void *W, void *y, int32_t T,
@@ -228,18 +261,82 @@ lora_status_t lora_linear_forward(const void *x, const void *W, void *y, int32_t
                                         ws_ptr<int32_t>(ws, L.header), ws_ptr<float>(ws, L.gemm_partial),
                                         ws_bytes - L.gemm_partial, s);
     float *v = ws_ptr<float>(ws, L.v);
-    st = launch_shrink(x, T, *pool, ids, sgmv, v, L, ws, s);
+    st = launch_shrink(x, T, pool, 1, ids, sgmv, v, L, ws, s);
     if (st != LORA_OK) return st;
-    const int32_t *perm = sgmv ? ws_ptr<int32_t>(ws, L.perm) : nullptr;
-    if (flags & LORA_FLAG_SEPARATE_EXPAND) {
-        st = launch_gemm(x, W, y, T, pool->d_in, pool->d_out, pool->dtype, nullptr, nullptr,
-                         nullptr, nullptr, ws_ptr<float>(ws, L.gemm_partial),
-                         ws_bytes - L.gemm_partial, s);
-        if (st != LORA_OK) return st;
-        return launch_expand(v, T, *pool, ids, sgmv, y, L, ws, s);
+    return gemm_and_expand(x, W, y, T, *pool, ids, v, pool->max_rank, sgmv, flags, L, ws, ws_bytes, s);
+}
+
+size_t lora_workspace_bytes_sliced(int32_t T, int32_t n_slots, int32_t max_rank, int32_t n_slices,
+                                   int32_t d_out) {
+    if (n_slices < 1 || n_slices > kMaxSlices || (int64_t)n_slices * max_rank > kMaxSliceRanks ||
+        max_rank < 8 || (max_rank % 8) != 0)
+        return 0;
+    return lora_workspace_bytes(T, n_slots, n_slices * max_rank, d_out);
+}
+
+lora_status_t lora_shrink_sliced(const void *x, int32_t T, const lora_pool_t *pools,
+                                 int32_t n_slices, const int32_t *ids, lora_mode_t mode, float *v,
+                                 void *ws, size_t ws_bytes, lora_stream_t stream) {
+    lora_status_t st = check_slices(pools, n_slices);
+    if (st != LORA_OK) return st;
+    if (T < 0 || !valid_mode(mode)) return LORA_ERR_INVALID_ARGUMENT;
+    if (T > 0 && (!x || !ids || !v || !aligned16(x) || !aligned16(v))) return LORA_ERR_INVALID_ARGUMENT;
+    ws_layout L;
+    st = check_ws(ws, ws_bytes, T, pools[0].n_slots, n_slices * pools[0].max_rank, &L);
+    if (st != LORA_OK) return st;
+    if (T == 0) return LORA_OK;
+    return launch_shrink(x, T, pools, n_slices, ids, mode == LORA_MODE_SGMV, v, L, ws, hs(stream));
+}
+
+lora_status_t lora_linear_forward_sliced(const void *x, const void *const *W, void *const *y,
+                                         int32_t T, const lora_pool_t *pools, int32_t n_slices,
+                                         const int32_t *ids, lora_mode_t mode, uint32_t flags,
+                                         void *ws, size_t ws_bytes, lora_stream_t stream) {
+    lora_status_t st = check_slices(pools, n_slices);
+    if (st != LORA_OK) return st;
+    if (T < 0 || !valid_mode(mode) || (flags & ~3u) || !W || !y) return LORA_ERR_INVALID_ARGUMENT;
+    if (T > 0) {
+        if (!x || !ids || !aligned16(x)) return LORA_ERR_INVALID_ARGUMENT;
+        for (int i = 0; i < n_slices; ++i)
+            if (!W[i] || !y[i] || !aligned16(W[i]) || !aligned16(y[i])) return LORA_ERR_INVALID_ARGUMENT;
     }
-    return launch_gemm(x, W, y, T, pool->d_in, pool->d_out, pool->dtype, pool, ids, v, perm,
-                       ws_ptr<float>(ws, L.gemm_partial), ws_bytes - L.gemm_partial, s);
+    const int32_t R = pools[0].max_rank, VS = n_slices * R;
+    ws_layout L;
+    st = check_ws(ws, ws_bytes, T, pools[0].n_slots, VS, &L);
+    if (st != LORA_OK) return st;
+    if (T == 0) return LORA_OK;
+    const hipStream_t s = hs(stream);
+    const bool sgmv = use_sgmv(mode, T);
+    // Each slice takes the path lora_linear_forward would take for it:
+    // decode-sized BGMV batches compute the shrink inside that slice's GEMM
+    // (on the x it streams anyway); the other slices share one shrink.
+    const bool try_fused = !sgmv && !(flags & LORA_FLAG_SEPARATE_EXPAND) && pools[0].dtype == LORA_BF16;
+    bool fused[kMaxSlices], any_shared = false;
+    for (int i = 0; i < n_slices; ++i) {
+        fused[i] = try_fused &&
+                   gemm_fused_shrink_ok(T, pools[i].d_in, pools[i].d_out, R, ws_bytes - L.gemm_partial);
+        any_shared |= !fused[i];
+    }
+    float *v = ws_ptr<float>(ws, L.v);
+    if (any_shared) {
+        if (sgmv && !(flags & LORA_FLAG_SEGMENTS_READY)) {
+            st = launch_segments(ids, T, pools[0].n_slots, L, ws, s);
+            if (st != LORA_OK) return st;
+        }
+        st = launch_shrink(x, T, pools, n_slices, ids, sgmv, v, L, ws, s);   // one x read, one launch
+        if (st != LORA_OK) return st;
+    }
+    for (int i = 0; i < n_slices; ++i) {
+        if (fused[i])
+            st = launch_gemm_fused_shrink(x, W[i], y[i], T, &pools[i], ids, ws_ptr<float>(ws, L.partial),
+                                          ws_ptr<int32_t>(ws, L.header), ws_ptr<float>(ws, L.gemm_partial),
+                                          ws_bytes - L.gemm_partial, s);
+        else
+            st = gemm_and_expand(x, W[i], y[i], T, pools[i], ids, v + i * R, VS, sgmv, flags, L, ws,
+                                 ws_bytes, s);
+        if (st != LORA_OK) return st;
+    }
+    return LORA_OK;
 }
 
 lora_status_t lora_get_device_error(void *ws, size_t ws_bytes, lora_stream_t stream,

@@ -95,6 +95,8 @@ __device__ __forceinline__ void flag_bad_row(int32_t *err, int32_t row) {
 constexpr int32_t kSegTile = 1024;     // rows per segment-builder tile
 constexpr int32_t kShrinkRows = 32;    // rows of one segment per grouped-shrink work block
 constexpr int32_t kMaxKSplit = 16;     // shrink k-split factor bound
+constexpr int32_t kMaxSlices = 4;      // pools sharing one shrink (projections that share x)
+constexpr int32_t kMaxSliceRanks = 128; // their summed max_rank
 constexpr int32_t kMaxSlots = 16000;   // slots per pool (LDS histogram bound, < 64 KiB)
 constexpr int32_t kErrNone = 0x7fffffff;
 constexpr int32_t kMaxGemmSplit = 16;   // split-K GEMM: most K ranges per tile
@@ -162,10 +164,14 @@ lora_status_t launch_pool_clear(const lora_pool_t &p, int32_t slot, hipStream_t 
 lora_status_t launch_ws_init(void *ws, hipStream_t s);
 lora_status_t launch_segments(const int32_t *ids, int32_t T, int32_t n_slots, const ws_layout &L,
                               void *ws, hipStream_t s);
-lora_status_t launch_shrink(const void *x, int32_t T, const lora_pool_t &p, const int32_t *ids,
-                            bool sgmv, float *v, const ws_layout &L, void *ws, hipStream_t s);
-lora_status_t launch_expand(const float *v, int32_t T, const lora_pool_t &p, const int32_t *ids,
-                            bool sgmv, void *y, const ws_layout &L, void *ws, hipStream_t s);
+// Shrink for n_slices pools that share x, ids, n_slots, d_in, max_rank and
+// dtype: v[t][s * max_rank + j] for slice s (row stride n_slices * max_rank).
+lora_status_t launch_shrink(const void *x, int32_t T, const lora_pool_t *pools, int32_t n_slices,
+                            const int32_t *ids, bool sgmv, float *v, const ws_layout &L, void *ws,
+                            hipStream_t s);
+lora_status_t launch_expand(const float *v, int32_t v_stride, int32_t T, const lora_pool_t &p,
+                            const int32_t *ids, bool sgmv, void *y, const ws_layout &L, void *ws,
+                            hipStream_t s);
 // y = x W (+ s v B when pool != nullptr); rows in perm order when perm != nullptr.
 bool gemm_fused_shrink_ok(int32_t T, int32_t d_in, int32_t d_out, int32_t max_rank,
                           size_t partial_bytes);
@@ -175,7 +181,7 @@ lora_status_t launch_gemm_fused_shrink(const void *x, const void *W, void *y, in
                                        hipStream_t s);
 lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int32_t d_in,
                           int32_t d_out, int32_t dtype, const lora_pool_t *pool,
-                          const int32_t *ids, const float *v, const int32_t *perm,
-                          float *partial, size_t partial_bytes, hipStream_t s);
+                          const int32_t *ids, const float *v, int32_t v_stride,
+                          const int32_t *perm, float *partial, size_t partial_bytes, hipStream_t s);
 
 }  // namespace lora

@@ -25,6 +25,7 @@ __global__ void __launch_bounds__(256) k_expand_rows(const float *__restrict__ v
                                                      const float *__restrict__ scale,
                                                      const int32_t *__restrict__ rank,
                                                      int32_t n_slots, int32_t max_rank,
+                                                     int32_t v_stride,
                                                      const int32_t *__restrict__ ids,
                                                      const int32_t *__restrict__ perm,
                                                      typename elem<DT>::T *__restrict__ y) {
@@ -39,7 +40,7 @@ __global__ void __launch_bounds__(256) k_expand_rows(const float *__restrict__ v
     const int32_t r = rank[id];
     if (r <= 0) return;
     const float s = scale[id];
-    for (int j = threadIdx.x; j < max_rank; j += 256) s_v[j] = v[(size_t)t * max_rank + j];
+    for (int j = threadIdx.x; j < max_rank; j += 256) s_v[j] = v[(size_t)t * v_stride + j];
     __syncthreads();
     const int n0 = (blockIdx.y * 256 + threadIdx.x) * 8;
     if (n0 >= d_out) return;
@@ -84,17 +85,18 @@ __global__ void __launch_bounds__(256) k_expand_rows(const float *__restrict__ v
     }
 }
 
-lora_status_t launch_expand(const float *v, int32_t T, const lora_pool_t &p, const int32_t *ids,
-                            bool sgmv, void *y, const ws_layout &L, void *ws, hipStream_t s) {
+lora_status_t launch_expand(const float *v, int32_t v_stride, int32_t T, const lora_pool_t &p,
+                            const int32_t *ids, bool sgmv, void *y, const ws_layout &L, void *ws,
+                            hipStream_t s) {
     const int32_t *perm = sgmv ? ws_ptr<int32_t>(ws, L.perm) : nullptr;
     const dim3 grid(T, (p.d_out + 2047) / 2048);
     if (p.dtype == LORA_F32)
         hipLaunchKernelGGL(k_expand_rows<LORA_F32>, grid, dim3(256), 0, s, v, T, p.d_out,
-                           (const float *)p.b, p.scale, p.rank, p.n_slots, p.max_rank, ids, perm,
+                           (const float *)p.b, p.scale, p.rank, p.n_slots, p.max_rank, v_stride, ids, perm,
                            (float *)y);
     else
         hipLaunchKernelGGL(k_expand_rows<LORA_BF16>, grid, dim3(256), 0, s, v, T, p.d_out,
-                           (const uint16_t *)p.b, p.scale, p.rank, p.n_slots, p.max_rank, ids,
+                           (const uint16_t *)p.b, p.scale, p.rank, p.n_slots, p.max_rank, v_stride, ids,
                            perm, (uint16_t *)y);
     return hip_status(hipGetLastError());
 }

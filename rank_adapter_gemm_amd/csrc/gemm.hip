@@ -38,7 +38,8 @@ struct gemm_args {
     const int32_t *rank;
     int32_t n_slots, max_rank;
     const int32_t *ids;
-    const float *v;
+    const float *v;                // [T][v_stride] fp32, this pool's ranks at columns 0..max_rank-1
+    int32_t v_stride;
     int32_t n_tiles_m, n_tiles_n;
     int32_t tile_base, n_tiles;    // this launch: tiles [tile_base, tile_base + n_tiles) in tile order
     int32_t splits, k_chunk;       // split-K: number of K ranges and their length
@@ -149,7 +150,7 @@ __device__ __forceinline__ void lora_pass_impl(const gemm_args &g, f32x16_t (&ac
             const int32_t ra = g.rank[a];
             const float sa = g.scale[a];
             const uint32_t vm = (my_id == a) ? ~0u : 0u;
-            const float *vrow = g.v + (int64_t)(my_id == a ? my_t : 0) * R;
+            const float *vrow = g.v + (int64_t)(my_id == a ? my_t : 0) * g.v_stride;
             for (int ks = 0; ks * 16 < ra; ++ks) {
                 const int j0 = 16 * ks + 8 * half;
                 const int oct = 2 * ks + half;
@@ -569,7 +570,7 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g) {
             if (rk > 0) {
                 float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
                 lora_delta8(g.b, raw, R, N, n, (rk + 7) >> 3,
-                            VP ? s_v + (r - chunk * RW) * R : g.v + (int64_t)t * R, d);
+                            VP ? s_v + (r - chunk * RW) * R : g.v + (int64_t)t * g.v_stride, d);
                 const float sc = g.scale[raw];
 #pragma unroll
                 for (int q = 0; q < 8; ++q) o[q] = fmaf(sc, d[q], o[q]);
@@ -591,6 +592,7 @@ struct gemm_f32_args {
     int32_t n_slots, max_rank;
     const int32_t *ids;
     const float *v;
+    int32_t v_stride;
     int32_t n_tiles_n;
 };
 
@@ -657,7 +659,7 @@ __global__ void __launch_bounds__(256) k_gemm_f32(gemm_f32_args g) {
             float val = acc[i][j];
             if (LORA && id >= 0) {
                 const float *bq = g.b + ((int64_t)id * g.max_rank * N + (int64_t)n * 8);
-                const float *vi = g.v + t * g.max_rank;
+                const float *vi = g.v + t * g.v_stride;
                 float d = 0.0f;
                 for (int q = 0; q < r; ++q) d = fmaf(vi[q], bq[(int64_t)(q >> 3) * N * 8 + (q & 7)], d);
                 val = fmaf(s, d, val);
@@ -780,6 +782,7 @@ lora_status_t launch_gemm_fused_shrink(const void *x, const void *W, void *y, in
     g.max_rank = pool->max_rank;
     g.ids = ids;
     g.v = nullptr;
+    g.v_stride = pool->max_rank;
     const gemm_plan pl = plan_gemm(T, g.K, g.N, partial_bytes);
     g.n_tiles_m = ceil_div(T, pl.bm);
     g.n_tiles_n = ceil_div(g.N, pl.bn);
@@ -799,8 +802,8 @@ lora_status_t launch_gemm_fused_shrink(const void *x, const void *W, void *y, in
 
 lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int32_t d_in,
                           int32_t d_out, int32_t dtype, const lora_pool_t *pool,
-                          const int32_t *ids, const float *v, const int32_t *perm,
-                          float *partial, size_t partial_bytes, hipStream_t s) {
+                          const int32_t *ids, const float *v, int32_t v_stride,
+                          const int32_t *perm, float *partial, size_t partial_bytes, hipStream_t s) {
     if (dtype == LORA_BF16) {
         gemm_args g;
         g.x = (const uint16_t *)x;
@@ -817,6 +820,7 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
         g.max_rank = pool ? pool->max_rank : 0;
         g.ids = ids;
         g.v = v;
+        g.v_stride = v_stride;
         const gemm_plan pl = plan_gemm(T, d_in, d_out, partial ? partial_bytes : 0);
         g.n_tiles_m = ceil_div(T, pl.bm);
         g.n_tiles_n = ceil_div(d_out, pl.bn);
@@ -846,6 +850,7 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
         g.max_rank = pool ? pool->max_rank : 0;
         g.ids = ids;
         g.v = v;
+        g.v_stride = v_stride;
         g.n_tiles_n = (d_out + 63) / 64;
         const int tiles = ((T + 63) / 64) * g.n_tiles_n;
         if (pool)

@@ -22,6 +22,15 @@
 
 namespace lora {
 
+// Pools that share x, ids, n_slots, d_in, max_rank and dtype (projections
+// fed by the same input): one shrink reads x once for all of them and
+// writes v[t][s * max_rank + j] for slice s.
+struct slice_set {
+    const void *a[kMaxSlices];
+    const int32_t *rank[kMaxSlices];
+    int32_t n;
+};
+
 // ---------------------------------------------------------------------------
 // Transposing butterfly: on entry each lane holds N partial sums acc[0..N)
 // (N a power of two, N <= 64); on exit lane l holds, in acc[0], the full sum
@@ -64,9 +73,7 @@ __device__ __forceinline__ int owned_index(int lane) {
 
 template <int DT, int RM>
 __global__ void __launch_bounds__(512) k_shrink_rows(const typename elem<DT>::T *__restrict__ x,
-                                                     int32_t T, int32_t d_in,
-                                                     const typename elem<DT>::T *__restrict__ a,
-                                                     const int32_t *__restrict__ rank,
+                                                     int32_t T, int32_t d_in, slice_set ss,
                                                      int32_t n_slots, int32_t max_rank,
                                                      const int32_t *__restrict__ ids,
                                                      const int32_t *__restrict__ perm,
@@ -82,15 +89,22 @@ __global__ void __launch_bounds__(512) k_shrink_rows(const typename elem<DT>::T 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int32_t id = ids[t];
     const bool in_range = id >= 0 && id < n_slots;
-    const int32_t r = in_range ? rank[id] : 0;
-    if (tid == 0 && ((id < -1 || id >= n_slots) || (in_range && r == 0))) flag_bad_row(err, t);
-    float *vt = v + (size_t)t * max_rank;
-    if (r <= 0) {
-        for (int j = tid; j < max_rank; j += NW * 64) vt[j] = 0.0f;
-        return;
-    }
+    bool any_empty = false;
+    if (in_range)
+        for (int sl = 0; sl < ss.n; ++sl) any_empty |= ss.rank[sl][id] <= 0;
+    if (tid == 0 && ((id < -1 || id >= n_slots) || (in_range && any_empty))) flag_bad_row(err, t);
+    const int VS = ss.n * max_rank;                       // v row stride
     const E *xt = x + (size_t)t * d_in;
-    const E *At = a + (size_t)id * max_rank * d_in;
+    // One slice after the other: x[t] comes from HBM for the first and from
+    // the cache for the rest.
+    for (int sl = 0; sl < ss.n; ++sl) {
+    const int32_t r = in_range ? ss.rank[sl][id] : 0;
+    float *vt = v + (size_t)t * VS + sl * max_rank;
+    if (r <= 0) {                                         // uniform: no adapter in this slice
+        for (int j = tid; j < max_rank; j += NW * 64) vt[j] = 0.0f;
+        continue;
+    }
+    const E *At = reinterpret_cast<const E *>(ss.a[sl]) + (size_t)id * max_rank * d_in;
     float acc[RM];
 #pragma unroll
     for (int j = 0; j < RM; ++j) acc[j] = 0.0f;
@@ -137,6 +151,8 @@ __global__ void __launch_bounds__(512) k_shrink_rows(const typename elem<DT>::T 
         }
         vt[j] = sum;
     }
+    __syncthreads();                                      // s_red is reused by the next slice
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -155,9 +171,9 @@ __global__ void __launch_bounds__(512) k_shrink_rows(const typename elem<DT>::T 
 // ---------------------------------------------------------------------------
 template <int RCH>   // 16-rank chunks
 __global__ void __launch_bounds__(256) k_shrink_grouped(
-    const uint16_t *__restrict__ x, int32_t T, int32_t d_in, const uint16_t *__restrict__ a,
-    const int32_t *__restrict__ rank, int32_t max_rank, const int32_t *__restrict__ perm,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ seg_id,
+    const uint16_t *__restrict__ x, int32_t T, int32_t d_in, slice_set ss, int32_t max_rank,
+    const int32_t *__restrict__ perm, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ seg_id,
     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ n_seg_p,
     const int32_t *__restrict__ blk_start, const int32_t *__restrict__ blk_seg,
     int32_t n_work_upper, int32_t k_chunk,
@@ -168,16 +184,17 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
     __shared__ float s_acc[4][BR][RCH * 16 + 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wid = blockIdx.x;
+    const int VS = ss.n * max_rank;                      // v row stride: all slices
     if (wid >= n_work_upper) {
         // base-only block: sorted positions [0, offsets[1]) get v = 0
         if (blockIdx.y != 0) return;
         const int p0 = (wid - n_work_upper) * BR;
         const int pend = min(offsets[1], p0 + BR);
-        for (int e = tid; e < BR * max_rank; e += 256) {
-            const int p = p0 + e / max_rank, j = e % max_rank;
+        for (int e = tid; e < BR * VS; e += 256) {
+            const int p = p0 + e / VS, j = e % VS;
             if (p < pend) {
                 const int32_t t = perm_row(perm, p, T);
-                if (t >= 0) v[(size_t)t * max_rank + j] = 0.0f;
+                if (t >= 0) v[(size_t)t * VS + j] = 0.0f;
             }
         }
         return;
@@ -188,7 +205,12 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
     const int32_t aid = seg_id[lo];
     const int p0 = seg_start[lo] + (wid - blk_start[lo]) * BR;
     const int pend = min(seg_start[lo + 1], p0 + BR);
-    const int32_t r = rank[aid];
+    bool any_rank = false, any_empty = false;
+    for (int sl = 0; sl < ss.n; ++sl) {
+        const int32_t rs = ss.rank[sl][aid];
+        any_rank |= rs > 0;
+        any_empty |= rs <= 0;
+    }
     const int k_begin = blockIdx.y * k_chunk;
     const int k_end = min(d_in, k_begin + k_chunk);
 
@@ -205,14 +227,17 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
         xm[rb] = t >= 0 ? ~0u : 0u;
         xoff[rb] = (int64_t)(t >= 0 ? t : (t_first >= 0 ? t_first : 0)) * d_in;
     }
-    const uint16_t *At = a + (size_t)aid * max_rank * d_in;
-    int64_t aoff[RCH];
-    uint32_t am[RCH];                                    // all-ones for a rank below r, else 0
+    // rank column j of the concatenated slices: slice j / max_rank, rank j % max_rank
+    const uint16_t *aptr[RCH];
+    uint32_t am[RCH];                                    // all-ones for a rank below the slice's r
 #pragma unroll
     for (int rc = 0; rc < RCH; ++rc) {
         const int j = rc * 16 + lr;
-        am[rc] = j < r ? ~0u : 0u;
-        aoff[rc] = (int64_t)min(j, r > 0 ? r - 1 : 0) * d_in;
+        const int sl = j / max_rank, jj = j - sl * max_rank;
+        const int32_t rs = sl < ss.n ? ss.rank[sl][aid] : 0;
+        am[rc] = jj < rs ? ~0u : 0u;
+        aptr[rc] = reinterpret_cast<const uint16_t *>(ss.a[sl < ss.n ? sl : 0]) +
+                   ((size_t)aid * max_rank + (rs > 0 ? min(jj, rs - 1) : 0)) * d_in;
     }
     f32x4_t acc[RBN][RCH];
 #pragma unroll
@@ -220,7 +245,7 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
 #pragma unroll
         for (int rc = 0; rc < RCH; ++rc) acc[rb][rc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    if (r > 0) {
+    if (any_rank) {
         for (int kb = k_begin + wave * 32; kb < k_end; kb += 4 * 32 * U) {
             uint4 xq[U][RBN], aq[U][RCH];
             uint32_t km[U];
@@ -232,7 +257,7 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
 #pragma unroll
                 for (int rb = 0; rb < RBN; ++rb) xq[u][rb] = ldg16(x + xoff[rb] + kc);
 #pragma unroll
-                for (int rc = 0; rc < RCH; ++rc) aq[u][rc] = ldg16(At + aoff[rc] + kc);
+                for (int rc = 0; rc < RCH; ++rc) aq[u][rc] = ldg16(aptr[rc] + kc);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -257,9 +282,9 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
                             __builtin_bit_cast(bf16x8_t, xq[u][rb]),
                             __builtin_bit_cast(bf16x8_t, aq[u][rc]), acc[rb][rc], 0, 0, 0);
         }
-    } else if (blockIdx.y == 0 && tid < BR && p0 + tid < pend) {
-        flag_bad_row(err, perm_row(perm, p0 + tid, T));     // segment of an empty slot
     }
+    if (any_empty && blockIdx.y == 0 && tid < BR && p0 + tid < pend)
+        flag_bad_row(err, perm_row(perm, p0 + tid, T));     // segment of an empty slot
 #pragma unroll
     for (int rb = 0; rb < RBN; ++rb)
 #pragma unroll
@@ -267,17 +292,17 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
 #pragma unroll
             for (int q = 0; q < 4; ++q) s_acc[wave][rb * 16 + 4 * kg + q][rc * 16 + lr] = acc[rb][rc][q];
     __syncthreads();
-    for (int e = tid; e < BR * max_rank; e += 256) {
-        const int i = e / max_rank, j = e % max_rank;
+    for (int e = tid; e < BR * VS; e += 256) {
+        const int i = e / VS, j = e % VS;
         const int p = p0 + i;
         if (p >= pend) continue;
         float sum = 0.0f;
         if (j < RCH * 16) sum = (s_acc[0][i][j] + s_acc[1][i][j]) + (s_acc[2][i][j] + s_acc[3][i][j]);
         if (partial) {
-            partial[((size_t)blockIdx.y * T + p) * max_rank + j] = sum;
+            partial[((size_t)blockIdx.y * T + p) * VS + j] = sum;
         } else {
             const int32_t t = perm_row(perm, p, T);
-            if (t >= 0) v[(size_t)t * max_rank + j] = sum;
+            if (t >= 0) v[(size_t)t * VS + j] = sum;
         }
     }
 }
@@ -303,14 +328,14 @@ __global__ void __launch_bounds__(256) k_shrink_reduce(const float *__restrict__
 }
 
 template <int DT>
-static void launch_rows(const void *x, int32_t T, const lora_pool_t &p, const int32_t *ids,
-                        const int32_t *perm, float *v, int32_t *err, hipStream_t s) {
+static void launch_rows(const void *x, int32_t T, const lora_pool_t &p, const slice_set &ss,
+                        const int32_t *ids, const int32_t *perm, float *v, int32_t *err,
+                        hipStream_t s) {
     typedef typename elem<DT>::T E;
     const E *xe = (const E *)x;
-    const E *ae = (const E *)p.a;
 #define LORA_SHRINK_ROWS(RMV)                                                                   \
-    hipLaunchKernelGGL((k_shrink_rows<DT, RMV>), dim3(T), dim3(512), 0, s, xe, T, p.d_in, ae,   \
-                       p.rank, p.n_slots, p.max_rank, ids, perm, v, err)
+    hipLaunchKernelGGL((k_shrink_rows<DT, RMV>), dim3(T), dim3(512), 0, s, xe, T, p.d_in, ss,   \
+                       p.n_slots, p.max_rank, ids, perm, v, err)
     if (p.max_rank <= 8) LORA_SHRINK_ROWS(8);
     else if (p.max_rank <= 16) LORA_SHRINK_ROWS(16);
     else if (p.max_rank <= 32) LORA_SHRINK_ROWS(32);
@@ -319,13 +344,23 @@ static void launch_rows(const void *x, int32_t T, const lora_pool_t &p, const in
 #undef LORA_SHRINK_ROWS
 }
 
-lora_status_t launch_shrink(const void *x, int32_t T, const lora_pool_t &p, const int32_t *ids,
-                            bool sgmv, float *v, const ws_layout &L, void *ws, hipStream_t s) {
+lora_status_t launch_shrink(const void *x, int32_t T, const lora_pool_t *pools, int32_t n_slices,
+                            const int32_t *ids, bool sgmv, float *v, const ws_layout &L, void *ws,
+                            hipStream_t s) {
+    const lora_pool_t &p = pools[0];
+    slice_set ss;
+    ss.n = n_slices;
+    for (int i = 0; i < kMaxSlices; ++i) {
+        const lora_pool_t &q = pools[i < n_slices ? i : 0];
+        ss.a[i] = q.a;
+        ss.rank[i] = q.rank;
+    }
+    const int32_t VS = n_slices * p.max_rank;
     int32_t *err = ws_ptr<int32_t>(ws, L.header);
     const int32_t *perm = sgmv ? ws_ptr<int32_t>(ws, L.perm) : nullptr;
     if (!sgmv || p.dtype == LORA_F32) {
-        if (p.dtype == LORA_F32) launch_rows<LORA_F32>(x, T, p, ids, perm, v, err, s);
-        else launch_rows<LORA_BF16>(x, T, p, ids, perm, v, err, s);
+        if (p.dtype == LORA_F32) launch_rows<LORA_F32>(x, T, p, ss, ids, perm, v, err, s);
+        else launch_rows<LORA_BF16>(x, T, p, ss, ids, perm, v, err, s);
         return hip_status(hipGetLastError());
     }
     // SGMV bf16: grouped over segment blocks; split K so that about 512
@@ -340,12 +375,11 @@ lora_status_t launch_shrink(const void *x, int32_t T, const lora_pool_t &p, cons
     split = (p.d_in + k_chunk - 1) / k_chunk;
     float *partial = split > 1 ? ws_ptr<float>(ws, L.partial) : nullptr;
     const uint16_t *xe = (const uint16_t *)x;
-    const uint16_t *ae = (const uint16_t *)p.a;
-    const int rc = (p.max_rank + 15) / 16;
+    const int rc = (VS + 15) / 16;
     const int32_t *offsets = ws_ptr<int32_t>(ws, L.offsets);
     const dim3 grid(n_work_upper + row_blocks, split);
 #define LORA_SHRINK_GROUPED(RCV)                                                                  \
-    hipLaunchKernelGGL((k_shrink_grouped<RCV>), grid, dim3(256), 0, s, xe, T, p.d_in, ae, p.rank, \
+    hipLaunchKernelGGL((k_shrink_grouped<RCV>), grid, dim3(256), 0, s, xe, T, p.d_in, ss,         \
                        p.max_rank, perm, offsets, ws_ptr<int32_t>(ws, L.seg_id),                  \
                        ws_ptr<int32_t>(ws, L.seg_start), ws_ptr<int32_t>(ws, L.n_seg),            \
                        ws_ptr<int32_t>(ws, L.blk_start), ws_ptr<int32_t>(ws, L.blk_seg),          \
@@ -362,11 +396,11 @@ lora_status_t launch_shrink(const void *x, int32_t T, const lora_pool_t &p, cons
     }
 #undef LORA_SHRINK_GROUPED
     if (split > 1) {
-        size_t n = (size_t)T * p.max_rank;
+        size_t n = (size_t)T * VS;
         int g = (int)((n + 255) / 256);
         if (g > 4096) g = 4096;
-        hipLaunchKernelGGL(k_shrink_reduce, dim3(g), dim3(256), 0, s, partial, split, T,
-                           p.max_rank, perm, offsets, v);
+        hipLaunchKernelGGL(k_shrink_reduce, dim3(g), dim3(256), 0, s, partial, split, T, VS, perm,
+                           offsets, v);
     }
     return hip_status(hipGetLastError());
 }

@@ -37,6 +37,7 @@ EXPORTED = (
     "lora_pool_bytes", "lora_pool_create", "lora_pool_upload", "lora_pool_clear",
     "lora_workspace_bytes", "lora_workspace_init", "lora_segments_view", "lora_build_segments",
     "lora_shrink", "lora_expand", "lora_gemm", "lora_gemm_expand", "lora_linear_forward",
+    "lora_workspace_bytes_sliced", "lora_shrink_sliced", "lora_linear_forward_sliced",
     "lora_get_device_error",
     "lora_status_string", "lora_version",
 )
@@ -104,6 +105,10 @@ def load(path: str = LIB_PATH):
         "lora_gemm": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_sz, c_vp]),
         "lora_gemm_expand": (c_i32, [c_vp, c_vp, c_vp, c_i32, P(lora_pool_t), c_vp, c_vp, c_i32, c_vp, c_sz, c_vp]),
         "lora_linear_forward": (c_i32, [c_vp, c_vp, c_vp, c_i32, P(lora_pool_t), c_vp, c_i32, c_u32, c_vp, c_sz, c_vp]),
+        "lora_workspace_bytes_sliced": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
+        "lora_shrink_sliced": (c_i32, [c_vp, c_i32, P(lora_pool_t), c_i32, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
+        "lora_linear_forward_sliced": (c_i32, [c_vp, P(c_vp), P(c_vp), c_i32, P(lora_pool_t), c_i32, c_vp,
+                                               c_i32, c_u32, c_vp, c_sz, c_vp]),
         "lora_get_device_error": (c_i32, [c_vp, c_sz, c_vp, P(c_i32)]),
         "lora_status_string": (ctypes.c_char_p, [c_i32]),
         "lora_version": (ctypes.c_char_p, []),
@@ -229,6 +234,34 @@ def lora_linear_forward(x, W, y, T, pool, ids, mode, flags, ws, stream=None):
         "lora_linear_forward")
 
 
+def lora_workspace_bytes_sliced(T, n_slots, max_rank, n_slices, d_out=0) -> int:
+    return int(load().lora_workspace_bytes_sliced(T, n_slots, max_rank, n_slices, d_out))
+
+
+def _pool_array(pools):
+    arr = (lora_pool_t * len(pools))()
+    for i, p in enumerate(pools):
+        arr[i] = p
+    return arr
+
+
+def lora_shrink_sliced(x, T, pools, ids, mode, v, ws, stream=None):
+    """pools: a list of lora_pool_t (one per slice)."""
+    _ok(load().lora_shrink_sliced(_ptr(x), T, _pool_array(pools), len(pools), _ptr(ids), mode, _ptr(v),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+        "lora_shrink_sliced")
+
+
+def lora_linear_forward_sliced(x, Ws, ys, T, pools, ids, mode, flags, ws, stream=None):
+    """Ws, ys: lists of device tensors, one per slice; pools: list of lora_pool_t."""
+    n = len(pools)
+    w_arr = (ctypes.c_void_p * n)(*[_ptr(w) for w in Ws])
+    y_arr = (ctypes.c_void_p * n)(*[_ptr(y) for y in ys])
+    _ok(load().lora_linear_forward_sliced(_ptr(x), w_arr, y_arr, T, _pool_array(pools), n, _ptr(ids), mode,
+                                          flags, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+        "lora_linear_forward_sliced")
+
+
 def lora_get_device_error(ws, stream=None) -> int:
     row = ctypes.c_int32()
     _ok(load().lora_get_device_error(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream),
@@ -269,8 +302,8 @@ class AdapterPool:
 class Workspace:
     """A device workspace sized for (T, n_slots, max_rank, d_out), initialised."""
 
-    def __init__(self, T, n_slots, max_rank, d_out=0, device="cuda", stream=None):
-        n = lora_workspace_bytes(T, n_slots, max_rank, d_out)
+    def __init__(self, T, n_slots, max_rank, d_out=0, device="cuda", stream=None, n_slices=1):
+        n = lora_workspace_bytes_sliced(T, n_slots, max_rank, n_slices, d_out)
         if n == 0:
             raise LoraError(LORA_ERR_INVALID_ARGUMENT, "lora_workspace_bytes")
         self.T, self.n_slots, self.max_rank = T, n_slots, max_rank

@@ -126,3 +126,44 @@ def test_segments_view_is_pointer_arithmetic(lib):
     assert lib.lora_segments_view(fake, L.lora_workspace_bytes(100, 10, 64), 100, 10, 64,
                                   ctypes.byref(seg2)) == L.LORA_OK
     assert seg2.perm == seg.perm and seg2.offsets == seg.offsets
+
+
+def test_sliced_validation(lib):
+    """Pools of one sliced call must agree on n_slots, d_in, max_rank and
+    dtype; at most 4 slices and 128 summed ranks.  All checks run on the host
+    before anything is enqueued (fake device addresses)."""
+    fake = 1 << 40
+    P = L.lora_pool_t
+    q = P(8, 256, 512, 16, L.LORA_BF16, fake, fake, fake, fake)
+    k = P(8, 256, 128, 16, L.LORA_BF16, fake, fake, fake, fake)
+    assert L.lora_workspace_bytes_sliced(64, 8, 16, 3, 512) == L.lora_workspace_bytes(64, 8, 48, 512)
+    assert L.lora_workspace_bytes_sliced(64, 8, 16, 1, 0) == L.lora_workspace_bytes(64, 8, 16, 0)
+    assert L.lora_workspace_bytes_sliced(64, 8, 64, 3, 0) == 0        # 192 ranks
+    assert L.lora_workspace_bytes_sliced(64, 8, 16, 5, 0) == 0
+    need = L.lora_workspace_bytes_sliced(64, 8, 16, 3, 512)
+    arr = L._pool_array([q, k, k])
+    f = lib.lora_shrink_sliced
+    bad = L._pool_array([q, P(8, 264, 128, 16, L.LORA_BF16, fake, fake, fake, fake)])
+    assert f(fake, 64, bad, 2, fake, 0, fake, fake, need, None) == L.LORA_ERR_INVALID_ARGUMENT
+    bad = L._pool_array([q, P(8, 256, 128, 32, L.LORA_BF16, fake, fake, fake, fake)])
+    assert f(fake, 64, bad, 2, fake, 0, fake, fake, need, None) == L.LORA_ERR_INVALID_ARGUMENT
+    bad = L._pool_array([q, P(9, 256, 128, 16, L.LORA_BF16, fake, fake, fake, fake)])
+    assert f(fake, 64, bad, 2, fake, 0, fake, fake, need, None) == L.LORA_ERR_INVALID_ARGUMENT
+    five = L._pool_array([q] * 5)
+    assert f(fake, 64, five, 5, fake, 0, fake, fake, need, None) == L.LORA_ERR_UNSUPPORTED
+    big = P(8, 256, 512, 128, L.LORA_BF16, fake, fake, fake, fake)
+    assert f(fake, 64, L._pool_array([big, big]), 2, fake, 0, fake, fake, need, None) == L.LORA_ERR_UNSUPPORTED
+    assert f(fake, 64, arr, 0, fake, 0, fake, fake, need, None) == L.LORA_ERR_INVALID_ARGUMENT
+    need0 = L.lora_workspace_bytes_sliced(64, 8, 16, 3, 0)     # the check these entry points make
+    assert f(fake, 64, arr, 3, fake, 0, fake, fake, need0 - 1, None) == L.LORA_ERR_WORKSPACE_TOO_SMALL
+    assert f(fake, 64, L._pool_array([q]), 1, fake, 0, fake, fake, L.lora_workspace_bytes(64, 8, 16) - 1,
+             None) == L.LORA_ERR_WORKSPACE_TOO_SMALL
+    assert f(None, 0, arr, 3, None, 0, None, fake, need, None) == L.LORA_OK   # T == 0
+    g = lib.lora_linear_forward_sliced
+    W = (ctypes.c_void_p * 3)(fake, fake, fake)
+    Y = (ctypes.c_void_p * 3)(fake, fake, None)
+    assert g(fake, W, Y, 64, arr, 3, fake, 0, 0, fake, need, None) == L.LORA_ERR_INVALID_ARGUMENT
+    Y = (ctypes.c_void_p * 3)(fake, fake, fake + 8)
+    assert g(fake, W, Y, 64, arr, 3, fake, 0, 0, fake, need, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert g(fake, W, Y, 64, arr, 3, fake, 0, 8, fake, need, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert g(None, W, Y, 0, arr, 3, None, 0, 0, fake, need, None) == L.LORA_OK
