@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--workload", default="decode_bgmv")
     ap.add_argument("--mode", default="auto", choices=["auto", "bgmv", "sgmv"])
     ap.add_argument("--separate-expand", action="store_true")
+    ap.add_argument("--no-slices", action="store_true",
+                    help="one lora_linear_forward per projection, also where projections share x")
     ap.add_argument("--cold-sets", type=int, default=None, help="copies of the working set to rotate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU work of the oracle sample")
@@ -129,17 +131,36 @@ def main():
                 ps.append(q)
         ys = [torch.empty(T, p.d_out, dtype=wl.dtype, device=dev) for p in wl.projections]
         sets.append(dict(xs=xs, Ws=Ws, pools=ps, ys=ys, keep=keep))
-    ws = L.Workspace(T, wl.n_slots, R, max(p.d_out for p in wl.projections), device=dev)
+    # Projections that share an input (consecutive, same x) run as slices of
+    # one lora_linear_forward_sliced call: one shrink, one read of x.
+    groups = []
+    for k, pr in enumerate(wl.projections):
+        if (not args.no_slices and groups and wl.projections[groups[-1][0]].x_group == pr.x_group
+                and len(groups[-1]) < 4 and (len(groups[-1]) + 1) * R <= 128):
+            groups[-1].append(k)
+        else:
+            groups.append([k])
+    ws = L.Workspace(T, wl.n_slots, R, max(p.d_out for p in wl.projections), device=dev,
+                     n_slices=max(len(g) for g in groups))
     v = torch.empty(T, R, dtype=torch.float32, device=dev)
     flags0 = L.LORA_FLAG_SEPARATE_EXPAND if args.separate_expand else 0
     torch.cuda.synchronize()
 
+    def forward_group(gi, i):
+        s_ = sets[i % n_sets]
+        grp = groups[gi]
+        fl = flags0 | (L.LORA_FLAG_SEGMENTS_READY if (sgmv and gi > 0) else 0)
+        x = s_["xs"][wl.projections[grp[0]].x_group]
+        if len(grp) == 1:
+            k = grp[0]
+            L.lora_linear_forward(x, s_["Ws"][k], s_["ys"][k], T, s_["pools"][k], ids, mode, fl, ws.buf)
+        else:
+            L.lora_linear_forward_sliced(x, [s_["Ws"][k] for k in grp], [s_["ys"][k] for k in grp], T,
+                                         [s_["pools"][k] for k in grp], ids, mode, fl, ws.buf)
+
     def step(i):
-        s = sets[i % n_sets]
-        for k, pr in enumerate(wl.projections):
-            fl = flags0 | (L.LORA_FLAG_SEGMENTS_READY if (sgmv and k > 0) else 0)
-            L.lora_linear_forward(s["xs"][pr.x_group], s["Ws"][k], s["ys"][k], T, s["pools"][k], ids,
-                                  mode, fl, ws.buf)
+        for gi in range(len(groups)):
+            forward_group(gi, i)
 
     # The step is captured into HIP graphs (one graph replays every working-set
     # copy once) so host-side launch overhead is not part of the timing.
@@ -229,20 +250,14 @@ def main():
     # The step itself calls lora_linear_forward once per projection; time each
     # of those calls alone the same way (segments already built for k > 0).
     fwd = {}
-    for k in range(len(wl.projections)):
-        def fcall(i, k=k):
-            s_ = sets[i % n_sets]
-            pr = wl.projections[k]
-            fl = flags0 | (L.LORA_FLAG_SEGMENTS_READY if (sgmv and k > 0) else 0)
-            L.lora_linear_forward(s_["xs"][pr.x_group], s_["Ws"][k], s_["ys"][k], T, s_["pools"][k], ids,
-                                  mode, fl, ws.buf)
+    for gi in range(len(groups)):
         for i in range(2):
-            fcall(i)
+            forward_group(gi, i)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(reps):
-                fcall(i)
+                forward_group(gi, i)
         g.replay()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -253,7 +268,7 @@ def main():
             g.replay()
         e1.record()
         torch.cuda.synchronize()
-        fwd[k] = e0.elapsed_time(e1) / (n_rep * reps)
+        fwd[gi] = e0.elapsed_time(e1) / (n_rep * reps)
         del g
 
     # ---- algorithmic bytes / flops per launch ----
@@ -279,17 +294,23 @@ def main():
             return by, 2 * T * d_in * d_out + 2 * sum_row_r * d_out
         raise KeyError(name)
 
-    def fwd_work(k):
-        """One forward of projection k: x read once (shrink and base product
-        share it), W, y written, the used adapters' A and B, segments."""
-        pr = wl.projections[k]
-        b_g, f_g = work("gemm", pr)
-        b_s, f_s = work("shrink", pr)
-        b_e, f_e = work("expand", pr)
-        by = b_g + (b_s - T * pr.d_in * eb - T * R * 4) + (b_e - T * R * 4 - 2 * T * pr.d_out * eb)
-        if sgmv and k == 0:
-            by += work("segments", pr)[0]
-        return by, f_g + f_s + f_e
+    def fwd_work(gi):
+        """One forward call of group gi: x read once (shrink and base
+        products share it), each slice's W and y, the used adapters' A and B,
+        segments for the first call of an SGMV step."""
+        by = fl = 0
+        for j, k in enumerate(groups[gi]):
+            pr = wl.projections[k]
+            b_g, f_g = work("gemm", pr)
+            b_s, f_s = work("shrink", pr)
+            b_e, f_e = work("expand", pr)
+            by += b_g + (b_s - T * pr.d_in * eb - T * R * 4) + (b_e - T * R * 4 - 2 * T * pr.d_out * eb)
+            if j > 0:
+                by -= T * pr.d_in * eb                   # x is shared by the slices
+            fl += f_g + f_s + f_e
+        if sgmv and gi == 0:
+            by += work("segments", wl.projections[groups[0][0]])[0]
+        return by, fl
 
     breakdown = {}
     for name in names:
@@ -319,15 +340,15 @@ def main():
         roof = dict(bound="hbm", achieved=round(by_d / t_d / 1e9, 1), peak=HBM_PEAK_GBS, unit="GB/s")
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["kernel"] = "forward"
-    roof["projection"] = wl.projections[kd].name
+    roof["projection"] = "+".join(wl.projections[k].name for k in groups[kd])
     roof["launches_per_step"] = 1
     roof["avg_launch_us"] = round(fwd[kd] * 1e3, 3)
     roof["algorithmic_bytes_per_launch"] = int(by_d)
     roof["algorithmic_flops_per_launch"] = int(fl_d)
-    roof["traffic"] = stored_traffic("forward", args.workload, wl.projections[kd].name)
+    roof["traffic"] = stored_traffic("forward", args.workload, roof["projection"])
     breakdown["forward"] = dict(us_per_step=round(1e3 * sum(fwd.values()), 3),
-                                per_projection_us={wl.projections[k].name: round(1e3 * v, 3)
-                                                   for k, v in fwd.items()})
+                                per_call_us={"+".join(wl.projections[k].name for k in groups[gi]):
+                                             round(1e3 * v, 3) for gi, v in fwd.items()})
 
     # ---- calibration copy kernel (counter scaling runs) ----
     if args.calib_copy:
@@ -362,6 +383,7 @@ def main():
             "n_slots": wl.n_slots, "max_rank": R, "distinct_adapters": int(used.size),
             "mode": ("sgmv" if sgmv else "bgmv") + ("" if args.mode != "auto" else " (auto)"),
             "expand": "separate" if args.separate_expand else "fused into the base GEMM",
+            "calls": ["+".join(wl.projections[k].name for k in g) for g in groups],
             "cold_sets": n_sets, "working_set_MB": round(set_bytes / 1e6, 1),
         },
         "roofline": roof,
