@@ -154,7 +154,7 @@ __device__ __forceinline__ void lora_pass_impl(const gemm_args &g, f32x16_t (&ac
             for (int ks = 0; ks * 16 < ra; ++ks) {
                 const int j0 = 16 * ks + 8 * half;
                 const int oct = 2 * ks + half;
-                const bool j_ok = j0 < R;
+                const bool j_ok = j0 < ra;              // octets past the slot's rank: not read
                 const float *vp = vrow + (j_ok ? j0 : 0);
                 float4 v0 = *reinterpret_cast<const float4 *>(vp);
                 float4 v1 = *reinterpret_cast<const float4 *>(vp + 4);

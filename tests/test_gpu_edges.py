@@ -250,3 +250,22 @@ def test_split_k_and_tile_configs(T, d_in, d_out):
     base = c.oracle(ids=np.full(T, -1, np.int32))
     assert_parity(y1, base, torch.bfloat16, "gemm split")
     assert_parity(y2, base, torch.bfloat16, "gemm")
+
+
+@pytest.mark.parametrize("T", [300, 1500])
+def test_padding_to_max_rank_does_not_change_results(T):
+    """The same adapters (ranks 3..16) in pools padded to max_rank 16, 32 and
+    64: kernels read only each slot's own rank rows, so the outputs agree to
+    fp32 summation order (and with the oracle), in both modes."""
+    ranks = [16, 3, 8, 13, 0, 9]
+    outs = {}
+    for R in (16, 32, 64):
+        c = Case(T=T, d_in=512, d_out=768, ranks=ranks, max_rank=R, dtype=torch.bfloat16, seed=3)
+        ref = c.oracle()
+        for mode in MODES:
+            y, _ = c.run(mode, 0)
+            assert_parity(y, ref, torch.bfloat16, "R=%d mode=%d" % (R, mode))
+            outs[(R, mode)] = y.float()
+    base = outs[(16, L.LORA_MODE_BGMV)]
+    for key, y in outs.items():
+        assert torch.max((y - base).abs() / (1 + base.abs())).item() <= 2 ** -7, key
