@@ -271,6 +271,67 @@ lora_status_t lora_linear_forward_sliced(const void *x, const void *const *W, vo
                                          const int32_t *ids, lora_mode_t mode, uint32_t flags,
                                          void *ws, size_t ws_bytes, lora_stream_t stream);
 
+/* ---- adapter residency: a host tier and the HBM slots as its cache ------------ */
+
+/* Adapters live in host DRAM and are brought into the pool's GPU slots on
+ * demand, least recently used out ("Multi-LoRA Serving: Architecture for
+ * Thousands of Adapters", sections "Unified paging of adapters and KV cache"
+ * and "A worked memory example"; "Serving LoRA adapters ...", Step 3: a fixed
+ * number of slots, LRU eviction, activation copies an adapter into its slot).
+ *
+ * Pack one adapter for a host tier: A HOST [d_in, r] (leading dimension lda)
+ * and B HOST [r, d_out] (ldb) into a_slot HOST [max_rank * d_in] and b_slot
+ * HOST [max_rank * d_out] elements in the pool's slot layout (A^T rank rows,
+ * B rank octets, zero rows past r), so that promotion into a slot is a plain
+ * copy.  Host only; no GPU work. */
+lora_status_t lora_pack_host(int32_t d_in, int32_t d_out, int32_t max_rank, lora_dtype_t dtype,
+                             const void *A, int32_t lda, const void *B, int32_t ldb, int32_t r,
+                             void *a_slot, void *b_slot);
+
+/* A residency cache over n_slots slots of n_pools pools (the projections of
+ * one layer set, kept in step: slot s holds the same adapter in every pool;
+ * all pools have n_slots slots, one max_rank and one dtype) for adapter ids
+ * 0..max_adapters-1.  n_pools == 0 gives a planning-only cache: the same
+ * bookkeeping with no GPU work (for tests and schedulers).  The cache object
+ * is host memory owned by the library until lora_cache_destroy; it creates
+ * HIP events (one per slot plus one) but no device memory.  Not thread-safe:
+ * one host thread at a time per cache. */
+typedef struct lora_cache lora_cache_t;
+lora_status_t lora_cache_create(lora_cache_t **cache, int32_t n_slots, const lora_pool_t *pools,
+                                int32_t n_pools, int32_t max_adapters);
+lora_status_t lora_cache_destroy(lora_cache_t *cache);
+
+/* Register (or replace) an adapter in the host tier: host_a[p], host_b[p]
+ * HOST pointers, one per pool, to lora_pack_host output of that pool's
+ * shapes (page-locked memory lets the copies run asynchronously); they must
+ * stay valid while the cache may copy from them.  rank <= max_rank
+ * (LORA_ERR_RANK_EXCEEDS_MAX), s = alpha / rank.  Re-registering a resident
+ * adapter drops its slot, so the next batch loads the new version. */
+lora_status_t lora_cache_register(lora_cache_t *cache, int32_t adapter, const void *const *host_a,
+                                  const void *const *host_b, int32_t rank, float alpha);
+
+/* Map a batch: adapters HOST [n] (adapter ids or -1) -> slots HOST [n] (slot
+ * of each id, -1 for -1), making every distinct adapter of the batch
+ * resident.  A miss takes an empty slot, else the least recently used slot
+ * the batch does not need.  The copy waits (on `copy`) for the victim slot's
+ * last use, then copies A, B, scale and rank; `compute` then waits for the
+ * copies, so kernels enqueued on `compute` after this call see the batch's
+ * adapters.  An unknown or unregistered id (LORA_ERR_INVALID_ARGUMENT) or
+ * more distinct adapters than slots (LORA_ERR_UNSUPPORTED; the per-step
+ * adapter limit of "Serving LoRA adapters ...", Step 2) changes nothing. */
+lora_status_t lora_cache_map(lora_cache_t *cache, const int32_t *adapters, int32_t n, int32_t *slots,
+                             lora_stream_t compute, lora_stream_t copy);
+
+/* After enqueuing the mapped batch's kernels on `compute`: record each of
+ * its slots' last use, which later evictions wait for. */
+lora_status_t lora_cache_commit(lora_cache_t *cache, lora_stream_t compute);
+
+/* Slot of an adapter (HOST out; -1 if not resident), and counters since
+ * creation: batch lookups that hit or missed, evictions, bytes copied. */
+lora_status_t lora_cache_slot_of(const lora_cache_t *cache, int32_t adapter, int32_t *slot);
+lora_status_t lora_cache_stats(const lora_cache_t *cache, int64_t *hits, int64_t *misses,
+                               int64_t *evictions, int64_t *bytes_uploaded);
+
 /* ---- errors ------------------------------------------------------------------- */
 
 /* Synchronise `stream`, read the workspace's error word into *first_bad_row

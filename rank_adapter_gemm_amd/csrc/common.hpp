@@ -96,6 +96,7 @@ constexpr int32_t kSegTile = 1024;     // rows per segment-builder tile
 constexpr int32_t kShrinkRows = 32;    // rows of one segment per grouped-shrink work block
 constexpr int32_t kMaxKSplit = 16;     // shrink k-split factor bound
 constexpr int32_t kMaxSlices = 4;      // pools sharing one shrink (projections that share x)
+constexpr int32_t kMaxCachePools = 8;  // pools (projections) one residency cache keeps in step
 constexpr int32_t kMaxSliceRanks = 128; // their summed max_rank
 constexpr int32_t kMaxSlots = 16000;   // slots per pool (LDS histogram bound, < 64 KiB)
 constexpr int32_t kErrNone = 0x7fffffff;
@@ -161,6 +162,7 @@ lora_status_t launch_pool_fill(void *a, size_t a_bytes, void *b, size_t b_bytes,
 lora_status_t launch_pool_upload(const lora_pool_t &p, int32_t slot, const void *A, int32_t lda,
                                  const void *B, int32_t ldb, int32_t r, float alpha, hipStream_t s);
 lora_status_t launch_pool_clear(const lora_pool_t &p, int32_t slot, hipStream_t s);
+lora_status_t launch_pool_meta(const lora_pool_t &p, int32_t slot, float scale, int32_t rank, hipStream_t s);
 lora_status_t launch_ws_init(void *ws, hipStream_t s);
 lora_status_t launch_segments(const int32_t *ids, int32_t T, int32_t n_slots, const ws_layout &L,
                               void *ws, hipStream_t s);

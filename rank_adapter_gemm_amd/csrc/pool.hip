@@ -95,6 +95,11 @@ lora_status_t launch_pool_upload(const lora_pool_t &p, int32_t slot, const void 
     return hip_status(hipGetLastError());
 }
 
+lora_status_t launch_pool_meta(const lora_pool_t &p, int32_t slot, float scale, int32_t rank, hipStream_t s) {
+    hipLaunchKernelGGL(k_set_meta, dim3(1), dim3(64), 0, s, p.scale, p.rank, slot, scale, rank);
+    return hip_status(hipGetLastError());
+}
+
 lora_status_t launch_pool_clear(const lora_pool_t &p, int32_t slot, hipStream_t s) {
     const size_t eb = p.dtype == LORA_F32 ? 4 : 2;
     const size_t a_bytes = (size_t)p.max_rank * p.d_in * eb, b_bytes = (size_t)p.max_rank * p.d_out * eb;

@@ -38,6 +38,8 @@ EXPORTED = (
     "lora_workspace_bytes", "lora_workspace_init", "lora_segments_view", "lora_build_segments",
     "lora_shrink", "lora_expand", "lora_gemm", "lora_gemm_expand", "lora_linear_forward",
     "lora_workspace_bytes_sliced", "lora_shrink_sliced", "lora_linear_forward_sliced",
+    "lora_pack_host", "lora_cache_create", "lora_cache_destroy", "lora_cache_register", "lora_cache_map",
+    "lora_cache_commit", "lora_cache_slot_of", "lora_cache_stats",
     "lora_get_device_error",
     "lora_status_string", "lora_version",
 )
@@ -109,6 +111,15 @@ def load(path: str = LIB_PATH):
         "lora_shrink_sliced": (c_i32, [c_vp, c_i32, P(lora_pool_t), c_i32, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
         "lora_linear_forward_sliced": (c_i32, [c_vp, P(c_vp), P(c_vp), c_i32, P(lora_pool_t), c_i32, c_vp,
                                                c_i32, c_u32, c_vp, c_sz, c_vp]),
+        "lora_pack_host": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_i32, c_i32, c_vp, c_vp]),
+        "lora_cache_create": (c_i32, [P(c_vp), c_i32, P(lora_pool_t), c_i32, c_i32]),
+        "lora_cache_destroy": (c_i32, [c_vp]),
+        "lora_cache_register": (c_i32, [c_vp, c_i32, P(c_vp), P(c_vp), c_i32, c_f]),
+        "lora_cache_map": (c_i32, [c_vp, P(c_i32), c_i32, P(c_i32), c_vp, c_vp]),
+        "lora_cache_commit": (c_i32, [c_vp, c_vp]),
+        "lora_cache_slot_of": (c_i32, [c_vp, c_i32, P(c_i32)]),
+        "lora_cache_stats": (c_i32, [c_vp, P(ctypes.c_int64), P(ctypes.c_int64), P(ctypes.c_int64),
+                                     P(ctypes.c_int64)]),
         "lora_get_device_error": (c_i32, [c_vp, c_sz, c_vp, P(c_i32)]),
         "lora_status_string": (ctypes.c_char_p, [c_i32]),
         "lora_version": (ctypes.c_char_p, []),
@@ -260,6 +271,67 @@ def lora_linear_forward_sliced(x, Ws, ys, T, pools, ids, mode, flags, ws, stream
     _ok(load().lora_linear_forward_sliced(_ptr(x), w_arr, y_arr, T, _pool_array(pools), n, _ptr(ids), mode,
                                           flags, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
         "lora_linear_forward_sliced")
+
+
+def lora_pack_host(d_in, d_out, max_rank, dtype, A, B, r, a_slot, b_slot):
+    """A [d_in, >= r], B [>= r, d_out] host tensors (row-major) -> a_slot, b_slot
+    host tensors of max_rank * d_in and max_rank * d_out elements."""
+    for t in (A, B, a_slot, b_slot):
+        assert t.device.type == "cpu" and t.is_contiguous()
+    _ok(load().lora_pack_host(d_in, d_out, max_rank, dtype, A.data_ptr(), A.shape[1], B.data_ptr(), B.shape[1],
+                              r, a_slot.data_ptr(), b_slot.data_ptr()), "lora_pack_host")
+
+
+class AdapterCache:
+    """The host tier + HBM slots residency cache (lora_cache_*).  pools: list
+    of lora_pool_t kept in step (empty list: planning only).  Host buffers
+    given to register() are kept alive here."""
+
+    def __init__(self, n_slots, pools, max_adapters):
+        self.n_pools = len(pools)
+        self._h = ctypes.c_void_p()
+        arr = _pool_array(pools) if pools else None
+        _ok(load().lora_cache_create(ctypes.byref(self._h), n_slots, arr, len(pools), max_adapters),
+            "lora_cache_create")
+        self._keep = {}
+
+    def register(self, adapter, host_a, host_b, rank, alpha):
+        n = self.n_pools
+        a_arr = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in host_a]) if n else None
+        b_arr = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in host_b]) if n else None
+        _ok(load().lora_cache_register(self._h, adapter, a_arr, b_arr, rank, alpha), "lora_cache_register")
+        self._keep[adapter] = (list(host_a), list(host_b))
+
+    def map(self, adapters, compute=None, copy=None):
+        n = len(adapters)
+        ids = (ctypes.c_int32 * max(n, 1))(*[int(a) for a in adapters])
+        out = (ctypes.c_int32 * max(n, 1))()
+        _ok(load().lora_cache_map(self._h, ids, n, out, _stream(compute), _stream(copy)), "lora_cache_map")
+        return [out[i] for i in range(n)]
+
+    def commit(self, compute=None):
+        _ok(load().lora_cache_commit(self._h, _stream(compute)), "lora_cache_commit")
+
+    def slot_of(self, adapter):
+        s = ctypes.c_int32()
+        _ok(load().lora_cache_slot_of(self._h, adapter, ctypes.byref(s)), "lora_cache_slot_of")
+        return s.value
+
+    def stats(self):
+        v = [ctypes.c_int64() for _ in range(4)]
+        _ok(load().lora_cache_stats(self._h, *[ctypes.byref(x) for x in v]), "lora_cache_stats")
+        return dict(zip(("hits", "misses", "evictions", "bytes"), [x.value for x in v]))
+
+    def close(self):
+        if self._h:
+            load().lora_cache_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def lora_get_device_error(ws, stream=None) -> int:
