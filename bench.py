@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--cold-sets", type=int, default=None, help="copies of the working set to rotate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU work of the oracle sample")
+    ap.add_argument("--residency", action="store_true",
+                    help="also measure the adapter cache's host-to-HBM promotion rate")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain fp32 copy kernel of known size (for counter scaling)")
     return ap.parse_args()
@@ -360,6 +362,8 @@ def main():
         torch.cuda.synchronize()
         print("calib-copy bytes_read=%d bytes_written=%d" % (a.numel() * 4, b.numel() * 4), file=sys.stderr)
 
+    residency = measure_residency(wl, pools, dev) if args.residency else None
+
     # ---- CPU baseline: the fp64 oracle on a bounded sample of this batch ----
     cpu = None
     if not args.no_cpu_baseline:
@@ -390,7 +394,61 @@ def main():
         "breakdown": breakdown,
         "cpu_baseline": cpu,
     }
+    if residency is not None:
+        line["residency"] = residency
     print(json.dumps(line), flush=True)
+
+
+def measure_residency(wl, pools, dev):
+    """Promotion rate of the adapter cache: 2 x Bn adapters packed in pinned
+    host memory, a cache of Bn slots over every projection's pool, and maps
+    that alternate between the two halves, so each map copies Bn adapters
+    into evicted slots.  Timed with events on the copy stream."""
+    import torch
+
+    from rank_adapter_gemm_amd import lora as L
+
+    R = wl.max_rank
+    per_adapter = sum(R * (p.d_in + p.d_out) * (4 if wl.dtype == torch.float32 else 2) for p in wl.projections)
+    bn = int(max(1, min(16, wl.n_slots // 2, (512 << 20) // (2 * per_adapter))))
+    cache = L.AdapterCache(bn, [pl.pool for pl in pools], 2 * bn)
+    code = L.dtype_code(wl.dtype)
+    keep = []
+    for a in range(2 * bn):
+        ha, hb = [], []
+        for pr in wl.projections:
+            A = (torch.randn(pr.d_in, R) * 0.02).to(wl.dtype)
+            B = (torch.randn(R, pr.d_out) * 0.02).to(wl.dtype)
+            sa = torch.empty(R * pr.d_in, dtype=wl.dtype).pin_memory()
+            sb = torch.empty(R * pr.d_out, dtype=wl.dtype).pin_memory()
+            L.lora_pack_host(pr.d_in, pr.d_out, R, code, A, B, R, sa, sb)
+            ha.append(sa)
+            hb.append(sb)
+        cache.register(a, ha, hb, R, 2.0 * R)
+        keep.append((ha, hb))
+    copy = torch.cuda.Stream()
+    compute = torch.cuda.current_stream()
+    halves = [list(range(bn)), list(range(bn, 2 * bn))]
+    for i in range(2):
+        cache.map(halves[i % 2], compute, copy)
+        cache.commit(compute)
+    torch.cuda.synchronize()
+    rounds = 8
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    b0 = cache.stats()["bytes"]
+    e0.record(copy)
+    for i in range(rounds):
+        cache.map(halves[i % 2], compute, copy)
+        cache.commit(compute)
+    e1.record(copy)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    moved = cache.stats()["bytes"] - b0
+    cache.close()
+    return {"h2d_gbs": round(moved / (ms * 1e-3) / 1e9, 2), "adapters_per_s": round(rounds * bn / (ms * 1e-3), 1),
+            "bytes_per_adapter": per_adapter, "adapters_per_map": bn, "maps": rounds,
+            "host_memory": "pinned, slot layout"}
 
 
 def stored_traffic(kernel: str, workload: str, projection: str | None = None):

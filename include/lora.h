@@ -288,9 +288,10 @@ lora_status_t lora_pack_host(int32_t d_in, int32_t d_out, int32_t max_rank, lora
                              const void *A, int32_t lda, const void *B, int32_t ldb, int32_t r,
                              void *a_slot, void *b_slot);
 
-/* A residency cache over n_slots slots of n_pools pools (the projections of
- * one layer set, kept in step: slot s holds the same adapter in every pool;
- * all pools have n_slots slots, one max_rank and one dtype) for adapter ids
+/* A residency cache over slots 0..n_slots-1 of n_pools pools (the projections
+ * of one layer set, kept in step: slot s holds the same adapter in every pool;
+ * every pool has at least n_slots slots, and all share one max_rank and one
+ * dtype) for adapter ids
  * 0..max_adapters-1.  n_pools == 0 gives a planning-only cache: the same
  * bookkeeping with no GPU work (for tests and schedulers).  The cache object
  * is host memory owned by the library until lora_cache_destroy; it creates

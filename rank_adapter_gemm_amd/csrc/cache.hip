@@ -91,7 +91,7 @@ lora_status_t lora_cache_create(lora_cache_t **out, int32_t n_slots, const lora_
     if (n_pools > lora::kMaxCachePools) return LORA_ERR_UNSUPPORTED;
     for (int32_t p = 0; p < n_pools; ++p) {
         const lora_pool_t &q = pools[p];
-        if (q.n_slots != n_slots || !q.a || !q.b || !q.scale || !q.rank || q.max_rank < 8 ||
+        if (q.n_slots < n_slots || !q.a || !q.b || !q.scale || !q.rank || q.max_rank < 8 ||
             q.max_rank > 128 || q.max_rank != pools[0].max_rank || q.dtype != pools[0].dtype)
             return LORA_ERR_INVALID_ARGUMENT;
     }
@@ -210,23 +210,42 @@ lora_status_t lora_cache_map(lora_cache_t *c, const int32_t *adapters, int32_t n
     for (int32_t i = 0; i < n; ++i) slots[i] = adapters[i] == -1 ? -1 : c->slot_of[adapters[i]];
     if (c->n_pools == 0 || uploads.empty()) return LORA_OK;
 
-    // device side: wait for each victim's last use, copy, then publish
+    // device side: wait for the victims' last uses, then every copy (one
+    // run of DMA work), then one kernel per kMetaBatch slots that publishes
+    // scale and rank in all pools
     const hipStream_t cs = hs(copy), ks = hs(compute);
     const size_t eb = c->pools[0].dtype == LORA_F32 ? 4 : 2;
+    for (const auto &u : uploads)
+        if (c->used[u.first] && hipStreamWaitEvent(cs, c->last_use[u.first], 0) != hipSuccess)
+            return LORA_ERR_HIP;
     for (const auto &u : uploads) {
         const int32_t s = u.first;
         const lora_cache::adapter &ad = c->adapters[u.second];
-        if (c->used[s] && hipStreamWaitEvent(cs, c->last_use[s], 0) != hipSuccess) return LORA_ERR_HIP;
         for (int32_t p = 0; p < c->n_pools; ++p) {
             const lora_pool_t &q = c->pools[p];
             const size_t ab = (size_t)q.max_rank * q.d_in * eb, bb = (size_t)q.max_rank * q.d_out * eb;
             if (hipMemcpyAsync((char *)q.a + (size_t)s * ab, ad.a[p], ab, hipMemcpyHostToDevice, cs) != hipSuccess ||
                 hipMemcpyAsync((char *)q.b + (size_t)s * bb, ad.b[p], bb, hipMemcpyHostToDevice, cs) != hipSuccess)
                 return LORA_ERR_HIP;
-            lora_status_t st = lora::launch_pool_meta(q, s, ad.alpha / (float)ad.rank, ad.rank, cs);
-            if (st != LORA_OK) return st;
             c->bytes += (int64_t)(ab + bb);
         }
+    }
+    for (size_t i0 = 0; i0 < uploads.size(); i0 += lora::kMetaBatch) {
+        lora::meta_batch m;
+        m.n_pools = c->n_pools;
+        for (int32_t p = 0; p < lora::kMaxCachePools; ++p) {
+            m.scale[p] = p < c->n_pools ? c->pools[p].scale : nullptr;
+            m.rank[p] = p < c->n_pools ? c->pools[p].rank : nullptr;
+        }
+        m.n = 0;
+        for (size_t i = i0; i < uploads.size() && m.n < lora::kMetaBatch; ++i, ++m.n) {
+            const lora_cache::adapter &ad = c->adapters[uploads[i].second];
+            m.slot[m.n] = uploads[i].first;
+            m.s[m.n] = ad.alpha / (float)ad.rank;
+            m.r[m.n] = ad.rank;
+        }
+        lora_status_t st = lora::launch_pool_meta_batch(m, cs);
+        if (st != LORA_OK) return st;
     }
     if (hipEventRecord(c->ready, cs) != hipSuccess || hipStreamWaitEvent(ks, c->ready, 0) != hipSuccess)
         return LORA_ERR_HIP;

@@ -163,6 +163,17 @@ lora_status_t launch_pool_upload(const lora_pool_t &p, int32_t slot, const void 
                                  const void *B, int32_t ldb, int32_t r, float alpha, hipStream_t s);
 lora_status_t launch_pool_clear(const lora_pool_t &p, int32_t slot, hipStream_t s);
 lora_status_t launch_pool_meta(const lora_pool_t &p, int32_t slot, float scale, int32_t rank, hipStream_t s);
+// Scale and rank of up to kMetaBatch slots, written in every pool by one launch.
+constexpr int32_t kMetaBatch = 64;
+struct meta_batch {
+    float *scale[kMaxCachePools];
+    int32_t *rank[kMaxCachePools];
+    int32_t n_pools, n;
+    int32_t slot[kMetaBatch];
+    float s[kMetaBatch];
+    int32_t r[kMetaBatch];
+};
+lora_status_t launch_pool_meta_batch(const meta_batch &m, hipStream_t s);
 lora_status_t launch_ws_init(void *ws, hipStream_t s);
 lora_status_t launch_segments(const int32_t *ids, int32_t T, int32_t n_slots, const ws_layout &L,
                               void *ws, hipStream_t s);

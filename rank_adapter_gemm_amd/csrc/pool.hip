@@ -95,6 +95,20 @@ lora_status_t launch_pool_upload(const lora_pool_t &p, int32_t slot, const void 
     return hip_status(hipGetLastError());
 }
 
+__global__ void k_set_meta_batch(meta_batch m) {
+    const int i = threadIdx.x;
+    if (i < m.n)
+        for (int p = 0; p < m.n_pools; ++p) {
+            m.scale[p][m.slot[i]] = m.s[i];
+            m.rank[p][m.slot[i]] = m.r[i];
+        }
+}
+
+lora_status_t launch_pool_meta_batch(const meta_batch &m, hipStream_t s) {
+    hipLaunchKernelGGL(k_set_meta_batch, dim3(1), dim3(kMetaBatch), 0, s, m);
+    return hip_status(hipGetLastError());
+}
+
 lora_status_t launch_pool_meta(const lora_pool_t &p, int32_t slot, float scale, int32_t rank, hipStream_t s) {
     hipLaunchKernelGGL(k_set_meta, dim3(1), dim3(64), 0, s, p.scale, p.rank, slot, scale, rank);
     return hip_status(hipGetLastError());
