@@ -192,31 +192,33 @@ __device__ __forceinline__ void lora_pass_impl(const gemm_args &g, f32x16_t (&ac
     }
 }
 
-template <int BM, int BN, int BK, int NS, bool SH> struct gemm_cfg {
-    static constexpr int WM = BM / 2, WN = BN / 2;          // per-wavefront tile
+template <int BM, int BN, int BK, int NS, bool SH, int WV = 4> struct gemm_cfg {
+    // WV wavefronts in a 2 x (WV/2) grid; each owns a WM x WN tile
+    static constexpr int WM = BM / 2, WN = BN / (WV / 2);   // per-wavefront tile
     static constexpr int RB = WM / 32, CB = WN / 32;        // 32x32 MFMA blocks per wavefront
     static constexpr int XCH = BK / 8, WCH = BN / 8;        // 16-byte chunks per LDS row
     static constexpr int XSTAGE = BM * BK, WSTAGE = BK * BN;
     // fused shrink: per stage, 64/R rows x R ranks x BK k of A^T (8 BK chunks)
     static constexpr int ACH = BK / 8, ASTAGE = SH ? 64 * BK : 0;
     static constexpr int STAGE = XSTAGE + WSTAGE + ASTAGE;  // uint16 elements per ring stage
-    static constexpr int XI = BM * XCH / 256, WI = BK * WCH / 256;   // DMA instructions per wave
+    static constexpr int XI = BM * XCH / (64 * WV), WI = BK * WCH / (64 * WV);   // DMA instructions per wave
     static constexpr int AI = SH ? BK / 32 : 0;
     static constexpr int SLD = WN + 4;                      // epilogue staging row stride (floats)
-    static constexpr int EPI = 4 * 32 * SLD * 4;             // epilogue LDS bytes
+    static constexpr int EPI = WV * 32 * SLD * 4;            // epilogue LDS bytes
     static constexpr int LDS = NS * STAGE * 2 > EPI ? NS * STAGE * 2 : EPI;
 };
 
-template <bool LORA, int BM, int BN, int BK, int NS, bool SPLIT, bool SH = false>
-__global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
+template <bool LORA, int BM, int BN, int BK, int NS, bool SPLIT, bool SH = false, int WV = 4>
+__global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
     static_assert(!SH || SPLIT, "the fused shrink runs in split-K mode");
-    typedef gemm_cfg<BM, BN, BK, NS, SH> C;
+    static_assert(!SH || WV == 4, "the fused shrink maps 256 threads");
+    typedef gemm_cfg<BM, BN, BK, NS, SH, WV> C;
     constexpr int WM = C::WM, WN = C::WN, RB = C::RB, CB = C::CB;
     constexpr int XCH = C::XCH, WCH = C::WCH, XSTAGE = C::XSTAGE, WSTAGE = C::WSTAGE;
     constexpr int XI = C::XI, WI = C::WI, AI = C::AI, ACH = C::ACH, STAGE = C::STAGE;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[C::LDS / 2];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = w / (WV / 2), wn = w % (WV / 2);
     int tm, tn, split, tidx;
     tile_of(blockIdx.x, gridDim.x, g, tm, tn, split, tidx);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -351,7 +353,7 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(gemm_args g) {
 
     // Per-row metadata of the tile (token row; usable adapter slot or -1).
     __shared__ int32_t s_meta_t[BM], s_meta_id[BM];
-    for (int i = tid; i < BM; i += 256) {
+    for (int i = tid; i < BM; i += WV * 64) {
         const int p = m0 + i;
         const int32_t t = (p < T) ? perm_row(g.perm, p, T) : -1;
         int32_t id = -1;
@@ -722,7 +724,7 @@ static gemm_plan plan_gemm(int T, int K, int N, size_t partial_bytes) {
     return {bm, bn, 0, tiles, ceil_div(K, k_chunk), k_chunk};
 }
 
-template <int BM, int BN, int NS = 2>
+template <int BM, int BN, int NS = 2, int WV = 4>
 static void launch_cfg(gemm_args g, const gemm_plan &pl, bool lora, hipStream_t s) {
     constexpr int BK = 64;
     if (pl.n_dp > 0) {
@@ -731,17 +733,19 @@ static void launch_cfg(gemm_args g, const gemm_plan &pl, bool lora, hipStream_t 
         g.splits = 1;
         g.k_chunk = g.K;
         if (lora)
-            hipLaunchKernelGGL((k_gemm_bf16<true, BM, BN, BK, NS, false>), dim3(pl.n_dp), dim3(256), 0, s, g);
+            hipLaunchKernelGGL((k_gemm_bf16<true, BM, BN, BK, NS, false, false, WV>), dim3(pl.n_dp), dim3(WV * 64),
+                               0, s, g);
         else
-            hipLaunchKernelGGL((k_gemm_bf16<false, BM, BN, BK, NS, false>), dim3(pl.n_dp), dim3(256), 0, s, g);
+            hipLaunchKernelGGL((k_gemm_bf16<false, BM, BN, BK, NS, false, false, WV>), dim3(pl.n_dp), dim3(WV * 64),
+                               0, s, g);
     }
     if (pl.tail > 0) {
         g.tile_base = pl.n_dp;
         g.n_tiles = pl.tail;
         g.splits = pl.splits;
         g.k_chunk = pl.k_chunk;
-        hipLaunchKernelGGL((k_gemm_bf16<false, BM, BN, BK, NS, true>), dim3(pl.tail * pl.splits), dim3(256),
-                           0, s, g);
+        hipLaunchKernelGGL((k_gemm_bf16<false, BM, BN, BK, NS, true, false, WV>), dim3(pl.tail * pl.splits),
+                           dim3(WV * 64), 0, s, g);
         const dim3 rgrid(pl.tail * (BM / (2048 / BN)));
         if (lora)
             hipLaunchKernelGGL((k_splitk_reduce<true, false, BM, BN>), rgrid, dim3(256), 0, s, g);
@@ -829,8 +833,10 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
         g.vpart = nullptr;
         g.err = nullptr;
         const bool lora = pool != nullptr;
-        if (pl.bm == 256 && pl.bn == 256) launch_cfg<256, 256>(g, pl, lora, s);
-        else if (pl.bm == 256 && pl.bn == 128) launch_cfg<256, 128>(g, pl, lora, s);
+        // 256-row tiles run 8 wavefronts (two per SIMD: one issues MFMAs while
+        // the other waits on LDS or the barrier); smaller tiles 4.
+        if (pl.bm == 256 && pl.bn == 256) launch_cfg<256, 256, 2, 8>(g, pl, lora, s);
+        else if (pl.bm == 256 && pl.bn == 128) launch_cfg<256, 128, 2, 8>(g, pl, lora, s);
         else if (pl.bm == 256) launch_cfg<256, 64, 3>(g, pl, lora, s);
         else if (pl.bn == 128) launch_cfg<128, 128>(g, pl, lora, s);
         else launch_cfg<128, 64>(g, pl, lora, s);
