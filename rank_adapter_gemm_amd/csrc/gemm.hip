@@ -192,9 +192,9 @@ __device__ __forceinline__ void lora_pass_impl(const gemm_args &g, f32x16_t (&ac
     }
 }
 
-template <int BM, int BN, int BK, int NS, bool SH, int WV = 4> struct gemm_cfg {
-    // WV wavefronts in a 2 x (WV/2) grid; each owns a WM x WN tile
-    static constexpr int WM = BM / 2, WN = BN / (WV / 2);   // per-wavefront tile
+template <int BM, int BN, int BK, int NS, bool SH, int WV = 4, int WR = 2> struct gemm_cfg {
+    // WV wavefronts in a WR x (WV/WR) grid; each owns a WM x WN tile
+    static constexpr int WM = BM / WR, WN = BN / (WV / WR); // per-wavefront tile
     static constexpr int RB = WM / 32, CB = WN / 32;        // 32x32 MFMA blocks per wavefront
     static constexpr int XCH = BK / 8, WCH = BN / 8;        // 16-byte chunks per LDS row
     static constexpr int XSTAGE = BM * BK, WSTAGE = BK * BN;
@@ -208,17 +208,17 @@ template <int BM, int BN, int BK, int NS, bool SH, int WV = 4> struct gemm_cfg {
     static constexpr int LDS = NS * STAGE * 2 > EPI ? NS * STAGE * 2 : EPI;
 };
 
-template <bool LORA, int BM, int BN, int BK, int NS, bool SPLIT, bool SH = false, int WV = 4>
+template <bool LORA, int BM, int BN, int BK, int NS, bool SPLIT, bool SH = false, int WV = 4, int WR = 2>
 __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
     static_assert(!SH || SPLIT, "the fused shrink runs in split-K mode");
     static_assert(!SH || WV == 4, "the fused shrink maps 256 threads");
-    typedef gemm_cfg<BM, BN, BK, NS, SH, WV> C;
+    typedef gemm_cfg<BM, BN, BK, NS, SH, WV, WR> C;
     constexpr int WM = C::WM, WN = C::WN, RB = C::RB, CB = C::CB;
     constexpr int XCH = C::XCH, WCH = C::WCH, XSTAGE = C::XSTAGE, WSTAGE = C::WSTAGE;
     constexpr int XI = C::XI, WI = C::WI, AI = C::AI, ACH = C::ACH, STAGE = C::STAGE;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[C::LDS / 2];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w / (WV / 2), wn = w % (WV / 2);
+    const int wm = w / (WV / WR), wn = w % (WV / WR);
     int tm, tn, split, tidx;
     tile_of(blockIdx.x, gridDim.x, g, tm, tn, split, tidx);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -724,19 +724,18 @@ static gemm_plan plan_gemm(int T, int K, int N, size_t partial_bytes) {
     return {bm, bn, 0, tiles, ceil_div(K, k_chunk), k_chunk};
 }
 
-template <int BM, int BN, int NS = 2, int WV = 4>
+template <int BM, int BN, int NS = 2, int WV = 4, int WR = 2, int BK = 64>
 static void launch_cfg(gemm_args g, const gemm_plan &pl, bool lora, hipStream_t s) {
-    constexpr int BK = 64;
     if (pl.n_dp > 0) {
         g.tile_base = 0;
         g.n_tiles = pl.n_dp;
         g.splits = 1;
         g.k_chunk = g.K;
         if (lora)
-            hipLaunchKernelGGL((k_gemm_bf16<true, BM, BN, BK, NS, false, false, WV>), dim3(pl.n_dp), dim3(WV * 64),
+            hipLaunchKernelGGL((k_gemm_bf16<true, BM, BN, BK, NS, false, false, WV, WR>), dim3(pl.n_dp), dim3(WV * 64),
                                0, s, g);
         else
-            hipLaunchKernelGGL((k_gemm_bf16<false, BM, BN, BK, NS, false, false, WV>), dim3(pl.n_dp), dim3(WV * 64),
+            hipLaunchKernelGGL((k_gemm_bf16<false, BM, BN, BK, NS, false, false, WV, WR>), dim3(pl.n_dp), dim3(WV * 64),
                                0, s, g);
     }
     if (pl.tail > 0) {
@@ -744,7 +743,7 @@ static void launch_cfg(gemm_args g, const gemm_plan &pl, bool lora, hipStream_t 
         g.n_tiles = pl.tail;
         g.splits = pl.splits;
         g.k_chunk = pl.k_chunk;
-        hipLaunchKernelGGL((k_gemm_bf16<false, BM, BN, BK, NS, true, false, WV>), dim3(pl.tail * pl.splits),
+        hipLaunchKernelGGL((k_gemm_bf16<false, BM, BN, BK, NS, true, false, WV, WR>), dim3(pl.tail * pl.splits),
                            dim3(WV * 64), 0, s, g);
         const dim3 rgrid(pl.tail * (BM / (2048 / BN)));
         if (lora)
