@@ -333,6 +333,61 @@ lora_status_t lora_cache_slot_of(const lora_cache_t *cache, int32_t adapter, int
 lora_status_t lora_cache_stats(const lora_cache_t *cache, int64_t *hits, int64_t *misses,
                                int64_t *evictions, int64_t *bytes_uploaded);
 
+/* ---- FP8 base weight with a bf16 adapter ----------------------------------- */
+
+/* A quantized base weight with a half-precision adapter is a common serving
+ * mix, and the adapter's contribution belongs in the base product's
+ * accumulator, never merged into the packed 8-bit weight ("Multi-LoRA
+ * Serving 与 Adapter 隔离", section on numerics and mixed precision).  The
+ * pages fix no scheme; this library uses OCP E4M3 codes (largest finite 448,
+ * subnormals, 0x7f / 0xff NaN) with one fp32 scale per token row of x and one
+ * per output column of W:
+ *     scale = amax / 448,  code = E4M3(clamp(v * (448 / amax), -448, 448))
+ * with correctly rounded fp32 division and product and round-to-nearest-even
+ * conversion; an all-zero row or column gets scale 0 and zero codes.  Inputs
+ * must be finite.  The layer is
+ *     y[t,n] = s_x[t] s_w[n] sum_k dq(xq[t,k]) dq(wq[n,k]) + s_a ((x A_a) B_a)[n]
+ * with the low-rank term from the bf16 x, fp32 accumulation and one rounding
+ * of y to bf16.  The FP8 products are exact; the matrix cores add each block
+ * of 64 of them with an error below about 2^-12 of the block's largest
+ * product, so results are not bitwise equal to an fp32 sum of the products.
+ * For all of these: d_in a positive multiple of 16, d_out of 8. */
+
+/* Codes and scales of DEVICE x bf16 [T, d]: xq DEVICE uint8 [T, d],
+ * x_scale DEVICE fp32 [T]. */
+lora_status_t lora_quantize_rows_fp8(const void *x, int32_t T, int32_t d, uint8_t *xq, float *x_scale,
+                                     lora_stream_t stream);
+
+/* Codes and scales of a base weight, once at load: W DEVICE bf16
+ * [d_in, d_out] -> wq DEVICE uint8 [d_out, d_in] (row n holds column n of W,
+ * K-contiguous), w_scale DEVICE fp32 [d_out]. */
+lora_status_t lora_quantize_weight_fp8(const void *W, int32_t d_in, int32_t d_out, uint8_t *wq,
+                                       float *w_scale, lora_stream_t stream);
+
+/* Base product only: y = s_x s_w (xq wq^T), y DEVICE bf16 [T, d_out].  ws
+ * (DEVICE, may be NULL) as for lora_gemm. */
+lora_status_t lora_gemm_fp8(const uint8_t *xq, const float *x_scale, const uint8_t *wq,
+                            const float *w_scale, void *y, int32_t T, int32_t d_in, int32_t d_out,
+                            void *ws, size_t ws_bytes, lora_stream_t stream);
+
+/* Workspace of lora_linear_forward_fp8: that of lora_workspace_bytes plus
+ * the quantized rows of x (T * d_in bytes and T scales).  0 on bad
+ * arguments. */
+size_t lora_workspace_bytes_fp8(int32_t T, int32_t n_slots, int32_t max_rank, int32_t d_in,
+                                int32_t d_out);
+
+/* The whole layer on an FP8 base weight: quantizes x into `ws`, computes the
+ * shrink from the bf16 x, then the FP8 GEMM with the expand in its epilogue
+ * (or, with LORA_FLAG_SEPARATE_EXPAND, as its own pass).  x DEVICE bf16
+ * [T, d_in], wq / w_scale from lora_quantize_weight_fp8, y DEVICE bf16
+ * [T, d_out], pool bf16 with pool->d_in == d_in and pool->d_out == d_out;
+ * mode and flags as for lora_linear_forward.  ws sized by
+ * lora_workspace_bytes_fp8. */
+lora_status_t lora_linear_forward_fp8(const void *x, const uint8_t *wq, const float *w_scale, void *y,
+                                      int32_t T, const lora_pool_t *pool, const int32_t *ids,
+                                      lora_mode_t mode, uint32_t flags, void *ws, size_t ws_bytes,
+                                      lora_stream_t stream);
+
 /* ---- errors ------------------------------------------------------------------- */
 
 /* Synchronise `stream`, read the workspace's error word into *first_bad_row

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "liblora.so")
-SOURCES = ["api.hip", "pool.hip", "segments.hip", "shrink.hip", "expand.hip", "gemm.hip", "cache.hip"]
+SOURCES = ["api.hip", "pool.hip", "segments.hip", "shrink.hip", "expand.hip", "gemm.hip", "gemm_fp8.hip", "cache.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.

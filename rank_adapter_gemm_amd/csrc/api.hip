@@ -33,6 +33,14 @@ inline lora_status_t check_ws(const void *ws, size_t ws_bytes, int32_t T, int32_
     return LORA_OK;
 }
 
+inline lora_status_t check_ws_fp8(const void *ws, size_t ws_bytes, int32_t T, int32_t n_slots,
+                                  int32_t max_rank, int32_t d_in, ws_layout *L) {
+    if (!ws || !aligned16(ws)) return LORA_ERR_INVALID_ARGUMENT;
+    *L = make_ws_layout(T, n_slots, max_rank, 0, d_in);
+    if (ws_bytes < L->total) return LORA_ERR_WORKSPACE_TOO_SMALL;
+    return LORA_OK;
+}
+
 inline bool use_sgmv(lora_mode_t mode, int32_t T) {
     if (mode == LORA_MODE_SGMV) return true;
     if (mode == LORA_MODE_BGMV) return false;
@@ -337,6 +345,80 @@ lora_status_t lora_linear_forward_sliced(const void *x, const void *const *W, vo
         if (st != LORA_OK) return st;
     }
     return LORA_OK;
+}
+
+lora_status_t lora_quantize_rows_fp8(const void *x, int32_t T, int32_t d, uint8_t *xq, float *x_scale,
+                                     lora_stream_t stream) {
+    if (T < 0 || d <= 0 || (d % 16)) return LORA_ERR_INVALID_ARGUMENT;
+    if (T > 0 && (!x || !xq || !x_scale || !aligned16(x) || !aligned16(xq) || !aligned16(x_scale)))
+        return LORA_ERR_INVALID_ARGUMENT;
+    return launch_quant_rows_fp8(x, T, d, xq, x_scale, hs(stream));
+}
+
+lora_status_t lora_quantize_weight_fp8(const void *W, int32_t d_in, int32_t d_out, uint8_t *wq,
+                                       float *w_scale, lora_stream_t stream) {
+    if (d_in <= 0 || d_out <= 0 || (d_in % 16) || (d_out % 8)) return LORA_ERR_INVALID_ARGUMENT;
+    if (!W || !wq || !w_scale || !aligned16(W) || !aligned16(wq) || !aligned16(w_scale))
+        return LORA_ERR_INVALID_ARGUMENT;
+    return launch_quant_cols_fp8(W, d_in, d_out, wq, w_scale, hs(stream));
+}
+
+lora_status_t lora_gemm_fp8(const uint8_t *xq, const float *x_scale, const uint8_t *wq,
+                            const float *w_scale, void *y, int32_t T, int32_t d_in, int32_t d_out,
+                            void *ws, size_t ws_bytes, lora_stream_t stream) {
+    if (T < 0 || d_in <= 0 || d_out <= 0 || (d_in % 16) || (d_out % 8)) return LORA_ERR_INVALID_ARGUMENT;
+    if (T > 0 && (!xq || !x_scale || !wq || !w_scale || !y || !aligned16(xq) || !aligned16(wq) ||
+                  !aligned16(w_scale) || !aligned16(y)))
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (ws && !aligned16(ws)) return LORA_ERR_INVALID_ARGUMENT;
+    if (T == 0) return LORA_OK;
+    return launch_gemm_fp8(xq, x_scale, wq, w_scale, y, T, d_in, d_out, nullptr, nullptr, nullptr, 0, nullptr,
+                           ws ? static_cast<float *>(ws) : nullptr, ws ? ws_bytes : 0, hs(stream));
+}
+
+size_t lora_workspace_bytes_fp8(int32_t T, int32_t n_slots, int32_t max_rank, int32_t d_in, int32_t d_out) {
+    if (lora_workspace_bytes(T, n_slots, max_rank, d_out) == 0 || d_in <= 0 || (d_in % 16)) return 0;
+    return make_ws_layout(T, n_slots, max_rank, d_out, d_in).total;
+}
+
+lora_status_t lora_linear_forward_fp8(const void *x, const uint8_t *wq, const float *w_scale, void *y,
+                                      int32_t T, const lora_pool_t *pool, const int32_t *ids,
+                                      lora_mode_t mode, uint32_t flags, void *ws, size_t ws_bytes,
+                                      lora_stream_t stream) {
+    if (!valid_pool(pool) || pool->dtype != LORA_BF16 || (pool->d_in % 16) || T < 0 || !valid_mode(mode) ||
+        (flags & ~3u))
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (T > 0 && (!x || !wq || !w_scale || !y || !ids || !aligned16(x) || !aligned16(wq) ||
+                  !aligned16(w_scale) || !aligned16(y)))
+        return LORA_ERR_INVALID_ARGUMENT;
+    ws_layout L;
+    lora_status_t st = check_ws_fp8(ws, ws_bytes, T, pool->n_slots, pool->max_rank, pool->d_in, &L);
+    if (st != LORA_OK) return st;
+    if (T == 0) return LORA_OK;
+    const hipStream_t s = hs(stream);
+    const bool sgmv = use_sgmv(mode, T);
+    if (sgmv && !(flags & LORA_FLAG_SEGMENTS_READY)) {
+        st = launch_segments(ids, T, pool->n_slots, L, ws, s);
+        if (st != LORA_OK) return st;
+    }
+    uint8_t *xq = ws_ptr<uint8_t>(ws, L.xq);
+    float *xs = ws_ptr<float>(ws, L.xs);
+    st = launch_quant_rows_fp8(x, T, pool->d_in, xq, xs, s);
+    if (st != LORA_OK) return st;
+    float *v = ws_ptr<float>(ws, L.v);
+    st = launch_shrink(x, T, pool, 1, ids, sgmv, v, L, ws, s);
+    if (st != LORA_OK) return st;
+    const int32_t *perm = sgmv ? ws_ptr<int32_t>(ws, L.perm) : nullptr;
+    float *partial = ws_ptr<float>(ws, L.gemm_partial);
+    const size_t partial_bytes = ws_bytes - L.gemm_partial;
+    if (flags & LORA_FLAG_SEPARATE_EXPAND) {
+        st = launch_gemm_fp8(xq, xs, wq, w_scale, y, T, pool->d_in, pool->d_out, nullptr, nullptr, nullptr, 0,
+                             nullptr, partial, partial_bytes, s);
+        if (st != LORA_OK) return st;
+        return launch_expand(v, pool->max_rank, T, *pool, ids, sgmv, y, L, ws, s);
+    }
+    return launch_gemm_fp8(xq, xs, wq, w_scale, y, T, pool->d_in, pool->d_out, pool, ids, v, pool->max_rank,
+                           perm, partial, partial_bytes, s);
 }
 
 lora_status_t lora_get_device_error(void *ws, size_t ws_bytes, lora_stream_t stream,

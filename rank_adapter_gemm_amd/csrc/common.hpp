@@ -118,13 +118,17 @@ struct ws_layout {
     size_t tile_hist;   // int32[(n_slots + 1) * n_tiles]
     size_t v;           // fp32[T * max_rank]
     size_t partial;     // fp32[kMaxKSplit * T * max_rank]
+    size_t xq;          // FP8 base only: E4M3 codes of x, uint8[T * d_in]
+    size_t xs;          // FP8 base only: row scales, fp32[T]
     size_t gemm_partial;  // split-K GEMM partials (fp32 tiles), may be empty
     size_t total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-inline ws_layout make_ws_layout(int32_t T, int32_t n_slots, int32_t max_rank, int32_t d_out) {
+// q8_d_in > 0 adds the regions of the FP8-base forward (quantized x rows).
+inline ws_layout make_ws_layout(int32_t T, int32_t n_slots, int32_t max_rank, int32_t d_out,
+                                int32_t q8_d_in = 0) {
     ws_layout L;
     size_t o = 0;
     const size_t t = (size_t)(T > 0 ? T : 1);
@@ -140,6 +144,9 @@ inline ws_layout make_ws_layout(int32_t T, int32_t n_slots, int32_t max_rank, in
     L.tile_hist = o; o = align256(o + 4 * (size_t)(n_slots + 1) * n_tiles);
     L.v = o;         o = align256(o + 4 * t * (size_t)max_rank);
     L.partial = o;   o = align256(o + 4 * (size_t)kMaxKSplit * t * (size_t)max_rank);
+    const size_t tq = q8_d_in > 0 ? t : 0;
+    L.xq = o;        o = align256(o + tq * (size_t)(q8_d_in > 0 ? q8_d_in : 0));
+    L.xs = o;        o = align256(o + 4 * tq);
     L.gemm_partial = o;
     if (d_out > 0 && T > 0) {
         const size_t tp = (t + 255) / 256 * 256, np = ((size_t)d_out + 255) / 256 * 256;
@@ -196,5 +203,13 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
                           int32_t d_out, int32_t dtype, const lora_pool_t *pool,
                           const int32_t *ids, const float *v, int32_t v_stride,
                           const int32_t *perm, float *partial, size_t partial_bytes, hipStream_t s);
+// FP8 base (E4M3 codes, fp32 scales): per-row and per-column quantizers and
+// y = s_x s_w (xq wq^T) (+ s v B when pool != nullptr), bf16 y.
+lora_status_t launch_quant_rows_fp8(const void *x, int32_t T, int32_t K, uint8_t *xq, float *xs, hipStream_t s);
+lora_status_t launch_quant_cols_fp8(const void *W, int32_t K, int32_t N, uint8_t *wq, float *wsc, hipStream_t s);
+lora_status_t launch_gemm_fp8(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *wsc, void *y,
+                              int32_t T, int32_t d_in, int32_t d_out, const lora_pool_t *pool,
+                              const int32_t *ids, const float *v, int32_t v_stride, const int32_t *perm,
+                              float *partial, size_t partial_bytes, hipStream_t s);
 
 }  // namespace lora

@@ -23,174 +23,9 @@
 //   * Split-K (small grids): each workgroup sums a K range and writes fp32
 //     partials in sorted-row order; k_splitk_reduce adds them in split order
 //     (deterministic, no atomics) and applies the same epilogue.
-#include "common.hpp"
+#include "gemm_common.hpp"
 
 namespace lora {
-
-struct gemm_args {
-    const uint16_t *x;
-    const uint16_t *W;
-    uint16_t *y;
-    int32_t T, K, N;
-    const int32_t *perm;
-    const uint16_t *b;
-    const float *scale;
-    const int32_t *rank;
-    int32_t n_slots, max_rank;
-    const int32_t *ids;
-    const float *v;                // [T][v_stride] fp32, this pool's ranks at columns 0..max_rank-1
-    int32_t v_stride;
-    int32_t n_tiles_m, n_tiles_n;
-    int32_t tile_base, n_tiles;    // this launch: tiles [tile_base, tile_base + n_tiles) in tile order
-    int32_t splits, k_chunk;       // split-K: number of K ranges and their length
-    float *partial;                // split-K: fp32 [n_tiles][splits][BM][BN] (tile-major)
-    const uint16_t *a;             // fused shrink: the pool's A^T [n_slots][max_rank][K]
-    float *vpart;                  // fused shrink: fp32 [splits][T][max_rank] rank partials
-    int32_t *err;                  // fused shrink: the workspace error word
-};
-
-// Tile order: workgroups are dispatched round-robin over the 8 XCDs (each
-// with its own L2), so workgroup b runs on XCD b % 8.  Give each XCD a
-// contiguous range of work items, walked in groups of GROUP_M row tiles (down
-// M first, then across N) so the tiles resident on one XCD share x rows and W
-// columns in its L2.  With split-K the split index varies slowest.
-constexpr int kXcds = 8, kGroupM = 8;
-
-__device__ __forceinline__ void grouped_tile(int v, int n_tiles_m, int n_tiles_n, int &tm, int &tn) {
-    const int per_group = kGroupM * n_tiles_n;
-    const int grp = v / per_group;
-    const int first_m = grp * kGroupM;
-    const int gm = min(kGroupM, n_tiles_m - first_m);
-    const int in = v - grp * per_group;
-    tm = first_m + in % gm;
-    tn = in / gm;
-}
-
-// Work item of workgroup b in a launch of `total` workgroups covering
-// n_tiles tiles (from tile_base, in tile order) times the split count.
-// Returns the tile (tm, tn), the split, and the launch-local tile index.
-__device__ __forceinline__ void tile_of(int b, int total, const gemm_args &g, int &tm, int &tn,
-                                        int &split, int &tidx) {
-    const int q = total / kXcds, r = total % kXcds;
-    const int x = b % kXcds, slot = b / kXcds;
-    int v = x * q + min(x, r) + slot;
-    split = v / g.n_tiles;
-    tidx = v - split * g.n_tiles;
-    grouped_tile(g.tile_base + tidx, g.n_tiles_m, g.n_tiles_n, tm, tn);
-}
-
-// A 16-byte zero vector in global memory: the source of the DMA loads of
-// masked lanes (rows past T, k past K, columns past N), so those LDS slots
-// hold zeros.
-__device__ __attribute__((aligned(16))) uint4 g_zero16[1];
-
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef short short8_t __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) short4_t lds_short4_t;
-
-// One 16-byte-per-lane DMA load from global memory straight into LDS: lane
-// l's bytes land at lds_wave_base + 16 l (gfx950 global_load_lds_dwordx4).
-// Issued as inline assembly so the compiler does not add its own
-// conservative vmcnt waits before later LDS reads; the kernel orders these
-// loads itself with explicit s_waitcnt vmcnt before each barrier.
-__device__ __forceinline__ void dma16(const void *gptr, const void *lds_wave_base) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_wave_base)));
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0)
-                 : "memory", "m0");
-}
-
-// XOR swizzles of the 16-byte chunk index inside an LDS row: conflict-free
-// fragment reads for 32 and for 64 LDS banks.
-//   x rows (BK bf16): ds_read_b128 of 16 consecutive rows at one chunk.
-//   W rows (BN bf16): ds_read_b64_tr_b16 of 4 rows x 64 bytes per half-wave.
-template <int BK> __device__ __forceinline__ int swz_x(int r) {
-    return BK == 64 ? ((r ^ (r >> 3)) & 7) : (((r >> 2) ^ (r >> 1)) & 3);
-}
-template <int BN> __device__ __forceinline__ int swz_w(int k) {
-    // rows of >= 16 chunks: 0, 6, 10, 12 for k % 4 = 0..3; rows of 8 chunks: 0, 2, 4, 6
-    return BN >= 128 ? ((0xCA60 >> (4 * (k & 3))) & 0xF) : 2 * (k & 3);
-}
-
-// Scheduling pattern for one group of NMFMA MFMAs and the NREAD LDS reads of
-// the next fragments (sched_group_barrier masks: 0x100 LDS read, 0x008 MFMA):
-// the reads go out early, at least two per MFMA.
-template <int NREAD, int NMFMA> __device__ __forceinline__ void sched_interleave() {
-    constexpr int per = (NREAD + NMFMA - 1) / NMFMA > 2 ? (NREAD + NMFMA - 1) / NMFMA : 2;
-#pragma unroll
-    for (int i = 0; i < NMFMA; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-}
-
-// The expand on MFMA: acc[rb][cb] += (s_a v[t]) B_a for the rows of each
-// distinct adapter a among a wavefront's 32-row block (found with ballots;
-// other rows get zero operands).  v is split into bf16 high and low parts so
-// the fp32 intermediate keeps about 16 mantissa bits; B octets (8 ranks of
-// one column, 16 bytes) are exactly the MFMA B operand of one lane.
-// Operand mapping of v_mfma_f32_32x32x16_bf16 per lane l: A = row (l % 32),
-// ranks 16 ks + 8 (l / 32) + 0..7; B = column (l % 32), the same ranks.
-template <int RB, int CB>
-__device__ __forceinline__ void lora_pass_impl(const gemm_args &g, f32x16_t (&acc)[RB][CB],
-                                               const int32_t *s_t, const int32_t *s_id, int n0,
-                                               int wrow0, int wcol0, int lane) {
-    const int R = g.max_rank, RO = g.max_rank / 8, N = g.N;
-    const int half = lane >> 5;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int row = wrow0 + rb * 32 + (lane & 31);
-        const int32_t my_id = s_id[row];
-        const int32_t my_t = s_t[row];
-        uint64_t pend = __ballot(my_id >= 0) & 0xffffffffull;
-        while (pend) {
-            const int first = __ffsll((long long)pend) - 1;
-            const int32_t a = __shfl(my_id, first, 64);
-            pend &= ~(__ballot(my_id == a) & 0xffffffffull);
-            const int32_t ra = g.rank[a];
-            const float sa = g.scale[a];
-            const uint32_t vm = (my_id == a) ? ~0u : 0u;
-            const float *vrow = g.v + (int64_t)(my_id == a ? my_t : 0) * g.v_stride;
-            for (int ks = 0; ks * 16 < ra; ++ks) {
-                const int j0 = 16 * ks + 8 * half;
-                const int oct = 2 * ks + half;
-                const bool j_ok = j0 < ra;              // octets past the slot's rank: not read
-                const float *vp = vrow + (j_ok ? j0 : 0);
-                float4 v0 = *reinterpret_cast<const float4 *>(vp);
-                float4 v1 = *reinterpret_cast<const float4 *>(vp + 4);
-                uint4 bq[CB];
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    const int col = wcol0 + cb * 32 + (lane & 31);
-                    const bool ok = j_ok && col < N;
-                    bq[cb] = ldg16(g.b + ((int64_t)a * R * N + ((int64_t)(ok ? oct : 0) * N + (ok ? col : 0)) * 8));
-                    const uint32_t m = ok ? ~0u : 0u;
-                    bq[cb] = make_uint4(bq[cb].x & m, bq[cb].y & m, bq[cb].z & m, bq[cb].w & m);
-                }
-                const uint32_t m = j_ok ? vm : 0u;
-                float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-                uint32_t hi[4], lo[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float f0 = __uint_as_float(__float_as_uint(sa * vv[2 * e]) & m);
-                    const float f1 = __uint_as_float(__float_as_uint(sa * vv[2 * e + 1]) & m);
-                    const uint32_t h0 = f32_to_bf16_bits(f0), h1 = f32_to_bf16_bits(f1);
-                    hi[e] = h0 | (h1 << 16);
-                    lo[e] = f32_to_bf16_bits(f0 - __uint_as_float(h0 << 16)) |
-                            (f32_to_bf16_bits(f1 - __uint_as_float(h1 << 16)) << 16);
-                }
-                const bf16x8_t ahi = __builtin_bit_cast(bf16x8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
-                const bf16x8_t alo = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    const bf16x8_t bb = __builtin_bit_cast(bf16x8_t, bq[cb]);
-                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bb, acc[rb][cb], 0, 0, 0);
-                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bb, acc[rb][cb], 0, 0, 0);
-                }
-            }
-        }
-    }
-}
 
 template <int BM, int BN, int BK, int NS, bool SH, int WV = 4, int WR = 2> struct gemm_cfg {
     // WV wavefronts in a WR x (WV/WR) grid; each owns a WM x WN tile
@@ -453,133 +288,8 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
         if (sh_gq == 0 && sh_t < T) g.vpart[((int64_t)split * T + sh_t) * R + sh_j] = vsum;
     }
 
-    // ---- epilogue ----
-    // Each wavefront moves one 32 x WN block of its accumulators at a time
-    // through its own LDS area; a lane then owns 8 consecutive columns of
-    // several rows and writes them with 16-byte stores after one rounding (the
-    // low-rank term is already in the accumulators).  In split-K mode the
-    // staged fp32 rows go to the partial buffer instead.
-    constexpr int SLD = C::SLD;
-    constexpr int QN = WN / 8, RPP = 64 / QN, PASSES = 32 / RPP;
-    float *stage = reinterpret_cast<float *>(smem) + w * 32 * SLD;
-    const int q = lane % QN, rr = lane / QN;
-    const int n = n0 + wn * WN + 8 * q;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        __syncthreads();
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                stage[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * SLD + cb * 32 + (lane & 31)] =
-                    acc[rb][cb][e];
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < PASSES; ++k) {
-            const int i = wm * WM + rb * 32 + rr + RPP * k;
-            const int32_t tk = s_meta_t[i];
-            if (tk < 0 || n >= N) continue;
-            const float *src = stage + (rr + RPP * k) * SLD + 8 * q;
-            const float4 o0 = *reinterpret_cast<const float4 *>(src);
-            const float4 o1 = *reinterpret_cast<const float4 *>(src + 4);
-            if (SPLIT) {
-                float *dst = g.partial + (((int64_t)tidx * g.splits + split) * BM + i) * BN + (n - n0);
-                *reinterpret_cast<float4 *>(dst) = o0;
-                *reinterpret_cast<float4 *>(dst + 4) = o1;
-            } else {
-                const float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-                stg16(g.y + (int64_t)tk * N + n, vec16<LORA_BF16>::narrow(o));
-            }
-        }
-    }
-}
-
-// s * sum_j v[j] B[j][n..n+8] for one row: G rank octets of slot `id`, 8
-// consecutive columns starting at n (B in rank octets [R/8][N][8]).
-__device__ __forceinline__ void lora_delta8(const uint16_t *b, int32_t id, int32_t R, int32_t N,
-                                            int32_t n, int32_t G, const float *vrow, float *d) {
-    for (int gg = 0; gg < G; ++gg) {
-        const uint16_t *bp = b + ((int64_t)id * R * N + ((int64_t)gg * N + n) * 8);
-        const float4 v0 = *reinterpret_cast<const float4 *>(vrow + gg * 8);
-        const float4 v1 = *reinterpret_cast<const float4 *>(vrow + gg * 8 + 4);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            float bf[8];
-            vec16<LORA_BF16>::widen(ldg16(bp + c * 8), bf);
-            float a = d[c];
-            a = fmaf(v0.x, bf[0], a); a = fmaf(v0.y, bf[1], a);
-            a = fmaf(v0.z, bf[2], a); a = fmaf(v0.w, bf[3], a);
-            a = fmaf(v1.x, bf[4], a); a = fmaf(v1.y, bf[5], a);
-            a = fmaf(v1.z, bf[6], a); a = fmaf(v1.w, bf[7], a);
-            d[c] = a;
-        }
-    }
-}
-
-// Split-K reduction over the tiles of one split launch.  A workgroup takes
-// RW = 2048 / BN rows of one tile; a thread owns 8 consecutive columns of one
-// row: y[t][n..n+8] = bf16(sum_s partial[tile][s][r][c..c+8]
-//                          (+ s_a * sum_j v[t][j] B_a[j][n..n+8])), t = perm[p].
-// The partials of an element are summed in split order (deterministic).
-// With VP (fused shrink) the rows' v are first summed from the K-range rank
-// partials (in range order) into LDS, and the first column tile flags bad ids.
-template <bool LORA, bool VP, int BM, int BN>
-__global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g) {
-    constexpr int RW = 2048 / BN, CPR = BN / 8, CHUNKS = BM / RW;
-    const int tidx = blockIdx.x / CHUNKS, chunk = blockIdx.x % CHUNKS;
-    int tm, tn;
-    grouped_tile(g.tile_base + tidx, g.n_tiles_m, g.n_tiles_n, tm, tn);
-    const int T = g.T, N = g.N, R = g.max_rank;
-    const int r = chunk * RW + threadIdx.x / CPR, c = (threadIdx.x % CPR) * 8;
-    const int p = tm * BM + r, n = tn * BN + c;
-    __shared__ __attribute__((aligned(16))) float s_v[VP ? RW * 64 : 1];
-    if (VP) {
-        for (int e = threadIdx.x; e < RW * R; e += 256) {
-            const int rr = e / R, j = e % R;
-            const int pp = tm * BM + chunk * RW + rr;
-            float sum = 0.0f;
-            if (pp < T) {
-                const int32_t tt = perm_row(g.perm, pp, T);
-                if (tt >= 0) {
-                    for (int sidx = 0; sidx < g.splits; ++sidx)
-                        sum += g.vpart[((int64_t)sidx * T + tt) * R + j];
-                    if (j == 0 && tn == 0) {
-                        const int32_t raw = g.ids[tt];
-                        const bool ok = raw == -1 || (raw >= 0 && raw < g.n_slots && g.rank[raw] > 0);
-                        if (!ok) flag_bad_row(g.err, tt);
-                    }
-                }
-            }
-            s_v[rr * R + j] = sum;
-        }
-        __syncthreads();
-    }
-    if (p >= T || n >= N) return;
-    const int32_t t = perm_row(g.perm, p, T);
-    if (t < 0) return;
-    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int sidx = 0; sidx < g.splits; ++sidx) {
-        const float *src = g.partial + (((int64_t)tidx * g.splits + sidx) * BM + r) * BN + c;
-        const float4 a = *reinterpret_cast<const float4 *>(src);
-        const float4 b = *reinterpret_cast<const float4 *>(src + 4);
-        o[0] += a.x; o[1] += a.y; o[2] += a.z; o[3] += a.w;
-        o[4] += b.x; o[5] += b.y; o[6] += b.z; o[7] += b.w;
-    }
-    if (LORA) {
-        const int32_t raw = g.ids[t];
-        if (raw >= 0 && raw < g.n_slots) {
-            const int32_t rk = g.rank[raw];
-            if (rk > 0) {
-                float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                lora_delta8(g.b, raw, R, N, n, (rk + 7) >> 3,
-                            VP ? s_v + (r - chunk * RW) * R : g.v + (int64_t)t * g.v_stride, d);
-                const float sc = g.scale[raw];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) o[q] = fmaf(sc, d[q], o[q]);
-            }
-        }
-    }
-    stg16(g.y + (int64_t)t * N + n, vec16<LORA_BF16>::narrow(o));
+    gemm_store_tile<BM, BN, WV, WR, SPLIT>(g, acc, reinterpret_cast<float *>(smem), s_meta_t, n0, w, lane,
+                                         tidx, split);
 }
 
 struct gemm_f32_args {
@@ -671,59 +381,6 @@ __global__ void __launch_bounds__(256) k_gemm_f32(gemm_f32_args g) {
     }
 }
 
-// Tile configuration and K split for one bf16 GEMM shape.
-struct gemm_plan {
-    int bm, bn;
-    int n_dp;          // tiles computed whole (with the fused expand), from tile 0
-    int tail;          // tiles after those, computed as split-K pieces + reduction
-    int splits, k_chunk;
-};
-
-static int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
-
-// Largest tile that still gives close to one workgroup per CU.  When the last
-// round of tiles would leave most CUs idle (a tail of at most 160 of 256),
-// those tail tiles are split over K so every CU takes a share.  Grids that
-// stay small (few token rows) split K for all tiles.  Split-K needs room for
-// the fp32 partials in the workspace.
-static gemm_plan plan_gemm(int T, int K, int N, size_t partial_bytes) {
-    static const int cfg[4][2] = {{256, 256}, {256, 128}, {128, 128}, {128, 64}};
-    for (int c = 0; c < 4; ++c) {
-        const int bm = cfg[c][0], bn = cfg[c][1];
-        const int tiles = ceil_div(T, bm) * ceil_div(N, bn);
-        if (tiles < 224) continue;
-        gemm_plan p{bm, bn, tiles, 0, 1, K};
-        const int full = tiles / 256 * 256, rem = tiles - full;
-        if (full > 0 && rem > 0 && rem <= 160 && K >= 1024) {
-            int sp = 256 / rem;
-            if (sp > kMaxGemmSplit) sp = kMaxGemmSplit;
-            if (sp > K / 512) sp = K / 512;
-            while (sp > 1 && (size_t)sp * rem * bm * bn * 4 > partial_bytes) --sp;
-            if (sp >= 2) {
-                const int kc = ceil_div(ceil_div(K, sp), 64) * 64;
-                p = gemm_plan{bm, bn, full, rem, ceil_div(K, kc), kc};
-            }
-        }
-        return p;
-    }
-    // Small grid (decode-sized T): split K.  One 256-row tile covers T <= 256,
-    // so W is read once; narrow 64-column tiles keep the number of fp32
-    // partial copies (written and read back) low for the same grid size.
-    const int bm = T <= 256 ? 256 : 128, bn = T <= 256 ? 64 : 128;
-    const int tiles = ceil_div(T, bm) * ceil_div(N, bn);
-    int splits = ceil_div(256, tiles);
-    const int max_by_k = K / 256 > 0 ? K / 256 : 1;
-    if (splits > max_by_k) splits = max_by_k;
-    if (splits > kMaxGemmSplit) splits = kMaxGemmSplit;
-    while (splits > 1 && (size_t)splits * tiles * bm * bn * 4 > partial_bytes) --splits;
-    if (splits <= 1) {
-        const int t2 = ceil_div(T, 128) * ceil_div(N, 64);
-        return t2 > tiles ? gemm_plan{128, 64, t2, 0, 1, K} : gemm_plan{bm, bn, tiles, 0, 1, K};
-    }
-    const int k_chunk = ceil_div(ceil_div(K, splits), 64) * 64;
-    return {bm, bn, 0, tiles, ceil_div(K, k_chunk), k_chunk};
-}
-
 template <int BM, int BN, int NS = 2, int WV = 4, int WR = 2, int BK = 64>
 static void launch_cfg(gemm_args g, const gemm_plan &pl, bool lora, hipStream_t s) {
     if (pl.n_dp > 0) {
@@ -770,7 +427,7 @@ lora_status_t launch_gemm_fused_shrink(const void *x, const void *W, void *y, in
                                        const lora_pool_t *pool, const int32_t *ids, float *vpart,
                                        int32_t *err, float *partial, size_t partial_bytes,
                                        hipStream_t s) {
-    gemm_args g;
+    gemm_args g{};
     g.x = (const uint16_t *)x;
     g.W = (const uint16_t *)W;
     g.y = (uint16_t *)y;
@@ -808,7 +465,7 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
                           const int32_t *ids, const float *v, int32_t v_stride,
                           const int32_t *perm, float *partial, size_t partial_bytes, hipStream_t s) {
     if (dtype == LORA_BF16) {
-        gemm_args g;
+        gemm_args g{};
         g.x = (const uint16_t *)x;
         g.W = (const uint16_t *)W;
         g.y = (uint16_t *)y;

@@ -40,6 +40,8 @@ EXPORTED = (
     "lora_workspace_bytes_sliced", "lora_shrink_sliced", "lora_linear_forward_sliced",
     "lora_pack_host", "lora_cache_create", "lora_cache_destroy", "lora_cache_register", "lora_cache_map",
     "lora_cache_commit", "lora_cache_slot_of", "lora_cache_stats",
+    "lora_quantize_rows_fp8", "lora_quantize_weight_fp8", "lora_gemm_fp8", "lora_workspace_bytes_fp8",
+    "lora_linear_forward_fp8",
     "lora_get_device_error",
     "lora_status_string", "lora_version",
 )
@@ -120,6 +122,12 @@ def load(path: str = LIB_PATH):
         "lora_cache_slot_of": (c_i32, [c_vp, c_i32, P(c_i32)]),
         "lora_cache_stats": (c_i32, [c_vp, P(ctypes.c_int64), P(ctypes.c_int64), P(ctypes.c_int64),
                                      P(ctypes.c_int64)]),
+        "lora_quantize_rows_fp8": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp]),
+        "lora_quantize_weight_fp8": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp]),
+        "lora_gemm_fp8": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_sz, c_vp]),
+        "lora_workspace_bytes_fp8": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
+        "lora_linear_forward_fp8": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32, P(lora_pool_t), c_vp, c_i32, c_u32,
+                                            c_vp, c_sz, c_vp]),
         "lora_get_device_error": (c_i32, [c_vp, c_sz, c_vp, P(c_i32)]),
         "lora_status_string": (ctypes.c_char_p, [c_i32]),
         "lora_version": (ctypes.c_char_p, []),
@@ -334,6 +342,44 @@ class AdapterCache:
             pass
 
 
+def lora_quantize_rows_fp8(x, T, d, xq, x_scale, stream=None):
+    _ok(load().lora_quantize_rows_fp8(_ptr(x), T, d, _ptr(xq), _ptr(x_scale), _stream(stream)),
+        "lora_quantize_rows_fp8")
+
+
+def lora_quantize_weight_fp8(W, d_in, d_out, wq, w_scale, stream=None):
+    _ok(load().lora_quantize_weight_fp8(_ptr(W), d_in, d_out, _ptr(wq), _ptr(w_scale), _stream(stream)),
+        "lora_quantize_weight_fp8")
+
+
+def lora_gemm_fp8(xq, x_scale, wq, w_scale, y, T, d_in, d_out, ws=None, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _ok(load().lora_gemm_fp8(_ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(y), T, d_in, d_out,
+                             _ptr(ws), nbytes, _stream(stream)), "lora_gemm_fp8")
+
+
+def lora_workspace_bytes_fp8(T, n_slots, max_rank, d_in, d_out=0) -> int:
+    return int(load().lora_workspace_bytes_fp8(T, n_slots, max_rank, d_in, d_out))
+
+
+def lora_linear_forward_fp8(x, wq, w_scale, y, T, pool, ids, mode, flags, ws, stream=None):
+    _ok(load().lora_linear_forward_fp8(_ptr(x), _ptr(wq), _ptr(w_scale), _ptr(y), T, ctypes.byref(pool),
+                                       _ptr(ids), mode, flags, _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream(stream)), "lora_linear_forward_fp8")
+
+
+class Fp8Weight:
+    """E4M3 codes [d_out, d_in] and fp32 column scales of a bf16 base weight
+    W [d_in, d_out], made on the device by lora_quantize_weight_fp8."""
+
+    def __init__(self, W, stream=None):
+        d_in, d_out = W.shape
+        self.d_in, self.d_out = d_in, d_out
+        self.codes = torch.empty(d_out, d_in, dtype=torch.uint8, device=W.device)
+        self.scale = torch.empty(d_out, dtype=torch.float32, device=W.device)
+        lora_quantize_weight_fp8(W, d_in, d_out, self.codes, self.scale, stream)
+
+
 def lora_get_device_error(ws, stream=None) -> int:
     row = ctypes.c_int32()
     _ok(load().lora_get_device_error(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream),
@@ -374,8 +420,13 @@ class AdapterPool:
 class Workspace:
     """A device workspace sized for (T, n_slots, max_rank, d_out), initialised."""
 
-    def __init__(self, T, n_slots, max_rank, d_out=0, device="cuda", stream=None, n_slices=1):
-        n = lora_workspace_bytes_sliced(T, n_slots, max_rank, n_slices, d_out)
+    def __init__(self, T, n_slots, max_rank, d_out=0, device="cuda", stream=None, n_slices=1, fp8_d_in=0):
+        if fp8_d_in:
+            if n_slices != 1:
+                raise LoraError(LORA_ERR_INVALID_ARGUMENT, "lora_workspace_bytes_fp8")
+            n = lora_workspace_bytes_fp8(T, n_slots, max_rank, fp8_d_in, d_out)
+        else:
+            n = lora_workspace_bytes_sliced(T, n_slots, max_rank, n_slices, d_out)
         if n == 0:
             raise LoraError(LORA_ERR_INVALID_ARGUMENT, "lora_workspace_bytes")
         self.T, self.n_slots, self.max_rank = T, n_slots, max_rank

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     src = open(os.path.join(ROOT, "include", "lora.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(lora_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(lora_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -167,3 +167,44 @@ def test_sliced_validation(lib):
     assert g(fake, W, Y, 64, arr, 3, fake, 0, 0, fake, need, None) == L.LORA_ERR_INVALID_ARGUMENT
     assert g(fake, W, Y, 64, arr, 3, fake, 0, 8, fake, need, None) == L.LORA_ERR_INVALID_ARGUMENT
     assert g(None, W, Y, 0, arr, 3, None, 0, 0, fake, need, None) == L.LORA_OK
+
+
+def test_fp8_validation(lib):
+    """FP8 entry points: sizes, and every rejection happens on the host."""
+    fake = 1 << 20
+    P = L.lora_pool_t
+    assert L.lora_workspace_bytes_fp8(64, 8, 16, 512, 256) == \
+        L.lora_workspace_bytes(64, 8, 16, 256) + 64 * 512 + 256
+    assert L.lora_workspace_bytes_fp8(64, 8, 16, 520, 256) == 0           # d_in % 16
+    assert L.lora_workspace_bytes_fp8(64, 8, 12, 512, 256) == 0           # bad max_rank
+    q = lib.lora_quantize_rows_fp8
+    assert q(fake, 4, 24, fake, fake, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert q(fake, -1, 32, fake, fake, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert q(fake, 4, 32, fake + 8, fake, None) == L.LORA_ERR_INVALID_ARGUMENT
+    w = lib.lora_quantize_weight_fp8
+    assert w(fake, 24, 64, fake, fake, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert w(fake, 32, 60, fake, fake, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert w(None, 32, 64, fake, fake, None) == L.LORA_ERR_INVALID_ARGUMENT
+    gm = lib.lora_gemm_fp8
+    assert gm(fake, fake, fake, fake, fake, 4, 24, 64, None, 0, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert gm(fake, fake, fake, fake + 4, fake, 4, 32, 64, None, 0, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert gm(None, None, None, None, None, 0, 32, 64, None, 0, None) == L.LORA_OK   # T == 0
+    f = lib.lora_linear_forward_fp8
+    pool = P(8, 512, 256, 16, L.LORA_BF16, fake, fake, fake, fake)
+    need = L.lora_workspace_bytes_fp8(64, 8, 16, 512, 0)
+    assert f(fake, fake, fake, fake, 64, ctypes.byref(pool), fake, 0, 0, fake, need - 1, None) == \
+        L.LORA_ERR_WORKSPACE_TOO_SMALL
+    # the bf16 workspace is too small: the quantized rows of x need room
+    assert f(fake, fake, fake, fake, 64, ctypes.byref(pool), fake, 0, 0, fake,
+             L.lora_workspace_bytes(64, 8, 16, 0), None) == L.LORA_ERR_WORKSPACE_TOO_SMALL
+    f32pool = P(8, 512, 256, 16, L.LORA_F32, fake, fake, fake, fake)
+    assert f(fake, fake, fake, fake, 64, ctypes.byref(f32pool), fake, 0, 0, fake, need, None) == \
+        L.LORA_ERR_INVALID_ARGUMENT
+    odd = P(8, 520, 256, 16, L.LORA_BF16, fake, fake, fake, fake)
+    assert f(fake, fake, fake, fake, 64, ctypes.byref(odd), fake, 0, 0, fake, need, None) == \
+        L.LORA_ERR_INVALID_ARGUMENT
+    assert f(fake, fake, fake + 4, fake, 64, ctypes.byref(pool), fake, 0, 0, fake, need, None) == \
+        L.LORA_ERR_INVALID_ARGUMENT
+    assert f(fake, fake, fake, fake, 64, ctypes.byref(pool), fake, 3, 0, fake, need, None) == \
+        L.LORA_ERR_INVALID_ARGUMENT
+    assert f(None, None, None, None, 0, ctypes.byref(pool), None, 0, 0, fake, need, None) == L.LORA_OK
