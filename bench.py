@@ -32,13 +32,17 @@ if ROOT not in sys.path:
 METRIC = ("mixed-adapter LoRA-layer tokens/s; shrink/expand HBM GB/s and base-GEMM MFMA % of peak")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16 MFMA
+MFMA_FP8_PEAK_TFS = 5000.0     # dense fp8 MFMA
 FP32_VALU_PEAK_TFS = 157.3     # fp32 vector
 RIDGE = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
+RIDGE_FP8 = MFMA_FP8_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
 MALL_BYTES = 256 * 2 ** 20
 CSRC = os.path.join(ROOT, "rank_adapter_gemm_amd", "csrc")
-KERNEL_SOURCE = {"gemm_expand": ["gemm.hip"], "shrink": ["shrink.hip"], "segments": ["segments.hip"],
-                 "expand": ["expand.hip"],
-                 "forward": ["api.hip", "gemm.hip", "shrink.hip", "segments.hip", "expand.hip"]}
+KERNEL_SOURCE = {"gemm_expand": ["gemm.hip", "gemm_common.hpp"], "shrink": ["shrink.hip"],
+                 "segments": ["segments.hip"], "expand": ["expand.hip"],
+                 "forward": ["api.hip", "gemm.hip", "gemm_common.hpp", "shrink.hip", "segments.hip", "expand.hip"],
+                 "forward_fp8": ["api.hip", "gemm_fp8.hip", "gemm_common.hpp", "shrink.hip", "segments.hip",
+                                 "expand.hip"]}
 
 
 def parse():
@@ -56,6 +60,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU work of the oracle sample")
     ap.add_argument("--residency", action="store_true",
                     help="also measure the adapter cache's host-to-HBM promotion rate")
+    ap.add_argument("--fp8-base", action="store_true",
+                    help="E4M3 base weights (lora_linear_forward_fp8); reported apart from the bf16 headline")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain fp32 copy kernel of known size (for counter scaling)")
     return ap.parse_args()
@@ -109,7 +115,12 @@ def main():
         pr.A = pr.B = None
 
     # ---- working-set copies for cache-cold timing ----
-    set_bytes = sum(p.W.numel() * eb + pl.nbytes + T * p.d_out * eb for p, pl in zip(wl.projections, pools))
+    fp8 = args.fp8_base
+    if fp8 and wl.dtype != torch.bfloat16:
+        print("--fp8-base takes a bf16 workload", file=sys.stderr)
+        sys.exit(2)
+    wb = 1 if fp8 else eb                        # bytes per base weight read by the step
+    set_bytes = sum(p.W.numel() * wb + pl.nbytes + T * p.d_out * eb for p, pl in zip(wl.projections, pools))
     set_bytes += sum(x.numel() * eb for x in wl.xs.values())
     n_sets = args.cold_sets
     if n_sets is None:
@@ -132,19 +143,24 @@ def main():
                                   pl.pool.dtype, a.data_ptr(), b.data_ptr(), sc.data_ptr(), rk.data_ptr())
                 ps.append(q)
         ys = [torch.empty(T, p.d_out, dtype=wl.dtype, device=dev) for p in wl.projections]
-        sets.append(dict(xs=xs, Ws=Ws, pools=ps, ys=ys, keep=keep))
+        W8 = [L.Fp8Weight(W) for W in Ws] if fp8 else None
+        sets.append(dict(xs=xs, Ws=Ws, pools=ps, ys=ys, keep=keep, W8=W8))
     # Projections that share an input (consecutive, same x) run as slices of
     # one lora_linear_forward_sliced call: one shrink, one read of x.
     groups = []
     for k, pr in enumerate(wl.projections):
-        if (not args.no_slices and groups and wl.projections[groups[-1][0]].x_group == pr.x_group
+        if (not args.no_slices and not fp8 and groups and wl.projections[groups[-1][0]].x_group == pr.x_group
                 and len(groups[-1]) < 4 and (len(groups[-1]) + 1) * R <= 128):
             groups[-1].append(k)
         else:
             groups.append([k])
     ws = L.Workspace(T, wl.n_slots, R, max(p.d_out for p in wl.projections), device=dev,
-                     n_slices=max(len(g) for g in groups))
+                     n_slices=max(len(g) for g in groups),
+                     fp8_d_in=max(p.d_in for p in wl.projections) if fp8 else 0)
     v = torch.empty(T, R, dtype=torch.float32, device=dev)
+    if fp8:
+        xq8 = torch.empty(T, max(p.d_in for p in wl.projections), dtype=torch.uint8, device=dev)
+        xs8 = torch.empty(T, dtype=torch.float32, device=dev)
     flags0 = L.LORA_FLAG_SEPARATE_EXPAND if args.separate_expand else 0
     torch.cuda.synchronize()
 
@@ -153,7 +169,11 @@ def main():
         grp = groups[gi]
         fl = flags0 | (L.LORA_FLAG_SEGMENTS_READY if (sgmv and gi > 0) else 0)
         x = s_["xs"][wl.projections[grp[0]].x_group]
-        if len(grp) == 1:
+        if fp8:
+            k = grp[0]
+            L.lora_linear_forward_fp8(x, s_["W8"][k].codes, s_["W8"][k].scale, s_["ys"][k], T, s_["pools"][k],
+                                      ids, mode, fl, ws.buf)
+        elif len(grp) == 1:
             k = grp[0]
             L.lora_linear_forward(x, s_["Ws"][k], s_["ys"][k], T, s_["pools"][k], ids, mode, fl, ws.buf)
         else:
@@ -205,6 +225,8 @@ def main():
     names = (["segments"] if sgmv else []) + ["shrink", "gemm_expand"]
     if args.separate_expand:
         names = (["segments"] if sgmv else []) + ["shrink", "gemm", "expand"]
+    if fp8:
+        names = (["segments"] if sgmv else []) + ["quantize", "shrink", "gemm_fp8"]
     smode = L.LORA_MODE_SGMV if sgmv else L.LORA_MODE_BGMV
 
     def call(name, k, i):
@@ -219,6 +241,11 @@ def main():
             L.lora_gemm(x, W, y, T, pr.d_in, pr.d_out, L.dtype_code(wl.dtype), ws=ws.buf)
         elif name == "expand":
             L.lora_expand(v, T, pool, ids, smode, y, ws.buf)
+        elif name == "quantize":
+            L.lora_quantize_rows_fp8(x, T, pr.d_in, xq8, xs8)
+        elif name == "gemm_fp8":
+            w8 = s_["W8"][k]
+            L.lora_gemm_fp8(xq8, xs8, w8.codes, w8.scale, y, T, pr.d_in, pr.d_out, ws.buf)
         else:
             L.lora_gemm_expand(x, W, y, T, pool, ids, v, smode, ws.buf)
 
@@ -294,6 +321,10 @@ def main():
         if name == "gemm_expand":
             by = (T * d_in + d_in * d_out + T * d_out) * eb + T * R * 4 + sum_r * d_out * eb
             return by, 2 * T * d_in * d_out + 2 * sum_row_r * d_out
+        if name == "quantize":
+            return T * d_in * eb + T * d_in + 4 * T, 0
+        if name == "gemm_fp8":
+            return T * d_in + 4 * T + d_in * d_out + 4 * d_out + T * d_out * eb, 2 * T * d_in * d_out
         raise KeyError(name)
 
     def fwd_work(gi):
@@ -304,6 +335,8 @@ def main():
         for j, k in enumerate(groups[gi]):
             pr = wl.projections[k]
             b_g, f_g = work("gemm", pr)
+            if fp8:                                      # codes and column scales instead of bf16 W
+                b_g += pr.d_in * pr.d_out * (1 - eb) + 4 * pr.d_out
             b_s, f_s = work("shrink", pr)
             b_e, f_e = work("expand", pr)
             by += b_g + (b_s - T * pr.d_in * eb - T * R * 4) + (b_e - T * R * 4 - 2 * T * pr.d_out * eb)
@@ -336,7 +369,9 @@ def main():
     ai = fl_d / by_d
     if wl.dtype == torch.float32:
         roof = dict(bound="alu", achieved=round(fl_d / t_d / 1e12, 2), peak=FP32_VALU_PEAK_TFS, unit="TFLOP/s")
-    elif ai >= RIDGE:
+    elif fp8 and ai >= RIDGE_FP8:
+        roof = dict(bound="mfma", achieved=round(fl_d / t_d / 1e12, 2), peak=MFMA_FP8_PEAK_TFS, unit="TFLOP/s")
+    elif not fp8 and ai >= RIDGE:
         roof = dict(bound="mfma", achieved=round(fl_d / t_d / 1e12, 2), peak=MFMA_BF16_PEAK_TFS, unit="TFLOP/s")
     else:
         roof = dict(bound="hbm", achieved=round(by_d / t_d / 1e9, 1), peak=HBM_PEAK_GBS, unit="GB/s")
@@ -347,7 +382,7 @@ def main():
     roof["avg_launch_us"] = round(fwd[kd] * 1e3, 3)
     roof["algorithmic_bytes_per_launch"] = int(by_d)
     roof["algorithmic_flops_per_launch"] = int(fl_d)
-    roof["traffic"] = stored_traffic("forward", args.workload, roof["projection"])
+    roof["traffic"] = stored_traffic("forward_fp8" if fp8 else "forward", args.workload, roof["projection"])
     breakdown["forward"] = dict(us_per_step=round(1e3 * sum(fwd.values()), 3),
                                 per_call_us={"+".join(wl.projections[k].name for k in groups[gi]):
                                              round(1e3 * v, 3) for gi, v in fwd.items()})
@@ -366,7 +401,7 @@ def main():
 
     # ---- CPU baseline: the fp64 oracle on a bounded sample of this batch ----
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not fp8:      # the baseline belongs to the bf16 headline line
         cpu = cpu_baseline(wl, args.cpu_seconds)
 
     line = {
@@ -380,13 +415,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if wl.dtype == torch.float32 else "bf16",
+        "dtype": "f32" if wl.dtype == torch.float32 else ("e4m3+bf16" if fp8 else "bf16"),
         "data": "synthetic (seeded; random-init adapters and weights)",
         "config": {
             "workload": wl.name, "T": T, "projections": [[p.name, p.d_in, p.d_out] for p in wl.projections],
             "n_slots": wl.n_slots, "max_rank": R, "distinct_adapters": int(used.size),
             "mode": ("sgmv" if sgmv else "bgmv") + ("" if args.mode != "auto" else " (auto)"),
             "expand": "separate" if args.separate_expand else "fused into the base GEMM",
+            "base": ("fp8 e4m3 (per-row x, per-column W scales); bf16 adapters" if fp8 else
+                     ("fp32" if wl.dtype == torch.float32 else "bf16")),
             "calls": ["+".join(wl.projections[k].name for k in g) for g in groups],
             "cold_sets": n_sets, "working_set_MB": round(set_bytes / 1e6, 1),
         },

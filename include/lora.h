@@ -340,12 +340,14 @@ lora_status_t lora_cache_stats(const lora_cache_t *cache, int64_t *hits, int64_t
  * accumulator, never merged into the packed 8-bit weight ("Multi-LoRA
  * Serving 与 Adapter 隔离", section on numerics and mixed precision).  The
  * pages fix no scheme; this library uses OCP E4M3 codes (largest finite 448,
- * subnormals, 0x7f / 0xff NaN) with one fp32 scale per token row of x and one
- * per output column of W:
- *     scale = amax / 448,  code = E4M3(clamp(v * (448 / amax), -448, 448))
- * with correctly rounded fp32 division and product and round-to-nearest-even
- * conversion; an all-zero row or column gets scale 0 and zero codes.  Inputs
- * must be finite.  The layer is
+ * subnormals, 0x7f / 0xff NaN) with one power-of-two scale per token row of x
+ * and one per output column of W:
+ *     scale = 2^e, e the smallest integer with amax <= 448 * 2^e, clamped to
+ *     [-127, 127];  code = E4M3(v * 2^-e)  (exact scaling, round to nearest
+ *     even); an all-zero row or column gets e = -127 and zero codes.
+ * Inputs must be finite.  The matrix cores apply the scales inside the
+ * product (E8M0 block scales), so scales passed to lora_gemm_fp8 must be
+ * such powers of two (as the quantizers below write them).  The layer is
  *     y[t,n] = s_x[t] s_w[n] sum_k dq(xq[t,k]) dq(wq[n,k]) + s_a ((x A_a) B_a)[n]
  * with the low-rank term from the bf16 x, fp32 accumulation and one rounding
  * of y to bf16.  The FP8 products are exact; the matrix cores add each block
@@ -354,18 +356,19 @@ lora_status_t lora_cache_stats(const lora_cache_t *cache, int64_t *hits, int64_t
  * For all of these: d_in a positive multiple of 16, d_out of 8. */
 
 /* Codes and scales of DEVICE x bf16 [T, d]: xq DEVICE uint8 [T, d],
- * x_scale DEVICE fp32 [T]. */
+ * x_scale DEVICE fp32 [T] (each 2^e). */
 lora_status_t lora_quantize_rows_fp8(const void *x, int32_t T, int32_t d, uint8_t *xq, float *x_scale,
                                      lora_stream_t stream);
 
 /* Codes and scales of a base weight, once at load: W DEVICE bf16
  * [d_in, d_out] -> wq DEVICE uint8 [d_out, d_in] (row n holds column n of W,
- * K-contiguous), w_scale DEVICE fp32 [d_out]. */
+ * K-contiguous), w_scale DEVICE fp32 [d_out] (each 2^e). */
 lora_status_t lora_quantize_weight_fp8(const void *W, int32_t d_in, int32_t d_out, uint8_t *wq,
                                        float *w_scale, lora_stream_t stream);
 
-/* Base product only: y = s_x s_w (xq wq^T), y DEVICE bf16 [T, d_out].  ws
- * (DEVICE, may be NULL) as for lora_gemm. */
+/* Base product only: y = s_x s_w (xq wq^T), y DEVICE bf16 [T, d_out]; the
+ * scales are powers of two 2^e, e in [-127, 127] (only their exponents are
+ * read).  ws (DEVICE, may be NULL) as for lora_gemm. */
 lora_status_t lora_gemm_fp8(const uint8_t *xq, const float *x_scale, const uint8_t *wq,
                             const float *w_scale, void *y, int32_t T, int32_t d_in, int32_t d_out,
                             void *ws, size_t ws_bytes, lora_stream_t stream);

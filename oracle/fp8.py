@@ -16,13 +16,16 @@ here (and by the library) is the plainest FP8 one:
   * format: OCP 8-bit E4M3 ("e4m3fn": 1 sign, 4 exponent bits with bias 7,
     3 mantissa bits, subnormals, no infinities, codes 0x7f / 0xff are NaN,
     largest finite 448), rounding to nearest with ties to even;
-  * activations: one scale per token row, s_x[t] = amax_k |x[t,k]| / 448;
-  * weights: one scale per output column, s_w[n] = amax_k |W[k,n]| / 448,
-    codes stored K-contiguous (row n of Wq holds column n of W);
-  * a code is E4M3(clamp(v * (448 / amax), -448, 448)); an all-zero row or
-    column gets scale 0 and all codes 0.  Scale and scaled value are fp32
-    operations (a correctly rounded division, then a product), so the codes
-    are a function of the fp32 arithmetic, fixed here and on the GPU alike;
+  * one power-of-two scale per token row of x and per output column of W
+    (codes of W stored K-contiguous: row n of Wq holds column n of W):
+    s = 2^e with e the smallest integer such that amax <= 448 * 2^e, where
+    amax is the row's (column's) largest magnitude, clamped to
+    [-127, 127] (the range of the matrix cores' E8M0 block scales, which
+    apply these scales inside the product); an all-zero row or column gets
+    e = -127 and zero codes;
+  * a code is E4M3(v * 2^-e): the scaled value is exact (a power-of-two
+    product that stays within +-448), so the codes depend on no rounding
+    but the one to E4M3;
   * output: y[t,n] = s_x[t] s_w[n] sum_k dq(xq[t,k]) dq(wq[n,k])
                      + s_a * ((x[t] A_a) B_a)[n]   (adapter rows),
     where the low-rank term uses the unquantized bf16 x.
@@ -94,25 +97,32 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
     return (code | sign).astype(np.uint8)
 
 
+def scale_exponent(amax: np.ndarray) -> np.ndarray:
+    """Smallest integer e with amax <= 448 * 2^e, clamped to [-127, 127]
+    (-127 for amax = 0).  Exact: with amax = m * 2^E, 1 <= m < 2, and
+    448 = 1.75 * 2^8, e = E - 8 when m <= 1.75, else E - 7."""
+    amax = np.asarray(amax, dtype=np.float64)
+    f, E = np.frexp(amax)                   # amax = f * 2^E, 0.5 <= f < 1
+    m = 2.0 * f                             # amax = m * 2^(E - 1)
+    e = np.where(m <= 1.75, (E - 1) - 8, (E - 1) - 7)
+    e = np.where(amax > 0, e, -127)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
 def quantize_rows_e4m3(a: np.ndarray):
     """Per-row E4M3 quantization of a float32 matrix [R, K].
 
-    Returns (codes uint8 [R, K], scale float32 [R]) with
-    scale = amax / 448 and codes = E4M3(clamp(a * (448 / amax), +-448)),
-    every scale and product taken in float32 as stated above."""
+    Returns (codes uint8 [R, K], scale float32 [R]) with scale = 2^e, e from
+    ``scale_exponent`` of the row's largest magnitude, and
+    codes = E4M3(a * 2^-e) (an exact scaling)."""
     a = np.ascontiguousarray(a, dtype=np.float32)
     if a.ndim != 2:
         raise ValueError("quantize_rows_e4m3 takes a 2-D array")
     amax = np.abs(a).max(axis=1) if a.shape[1] else np.zeros(a.shape[0], np.float32)
-    amax = amax.astype(np.float32)
-    zero = amax == 0
-    with np.errstate(divide="ignore"):
-        inv = np.where(zero, np.float32(0), np.float32(E4M3_MAX) / np.where(zero, np.float32(1), amax))
-    inv = inv.astype(np.float32)
-    scaled = (a * inv[:, None]).astype(np.float32)
-    scaled = np.clip(scaled, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
-    codes = e4m3_encode(scaled.astype(np.float64))
-    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    e = scale_exponent(amax)
+    scaled = np.ldexp(a.astype(np.float64), -e[:, None])
+    codes = e4m3_encode(scaled)
+    scale = np.ldexp(1.0, e).astype(np.float32)      # 2^-127 is an fp32 subnormal, still exact
     return codes, scale
 
 

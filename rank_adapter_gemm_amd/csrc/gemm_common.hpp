@@ -29,8 +29,8 @@ struct gemm_args {
     int32_t *err;                  // fused shrink: the workspace error word
     const uint8_t *xq;             // FP8 base: E4M3 codes of the x rows [T][K]
     const uint8_t *wq;             // FP8 base: E4M3 codes of the W columns [N][K]
-    const float *xs;               // FP8 base: row scales [T]
-    const float *wsc;              // FP8 base: column scales [N]
+    const float *xs;               // FP8 base: row scales [T] (powers of two)
+    const float *wsc;              // FP8 base: column scales [N] (powers of two)
 };
 
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs (each
@@ -115,62 +115,123 @@ template <int NREAD, int NMFMA> __device__ __forceinline__ void sched_interleave
 // one column, 16 bytes) are exactly the MFMA B operand of one lane.
 // Operand mapping of v_mfma_f32_32x32x16_bf16 per lane l: A = row (l % 32),
 // ranks 16 ks + 8 (l / 32) + 0..7; B = column (l % 32), the same ranks.
-template <int RB, int CB>
+
+// Loads of one 16-rank step ks of adapter a for one lane: its row's 8 ranks
+// of v (zeroed later unless the row belongs to a) and its columns' B octets
+// (zero past the slot's rank or the last column).
+template <int CB>
+__device__ __forceinline__ void lora_step_load(const gemm_args &g, int32_t a, int32_t ra, bool mine,
+                                               int32_t my_t, int ks, int half, int wcol0, int lane,
+                                               float4 &v0, float4 &v1, uint4 (&bq)[CB]) {
+    const int R = g.max_rank, N = g.N;
+    const int j0 = 16 * ks + 8 * half;
+    const int oct = 2 * ks + half;
+    const bool j_ok = a >= 0 && j0 < ra;              // octets past the slot's rank: not read
+    const float *vp = g.v + (mine && j_ok ? (int64_t)my_t * g.v_stride + j0 : 0);
+    v0 = *reinterpret_cast<const float4 *>(vp);
+    v1 = *reinterpret_cast<const float4 *>(vp + 4);
+    const int64_t abase = (int64_t)(a >= 0 ? a : 0) * R * N;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const int col = wcol0 + cb * 32 + (lane & 31);
+        const bool ok = j_ok && col < N;
+        bq[cb] = ldg16(g.b + (abase + ((int64_t)(ok ? oct : 0) * N + (ok ? col : 0)) * 8));
+        const uint32_t m = ok ? ~0u : 0u;
+        bq[cb] = make_uint4(bq[cb].x & m, bq[cb].y & m, bq[cb].z & m, bq[cb].w & m);
+    }
+}
+
+// acc += (s_a v) B for one step from loaded operands; lanes with `use` false
+// (rows of other adapters, ranks past the slot's) contribute zero.
+template <int CB>
+__device__ __forceinline__ void lora_step_mfma(f32x16_t (&acc)[CB], float sa, bool use, const float4 &v0,
+                                               const float4 &v1, const uint4 (&bq)[CB]) {
+    const uint32_t m = use ? ~0u : 0u;
+    const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float f0 = __uint_as_float(__float_as_uint(sa * vv[2 * e]) & m);
+        const float f1 = __uint_as_float(__float_as_uint(sa * vv[2 * e + 1]) & m);
+        hi[e] = pack_bf16x2(f0, f1);
+        lo[e] = pack_bf16x2(f0 - bf16_lo(hi[e]), f1 - bf16_hi(hi[e]));
+    }
+    const bf16x8_t ahi = __builtin_bit_cast(bf16x8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+    const bf16x8_t alo = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const bf16x8_t bb = __builtin_bit_cast(bf16x8_t, bq[cb]);
+        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bb, acc[cb], 0, 0, 0);
+        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bb, acc[cb], 0, 0, 0);
+    }
+}
+
+// The whole pass over a wavefront's RB x CB blocks.  Every block first takes
+// the adapter of its lowest row with one (the only adapter of the block in
+// segment order): the operands of KB rank steps of RG blocks are loaded
+// before any of their MFMAs, so the wavefront waits for memory once per
+// group, not once per block and step.  Rows of further adapters in a block
+// (unsorted batches) are then taken one adapter at a time.  Per block the
+// MFMAs run in the same order either way: adapters by lowest row, ranks
+// ascending.
+template <int RB, int CB, int RG = 1, int KB = 1>
 __device__ __forceinline__ void lora_pass_impl(const gemm_args &g, f32x16_t (&acc)[RB][CB],
                                                const int32_t *s_t, const int32_t *s_id, int n0,
                                                int wrow0, int wcol0, int lane) {
-    const int R = g.max_rank, RO = g.max_rank / 8, N = g.N;
+    static_assert(RB % RG == 0, "row blocks come in whole groups");
     const int half = lane >> 5;
+    int32_t my_id[RB], my_t[RB], a0[RB], ra0[RB];
+    float sa0[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const int row = wrow0 + rb * 32 + (lane & 31);
-        const int32_t my_id = s_id[row];
-        const int32_t my_t = s_t[row];
-        uint64_t pend = __ballot(my_id >= 0) & 0xffffffffull;
+        my_id[rb] = s_id[row];
+        my_t[rb] = s_t[row];
+        const uint64_t pend = __ballot(my_id[rb] >= 0) & 0xffffffffull;
+        a0[rb] = pend ? __shfl(my_id[rb], __ffsll((long long)pend) - 1, 64) : -1;
+        ra0[rb] = a0[rb] >= 0 ? g.rank[a0[rb]] : 0;
+        sa0[rb] = a0[rb] >= 0 ? g.scale[a0[rb]] : 0.0f;
+    }
+#pragma unroll
+    for (int r0 = 0; r0 < RB; r0 += RG) {
+        int nks = 0;
+#pragma unroll
+        for (int i = 0; i < RG; ++i) nks = max(nks, (ra0[r0 + i] + 15) >> 4);
+        for (int ks0 = 0; ks0 < nks; ks0 += KB) {
+            float4 v0[RG][KB], v1[RG][KB];
+            uint4 bq[RG][KB][CB];
+#pragma unroll
+            for (int i = 0; i < RG; ++i)
+#pragma unroll
+                for (int u = 0; u < KB; ++u)
+                    lora_step_load<CB>(g, a0[r0 + i], ra0[r0 + i], my_id[r0 + i] == a0[r0 + i], my_t[r0 + i],
+                                       ks0 + u, half, wcol0, lane, v0[i][u], v1[i][u], bq[i][u]);
+#pragma unroll
+            for (int i = 0; i < RG; ++i)
+#pragma unroll
+                for (int u = 0; u < KB; ++u)
+                    if (16 * (ks0 + u) < ra0[r0 + i])      // wave-uniform
+                        lora_step_mfma<CB>(acc[r0 + i], sa0[r0 + i],
+                                           my_id[r0 + i] == a0[r0 + i] && 16 * (ks0 + u) + 8 * half < ra0[r0 + i],
+                                           v0[i][u], v1[i][u], bq[i][u]);
+        }
+    }
+    // further adapters of a block, one at a time
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        uint64_t pend = __ballot(my_id[rb] >= 0 && my_id[rb] != a0[rb]) & 0xffffffffull;
         while (pend) {
             const int first = __ffsll((long long)pend) - 1;
-            const int32_t a = __shfl(my_id, first, 64);
-            pend &= ~(__ballot(my_id == a) & 0xffffffffull);
+            const int32_t a = __shfl(my_id[rb], first, 64);
+            pend &= ~(__ballot(my_id[rb] == a) & 0xffffffffull);
             const int32_t ra = g.rank[a];
             const float sa = g.scale[a];
-            const uint32_t vm = (my_id == a) ? ~0u : 0u;
-            const float *vrow = g.v + (int64_t)(my_id == a ? my_t : 0) * g.v_stride;
+            const bool mine = my_id[rb] == a;
             for (int ks = 0; ks * 16 < ra; ++ks) {
-                const int j0 = 16 * ks + 8 * half;
-                const int oct = 2 * ks + half;
-                const bool j_ok = j0 < ra;              // octets past the slot's rank: not read
-                const float *vp = vrow + (j_ok ? j0 : 0);
-                float4 v0 = *reinterpret_cast<const float4 *>(vp);
-                float4 v1 = *reinterpret_cast<const float4 *>(vp + 4);
+                float4 v0, v1;
                 uint4 bq[CB];
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    const int col = wcol0 + cb * 32 + (lane & 31);
-                    const bool ok = j_ok && col < N;
-                    bq[cb] = ldg16(g.b + ((int64_t)a * R * N + ((int64_t)(ok ? oct : 0) * N + (ok ? col : 0)) * 8));
-                    const uint32_t m = ok ? ~0u : 0u;
-                    bq[cb] = make_uint4(bq[cb].x & m, bq[cb].y & m, bq[cb].z & m, bq[cb].w & m);
-                }
-                const uint32_t m = j_ok ? vm : 0u;
-                float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-                uint32_t hi[4], lo[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float f0 = __uint_as_float(__float_as_uint(sa * vv[2 * e]) & m);
-                    const float f1 = __uint_as_float(__float_as_uint(sa * vv[2 * e + 1]) & m);
-                    const uint32_t h0 = f32_to_bf16_bits(f0), h1 = f32_to_bf16_bits(f1);
-                    hi[e] = h0 | (h1 << 16);
-                    lo[e] = f32_to_bf16_bits(f0 - __uint_as_float(h0 << 16)) |
-                            (f32_to_bf16_bits(f1 - __uint_as_float(h1 << 16)) << 16);
-                }
-                const bf16x8_t ahi = __builtin_bit_cast(bf16x8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
-                const bf16x8_t alo = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    const bf16x8_t bb = __builtin_bit_cast(bf16x8_t, bq[cb]);
-                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bb, acc[rb][cb], 0, 0, 0);
-                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bb, acc[rb][cb], 0, 0, 0);
-                }
+                lora_step_load<CB>(g, a, ra, mine, my_t[rb], ks, half, wcol0, lane, v0, v1, bq);
+                lora_step_mfma<CB>(acc[rb], sa, mine && 16 * ks + 8 * half < ra, v0, v1, bq);
             }
         }
     }
@@ -252,9 +313,7 @@ __device__ __forceinline__ void lora_delta8(const uint16_t *b, int32_t id, int32
 // The partials of an element are summed in split order (deterministic).
 // With VP (fused shrink) the rows' v are first summed from the K-range rank
 // partials (in range order) into LDS, and the first column tile flags bad ids.
-// With Q8 (FP8 base) the summed partials are multiplied by the row scale and
-// then the column scale before the low-rank term is added.
-template <bool LORA, bool VP, int BM, int BN, bool Q8 = false>
+template <bool LORA, bool VP, int BM, int BN>
 __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g) {
     constexpr int RW = 2048 / BN, CPR = BN / 8, CHUNKS = BM / RW;
     const int tidx = blockIdx.x / CHUNKS, chunk = blockIdx.x % CHUNKS;
@@ -295,15 +354,6 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g) {
         const float4 b = *reinterpret_cast<const float4 *>(src + 4);
         o[0] += a.x; o[1] += a.y; o[2] += a.z; o[3] += a.w;
         o[4] += b.x; o[5] += b.y; o[6] += b.z; o[7] += b.w;
-    }
-    if (Q8) {
-        // FP8 base: the partials are sums of code products; scale by row and column
-        const float sx = g.xs[t];
-        const float4 w0 = *reinterpret_cast<const float4 *>(g.wsc + n);
-        const float4 w1 = *reinterpret_cast<const float4 *>(g.wsc + n + 4);
-        const float sw[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-        for (int q = 0; q < 8; ++q) o[q] = (o[q] * sx) * sw[q];
     }
     if (LORA) {
         const int32_t raw = g.ids[t];

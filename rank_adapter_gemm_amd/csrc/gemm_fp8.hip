@@ -5,27 +5,30 @@
 // adapter's contribution is added to the base product's accumulator, never
 // merged into the packed 8-bit weights ("Multi-LoRA Serving 与 Adapter 隔离",
 // section on numerics and mixed precision).  The pages fix no scheme; this
-// library uses OCP E4M3 codes with one fp32 scale per token row of x and one
-// per output column of W:
-//   scale = amax / 448, code = E4M3(clamp(v * (448 / amax), -448, 448)),
-// both divisions correctly rounded fp32, the product fp32, the conversion
-// round-to-nearest-even (v_cvt_pk_fp8_f32); an all-zero row or column gets
-// scale 0 and zero codes.  Inputs must be finite.
+// library uses OCP E4M3 codes with one power-of-two scale per token row of x
+// and one per output column of W:
+//   scale = 2^e, e the smallest integer with amax <= 448 * 2^e (clamped to
+//   [-127, 127]), code = E4M3(v * 2^-e) (an exact scaling; round to nearest
+//   even, v_cvt_pk_fp8_f32).  An all-zero row or column gets e = -127 and
+//   zero codes.  Inputs must be finite.
+// Powers of two are what the matrix cores' E8M0 block scales express, so the
+// scales are applied inside the product and the accumulator holds y's base
+// part directly.
 //
-// GEMM (gfx950, v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales,
-// fp32 accumulate):
+// GEMM (gfx950, v_mfma_scale_f32_32x32x64_f8f6f4, fp32 accumulate):
 //   * x codes are [T][K] and W codes [N][K] (K-contiguous, "NT"), so both
 //     tiles are rows of K bytes: one DMA plan, one XOR swizzle and
 //     ds_read_b128 fragment reads for both operands (no transposing reads).
 //   * BM x BN tile, K step 128 codes, NS LDS stages, the same tile order,
-//     split-K plan, DMA and stage hand-off as the bf16 kernel.
-//   * Epilogue: acc * s_x[t] * s_w[n] in fp32, then the low-rank term on MFMA
-//     (bf16 B, v split in high and low bf16 parts), one rounding to bf16.
-//     Split-K pieces write unscaled fp32 partials; the reduction scales them
-//     and adds the low-rank term.
-// Operand layout of the MFMA per lane l: A = row (l % 32), 32 consecutive k
-// starting at 32 (l / 32); B = column (l % 32), the same k; C as for the bf16
-// 32x32 MFMAs.
+//     split-K plan, DMA, stage hand-off, fused expand (before the K loop,
+//     while the first stages load) and tile store as the bf16 kernel; split-K
+//     pieces write fp32 partials that the bf16 reduction finishes.
+// MFMA lane mapping (checked on the GPU): lane l holds 32 codes of row (A) or
+// column (B) l % 32, the same k positions for both operands, so a lane may
+// take any 32 codes of its row as long as both operands agree; the E8M0
+// scale operand of lane l applies to row (column) l % 32 in K-block l / 32 --
+// with one scale per row and column, lanes l and l + 32 pass the same one.
+// The output layout is that of the bf16 32x32 MFMAs.
 #include "gemm_common.hpp"
 
 namespace lora {
@@ -37,6 +40,26 @@ constexpr float kE4M3Max = 448.0f;
 // ---------------------------------------------------------------------------
 // Quantizers
 // ---------------------------------------------------------------------------
+
+// Exponent of the power-of-two scale of a row or column whose largest
+// magnitude is amax (>= 0, finite): the smallest e with amax <= 448 * 2^e,
+// clamped to [-127, 127].  With amax = m 2^E (1 <= m < 2) and 448 = 1.75 2^8:
+// e = E - 8 if m <= 1.75, else E - 7; zero and subnormal amax give -127.
+__device__ __forceinline__ int scale_exp(float amax) {
+    const uint32_t u = __float_as_uint(amax);
+    const int field = (int)(u >> 23);
+    if (field == 0) return -127;
+    const int e = field - 135 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0);
+    return e < -127 ? -127 : e;
+}
+
+// 2^e as an fp32 value, exactly, for e in [-127, 127] (2^-127 is subnormal).
+__device__ __forceinline__ float exp2i(int e) {
+    return e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// E8M0 code (biased exponent) of a power-of-two scale 2^e, e in [-127, 127].
+__device__ __forceinline__ int e8m0_of(float s) { return (int)((__float_as_uint(s) >> 23) & 0xffu); }
 
 // Four fp32 values (already scaled) to four E4M3 codes, byte i = value i.
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
@@ -58,7 +81,7 @@ __device__ __forceinline__ float block_max256(float m, float *red) {
 }
 
 // One token row per workgroup: amax over the row, then the codes (second
-// read of the row, from cache).  x bf16 [T][K], K % 16 == 0.
+// read of the row, from cache).  x bf16 [T][K], K % 16 == 0; xs[t] = 2^e.
 __global__ void __launch_bounds__(256) k_quant_rows_fp8(const uint16_t *x, int32_t K, uint8_t *xq, float *xs) {
     __shared__ float red[4];
     const int64_t t = blockIdx.x;
@@ -71,9 +94,9 @@ __global__ void __launch_bounds__(256) k_quant_rows_fp8(const uint16_t *x, int32
 #pragma unroll
         for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
     }
-    const float amax = block_max256(m, red);
-    const float inv = amax > 0.0f ? kE4M3Max / amax : 0.0f;
-    if (threadIdx.x == 0) xs[t] = amax / kE4M3Max;
+    const int e = scale_exp(block_max256(m, red));
+    const float inv = exp2i(-e);
+    if (threadIdx.x == 0) xs[t] = exp2i(e);
     uint8_t *out = xq + t * K;
     for (int c = threadIdx.x; c < nch; c += 256) {
         float f[8];
@@ -114,8 +137,9 @@ __global__ void __launch_bounds__(256) k_quant_cols_fp8(const uint16_t *W, int32
     if (tid < 32) {
         float m = 0.0f;
         for (int k = 0; k < 64; ++k) m = fmaxf(m, red[k][tid]);
-        s_inv[tid] = m > 0.0f ? kE4M3Max / m : 0.0f;
-        if (n0 + tid < N) wsc[n0 + tid] = m / kE4M3Max;
+        const int e = scale_exp(m);
+        s_inv[tid] = exp2i(-e);
+        if (n0 + tid < N) wsc[n0 + tid] = exp2i(e);
     }
     __syncthreads();
     // pass 2: tiles of 128 k x 32 columns
@@ -252,19 +276,21 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_fp8(gemm_args g) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) b[cb] = frag(wsm, wn * WN + cb * 32 + fr, ks);
     };
+    // per-lane E8M0 scale operands: the row of each A block, the column of each B block
+    int esa[RB], esb[CB];
     auto mfmas = [&](const i32x8_t *a, const i32x8_t *b, int rb0, int rb1) {
 #pragma unroll
         for (int rb = rb0; rb < rb1; ++rb)
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb)
                 acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[rb], b[cb], acc[rb][cb], 0, 0, 0,
-                                                                              127, 0, 127);
+                                                                              esa[rb], 0, esb[cb]);
     };
     constexpr int NREAD = 2 * (RB + CB);                // LDS reads per k-substep
 
-    // Per-row metadata: token row, usable adapter slot or -1, row scale.
-    __shared__ int32_t s_meta_t[BM], s_meta_id[BM];
-    __shared__ __attribute__((aligned(16))) float s_sx[BM];
+    // Per-row metadata: token row, usable adapter slot or -1, E8M0 code of
+    // the row scale (1.0 for rows past T).
+    __shared__ int32_t s_meta_t[BM], s_meta_id[BM], s_esx[BM];
     for (int i = tid; i < BM; i += WV * 64) {
         const int p = m0 + i;
         const int32_t t = (p < T) ? perm_row(g.perm, p, T) : -1;
@@ -275,7 +301,7 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_fp8(gemm_args g) {
         }
         s_meta_t[i] = t;
         s_meta_id[i] = id;
-        s_sx[i] = (!SPLIT && t >= 0) ? g.xs[t] : 0.0f;
+        s_esx[i] = t >= 0 ? e8m0_of(g.xs[t]) : 127;
     }
 
     const int nk = (k_end - k_begin + BK - 1) / BK;
@@ -287,9 +313,22 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_fp8(gemm_args g) {
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
 #pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const int col = n0 + wn * WN + cb * 32 + fr;
+        esb[cb] = col < N ? e8m0_of(g.wsc[col]) : 127;
+    }
+#pragma unroll
     for (int st = 0; st < NS; ++st)
         if (st < nk) dma_stage(st, st);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // metadata stores visible after the barrier
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) esa[rb] = s_esx[wm * WM + rb * 32 + fr];
+    // The low-rank term goes into the accumulators before the K loop, while
+    // the first stages load (split-K tiles leave it to the reduction).
+    if (LORA && !SPLIT)
+        lora_pass_impl<RB, CB, (RB >= 4 ? RB : 1), 1>(g, acc, s_meta_t, s_meta_id, n0, wm * WM, n0 + wn * WN, lane);
     wait_stage(min(NS - 1, nk - 1));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -326,30 +365,6 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_fp8(gemm_args g) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    if (!SPLIT) {
-        // acc[i][n] = (acc * s_x[row]) * s_w[col]: lane's column is fixed per
-        // block, its rows 8 (e / 4) + 4 (l / 32) + e % 4 come as float4s.
-        float swv[CB];
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            const int col = n0 + wn * WN + cb * 32 + fr;
-            swv[cb] = col < N ? g.wsc[col] : 0.0f;
-        }
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            const int rbase = wm * WM + rb * 32 + 4 * fh;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float4 s4 = *reinterpret_cast<const float4 *>(s_sx + rbase + 8 * j);
-                const float sr[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int cb = 0; cb < CB; ++cb) acc[rb][cb][4 * j + i] = (acc[rb][cb][4 * j + i] * sr[i]) * swv[cb];
-            }
-        }
-        if (LORA) lora_pass_impl<RB, CB>(g, acc, s_meta_t, s_meta_id, n0, wm * WM, n0 + wn * WN, lane);
-    }
     gemm_store_tile<BM, BN, WV, WR, SPLIT>(g, acc, reinterpret_cast<float *>(smem), s_meta_t, n0, w, lane,
                                          tidx, split);
 }
@@ -375,9 +390,9 @@ static void launch_fp8_cfg(gemm_args g, const gemm_plan &pl, bool lora, hipStrea
                            0, s, g);
         const dim3 rgrid(pl.tail * (BM / (2048 / BN)));
         if (lora)
-            hipLaunchKernelGGL((k_splitk_reduce<true, false, BM, BN, true>), rgrid, dim3(256), 0, s, g);
+            hipLaunchKernelGGL((k_splitk_reduce<true, false, BM, BN>), rgrid, dim3(256), 0, s, g);
         else
-            hipLaunchKernelGGL((k_splitk_reduce<false, false, BM, BN, true>), rgrid, dim3(256), 0, s, g);
+            hipLaunchKernelGGL((k_splitk_reduce<false, false, BM, BN>), rgrid, dim3(256), 0, s, g);
     }
 }
 

@@ -7,10 +7,11 @@
   each tie.
 * The encoder agrees with a brute-force nearest-value search over the code
   table (ties to the even code) written here.
-* The quantizer maps each row's largest magnitude to +-448 exactly, gives
-  scale 0 and zero codes for a zero row, is invariant under power-of-two
-  scaling of a row (codes unchanged, scale scaled), and its round trip stays
-  within the format's half-step bound.
+* The scale exponent is the smallest e with amax <= 448 * 2^e (checked
+  against a brute-force search over e); the quantizer maps each row's
+  largest magnitude into (224, 448], gives zero codes to a zero row, is
+  invariant under power-of-two scaling of a row (codes unchanged, scale
+  scaled), and its round trip stays within the format's half-step bound.
 * On inputs that lie on the E4M3 grid times a power of two per row and per
   column (so the quantization is lossless), the FP8 layer must equal the
   plain fp64 layer of the bf16 oracle -- base product and low-rank term --
@@ -23,7 +24,7 @@ import torch
 
 from oracle import BF16, bf16_bits_from_f32, f32_from_bf16_bits, lora_scale, oracle_rows
 from oracle.fp8 import (E4M3_MAX, e4m3_decode, e4m3_encode, oracle_fp8_base, oracle_fp8_rows,
-                        quantize_rows_e4m3, quantize_weight_e4m3)
+                        quantize_rows_e4m3, quantize_weight_e4m3, scale_exponent)
 
 ALL = np.arange(256, dtype=np.uint8)
 
@@ -93,6 +94,20 @@ def test_encode_rejects_out_of_range():
         e4m3_encode(np.array([np.nan]))
 
 
+def test_scale_exponent_is_the_smallest_power():
+    rng = np.random.default_rng(5)
+    amax = np.concatenate([np.exp2(rng.uniform(-140, 120, 5000)), [448.0, 449.0, 224.0, 224.0001, 447.9999,
+                           1.75, 1.7500001, 2.0 ** -130, 3.0e38, 1.0]]).astype(np.float32).astype(np.float64)
+    e = scale_exponent(amax)
+    for a, k in zip(amax, e):
+        if a < 448.0 * 2.0 ** -127:
+            assert k == -127
+            continue
+        assert a <= 448.0 * 2.0 ** k and (k == -127 or a > 448.0 * 2.0 ** (k - 1)), (a, k)
+    assert scale_exponent(np.array([0.0]))[0] == -127
+    assert list(scale_exponent(np.array([448.0, 449.0, 224.0, 1.0]))) == [0, 1, -1, -8]
+
+
 def test_quantize_rows_properties():
     rng = np.random.default_rng(2)
     a = (rng.normal(size=(64, 300)) * np.exp2(rng.integers(-20, 20, size=(64, 1)))).astype(np.float32)
@@ -100,22 +115,23 @@ def test_quantize_rows_properties():
     a[6] = -0.0
     codes, scale = quantize_rows_e4m3(a)
     assert codes.shape == a.shape and scale.dtype == np.float32
-    assert scale[5] == 0 and scale[6] == 0 and not codes[5].any() and np.all(codes[6] == 0x80)
-    live = scale > 0
-    # the largest magnitude of every row maps to +-448 (code 0x7e / 0xfe)
+    assert not codes[5].any() and np.all(codes[6] == 0x80)
+    live = np.abs(a).max(axis=1) > 0
+    # scales are powers of two; the largest magnitude of a row lands in (224, 448]
+    m, _ = np.frexp(scale.astype(np.float64))
+    assert np.all(m == 0.5)
     am = np.argmax(np.abs(a), axis=1)
-    top = codes[np.arange(64), am]
-    assert np.all(((top & 0x7F) == 0x7E)[live])
-    # scale is amax / 448 in float32
-    assert np.array_equal(scale, (np.abs(a).max(axis=1) / np.float32(448)).astype(np.float32))
+    top = np.abs(a[np.arange(64), am].astype(np.float64)) / scale
+    assert np.all(((top > 224) & (top <= 448))[live])
     # power-of-two invariance (no overflow or underflow at these magnitudes)
     c2, s2 = quantize_rows_e4m3(a * np.float32(2.0 ** 7))
-    assert np.array_equal(c2, codes) and np.array_equal(s2, scale * np.float32(2.0 ** 7))
+    assert np.array_equal(c2, codes) and np.array_equal(s2[live], scale[live] * np.float32(2.0 ** 7))
+    assert s2[5] == scale[5] == np.float32(2.0 ** -127)       # zero rows keep the smallest scale
     # round trip: within half a step of the format (relative 2^-4 for normals,
-    # 2^-10 of the scale in the subnormal range), plus the fp32 scaling error
+    # 2^-10 of the scale in the subnormal range)
     back = e4m3_decode(codes) * scale[:, None].astype(np.float64)
     err = np.abs(back - a)
-    bound = np.maximum(2.0 ** -4 * np.abs(a), 2.0 ** -10 * scale[:, None]) * (1 + 2.0 ** -20)
+    bound = np.maximum(2.0 ** -4 * np.abs(a), 2.0 ** -10 * scale[:, None])
     assert np.all((err <= bound)[live])
 
 
