@@ -79,6 +79,24 @@ template <> struct vec16<LORA_F32> {
 __device__ __forceinline__ uint4 ldg16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ void stg16(void *p, const uint4 &v) { *reinterpret_cast<uint4 *>(p) = v; }
 
+// A 16-byte zero vector in global memory: the source of the DMA loads of
+// masked lanes (rows past T, k past K, columns past N), so those LDS slots
+// hold zeros.
+static __device__ __attribute__((aligned(16))) uint4 g_zero16[1];
+
+
+// One 16-byte-per-lane DMA load from global memory straight into LDS: lane
+// l's bytes land at lds_wave_base + 16 l (gfx950 global_load_lds_dwordx4).
+// Issued as inline assembly so the compiler does not add its own
+// conservative vmcnt waits before later LDS reads; the kernel orders these
+// loads itself with explicit s_waitcnt vmcnt before each barrier.
+__device__ __forceinline__ void dma16(const void *gptr, const void *lds_wave_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_wave_base)));
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0)
+                 : "memory", "m0");
+}
+
 // Row visited at sorted position p: identity without perm; a perm entry
 // outside [0, T) (segments not built for this batch) yields -1 = skip.
 __device__ __forceinline__ int32_t perm_row(const int32_t *perm, int32_t p, int32_t T) {

@@ -63,26 +63,9 @@ __device__ __forceinline__ void tile_of(int b, int total, const gemm_args &g, in
     grouped_tile(g.tile_base + tidx, g.n_tiles_m, g.n_tiles_n, tm, tn);
 }
 
-// A 16-byte zero vector in global memory: the source of the DMA loads of
-// masked lanes (rows past T, k past K, columns past N), so those LDS slots
-// hold zeros.
-static __device__ __attribute__((aligned(16))) uint4 g_zero16[1];
-
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
-
-// One 16-byte-per-lane DMA load from global memory straight into LDS: lane
-// l's bytes land at lds_wave_base + 16 l (gfx950 global_load_lds_dwordx4).
-// Issued as inline assembly so the compiler does not add its own
-// conservative vmcnt waits before later LDS reads; the kernel orders these
-// loads itself with explicit s_waitcnt vmcnt before each barrier.
-__device__ __forceinline__ void dma16(const void *gptr, const void *lds_wave_base) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_wave_base)));
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0)
-                 : "memory", "m0");
-}
 
 // XOR swizzles of the 16-byte chunk index inside an LDS row: conflict-free
 // fragment reads for 32 and for 64 LDS banks.

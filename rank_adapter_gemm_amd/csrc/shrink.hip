@@ -159,17 +159,37 @@ __global__ void __launch_bounds__(512) k_shrink_rows(const typename elem<DT>::T 
 // SGMV shrink, bf16: a grouped product over adapter segments.
 //   Work block w (grid.x) covers up to kShrinkRows consecutive sorted rows of
 //   ONE segment (the block table comes from the segment builder); grid.y
-//   splits K.  The 4 wavefronts take interleaved 32-wide k steps, batching the
-//   loads of U steps before the MFMAs (v_mfma_f32_16x16x32_bf16, fp32
-//   accumulate), and reduce in LDS in a fixed order.  Rows of a segment share
-//   one adapter, so its A^T rows are read once per block (L1/L2 hits across
-//   waves).  Extra workgroups past the work blocks write the zero v rows of
-//   the base-only block (and of bad ids) so every row of v is defined.
+//   splits K.  Rows of a segment share one adapter, so the block is a small
+//   GEMM: its x rows (gathered through perm) times the adapter's A^T rows.
+//   Both operands are K-contiguous rows, so they go global -> LDS by DMA
+//   (global_load_lds, whole 16-byte chunks of a row per lane: full cache
+//   lines), NS stages of 128 k (NS - 1 in flight), stored with an XOR swizzle of the
+//   16-byte chunk index by row (conflict-free fragment reads); masked rows,
+//   ranks past the slot's and k past the range load the zero vector.  Each of
+//   the 4 wavefronts takes one 32-k quarter of every stage
+//   (v_mfma_f32_16x16x32_bf16, fp32 accumulate), and the 4 partial sums are
+//   added in LDS in a fixed order.  Extra workgroups past the work blocks
+//   write the zero v rows of the base-only block (and of bad ids) so every
+//   row of v is defined.
 //   Operand mapping per lane l: A operand = x row (l % 16) of a 16-row block,
 //   8 consecutive k of k-group (l / 16); B operand = A^T row (rank) (l % 16) of
 //   a 16-rank chunk, the same 8 k.  Output: rank (l % 16), rows 4 (l / 16) + q.
 // ---------------------------------------------------------------------------
-template <int RCH>   // 16-rank chunks
+template <int RCH, int NS_> struct shrink_cfg {
+    static constexpr int BR = kShrinkRows;               // rows per work block
+    static constexpr int NR = RCH * 16;                  // rank columns
+    static constexpr int BK = 128;                       // k per stage
+    static constexpr int CH = BK / 8;                    // 16-byte chunks per LDS row
+    static constexpr int XST = BR * BK, AST = NR * BK;   // elements per stage
+    static constexpr int STAGE = XST + AST;
+    static constexpr int NS = NS_;                       // stages in LDS
+    static constexpr int XI = BR * CH / 256, AI = NR * CH / 256;   // DMA instructions per wave per stage
+    static constexpr int RED = 4 * BR * (NR + 1);        // fp32 reduction buffer
+    static constexpr int LDS_BYTES = NS * STAGE * 2 > RED * 4 ? NS * STAGE * 2 : RED * 4;
+    static_assert(XI * 256 == BR * CH && AI * 256 == NR * CH, "DMA plan must cover the stage");
+};
+
+template <int RCH, int NS_>   // 16-rank chunks, LDS stages
 __global__ void __launch_bounds__(256) k_shrink_grouped(
     const uint16_t *__restrict__ x, int32_t T, int32_t d_in, slice_set ss, int32_t max_rank,
     const int32_t *__restrict__ perm, const int32_t *__restrict__ offsets,
@@ -178,10 +198,11 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
     const int32_t *__restrict__ blk_start, const int32_t *__restrict__ blk_seg,
     int32_t n_work_upper, int32_t k_chunk,
     float *__restrict__ v, float *__restrict__ partial, int32_t *err) {
-    constexpr int BR = kShrinkRows;                      // rows per work block
+    typedef shrink_cfg<RCH, NS_> C;
+    constexpr int BR = C::BR, NR = C::NR, BK = C::BK, CH = C::CH, XST = C::XST, STAGE = C::STAGE;
+    constexpr int NS = C::NS, XI = C::XI, AI = C::AI, PER = XI + AI;
     constexpr int RBN = BR / 16;                         // 16-row MFMA blocks
-    constexpr int U = RCH <= 2 ? 4 : 2;                  // k steps per batch of loads
-    __shared__ float s_acc[4][BR][RCH * 16 + 1];
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[C::LDS_BYTES / 2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wid = blockIdx.x;
     const int VS = ss.n * max_rank;                      // v row stride: all slices
@@ -214,77 +235,100 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
     const int k_begin = blockIdx.y * k_chunk;
     const int k_end = min(d_in, k_begin + k_chunk);
 
-    const int lr = lane & 15, kg = lane >> 4;
-    // this lane's x row in each 16-row block; invalid rows read the block's
-    // first row and are zeroed
-    const int32_t t_first = perm_row(perm, p0, T);
-    int64_t xoff[RBN];
-    uint32_t xm[RBN];                                    // all-ones for a real row, else 0
+    // DMA plan: chunk c = (w * I + j) * 64 + lane of a stage sits at LDS row
+    // c / CH, slot c % CH, and holds the row's chunk slot ^ (row % CH).
+    int64_t xrow[XI];
+    const uint16_t *arow[AI];                            // the rank's A^T row, or null (zero rank)
+    int xcol[XI], acol[AI];
 #pragma unroll
-    for (int rb = 0; rb < RBN; ++rb) {
-        const int p = p0 + rb * 16 + lr;
-        const int32_t t = (p < pend) ? perm_row(perm, p, T) : -1;
-        xm[rb] = t >= 0 ? ~0u : 0u;
-        xoff[rb] = (int64_t)(t >= 0 ? t : (t_first >= 0 ? t_first : 0)) * d_in;
+    for (int j = 0; j < XI; ++j) {
+        const int c = (wave * XI + j) * 64 + lane;
+        const int r = c / CH, slot = c % CH;
+        const int p = p0 + r;
+        const int32_t t = p < pend ? perm_row(perm, p, T) : -1;
+        xrow[j] = t >= 0 ? (int64_t)t * d_in : -1;
+        xcol[j] = 8 * (slot ^ (r % CH));
     }
-    // rank column j of the concatenated slices: slice j / max_rank, rank j % max_rank
-    const uint16_t *aptr[RCH];
-    uint32_t am[RCH];                                    // all-ones for a rank below the slice's r
 #pragma unroll
-    for (int rc = 0; rc < RCH; ++rc) {
-        const int j = rc * 16 + lr;
-        const int sl = j / max_rank, jj = j - sl * max_rank;
+    for (int j = 0; j < AI; ++j) {
+        const int c = (wave * AI + j) * 64 + lane;
+        const int r = c / CH, slot = c % CH;
+        // rank column r of the concatenated slices: slice r / max_rank
+        const int sl = r / max_rank, jj = r - sl * max_rank;
         const int32_t rs = sl < ss.n ? ss.rank[sl][aid] : 0;
-        am[rc] = jj < rs ? ~0u : 0u;
-        aptr[rc] = reinterpret_cast<const uint16_t *>(ss.a[sl < ss.n ? sl : 0]) +
-                   ((size_t)aid * max_rank + (rs > 0 ? min(jj, rs - 1) : 0)) * d_in;
+        arow[j] = jj < rs ? reinterpret_cast<const uint16_t *>(ss.a[sl]) + ((int64_t)aid * max_rank + jj) * d_in
+                          : nullptr;
+        acol[j] = 8 * (slot ^ (r % CH));
     }
+    auto dma_stage = [&](int kt, int buf) {
+        uint16_t *xs = smem + buf * STAGE;
+        uint16_t *as = xs + XST;
+        const int k0 = k_begin + kt * BK;
+#pragma unroll
+        for (int j = 0; j < XI; ++j) {
+            const int kk = k0 + xcol[j];
+            const void *src = (xrow[j] >= 0 && kk < k_end) ? (const void *)(x + xrow[j] + kk) : (const void *)g_zero16;
+            dma16(src, xs + (wave * XI + j) * 64 * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < AI; ++j) {
+            const int kk = k0 + acol[j];
+            const void *src = (arow[j] && kk < k_end) ? (const void *)(arow[j] + kk) : (const void *)g_zero16;
+            dma16(src, as + (wave * AI + j) * 64 * 8);
+        }
+    };
+    auto wait_stage = [&](int ahead) {                    // stages issued after the awaited one
+        if (ahead >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PER) : "memory");
+        else if (ahead == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory");
+        else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+
     f32x4_t acc[RBN][RCH];
 #pragma unroll
     for (int rb = 0; rb < RBN; ++rb)
 #pragma unroll
         for (int rc = 0; rc < RCH; ++rc) acc[rb][rc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    if (any_rank) {
-        for (int kb = k_begin + wave * 32; kb < k_end; kb += 4 * 32 * U) {
-            uint4 xq[U][RBN], aq[U][RCH];
-            uint32_t km[U];
+    const int lr = lane & 15, kg = lane >> 4;
+    const int nk = any_rank ? (k_end - k_begin + BK - 1) / BK : 0;
+    // NS - 1 stages ahead; iteration kt waits for stage kt, then (after the
+    // barrier, when every wave is done with stage kt - 1) refills that buffer
+    // with stage kt + NS - 1 and computes stage kt.
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int k = kb + u * 128 + 8 * kg;
-                km[u] = k < k_end ? ~0u : 0u;
-                const int kc = k < k_end ? k : k_begin;
+    for (int st = 0; st < NS - 1; ++st)
+        if (st < nk) dma_stage(st, st);
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_stage(min(NS - 2, nk - 1 - kt));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (kt + NS - 1 < nk) dma_stage(kt + NS - 1, (kt + NS - 1) % NS);
+        const uint16_t *xs = smem + (kt % NS) * STAGE;
+        const uint16_t *as = xs + XST;
+        const int c = 4 * wave + kg;                     // this lane's logical chunk
+        uint4 xq[RBN], aq[RCH];
 #pragma unroll
-                for (int rb = 0; rb < RBN; ++rb) xq[u][rb] = ldg16(x + xoff[rb] + kc);
-#pragma unroll
-                for (int rc = 0; rc < RCH; ++rc) aq[u][rc] = ldg16(aptr[rc] + kc);
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-#pragma unroll
-                for (int rb = 0; rb < RBN; ++rb) {
-                    const uint32_t m = km[u] & xm[rb];
-                    xq[u][rb] = make_uint4(xq[u][rb].x & m, xq[u][rb].y & m, xq[u][rb].z & m, xq[u][rb].w & m);
-                }
-#pragma unroll
-                for (int rc = 0; rc < RCH; ++rc) {
-                    const uint32_t m = km[u] & am[rc];
-                    aq[u][rc] = make_uint4(aq[u][rc].x & m, aq[u][rc].y & m, aq[u][rc].z & m, aq[u][rc].w & m);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int rb = 0; rb < RBN; ++rb)
-#pragma unroll
-                    for (int rc = 0; rc < RCH; ++rc)
-                        acc[rb][rc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, xq[u][rb]),
-                            __builtin_bit_cast(bf16x8_t, aq[u][rc]), acc[rb][rc], 0, 0, 0);
+        for (int rb = 0; rb < RBN; ++rb) {
+            const int r = rb * 16 + lr;
+            xq[rb] = *reinterpret_cast<const uint4 *>(xs + r * BK + 8 * (c ^ (r % CH)));
         }
+#pragma unroll
+        for (int rc = 0; rc < RCH; ++rc) {
+            const int r = rc * 16 + lr;
+            aq[rc] = *reinterpret_cast<const uint4 *>(as + r * BK + 8 * (c ^ (r % CH)));
+        }
+#pragma unroll
+        for (int rb = 0; rb < RBN; ++rb)
+#pragma unroll
+            for (int rc = 0; rc < RCH; ++rc)
+                acc[rb][rc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, xq[rb]), __builtin_bit_cast(bf16x8_t, aq[rc]), acc[rb][rc], 0, 0, 0);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (any_empty && blockIdx.y == 0 && tid < BR && p0 + tid < pend)
         flag_bad_row(err, perm_row(perm, p0 + tid, T));     // segment of an empty slot
+    __syncthreads();                                     // all waves done with the stages
+    float (*s_acc)[BR][NR + 1] = reinterpret_cast<float (*)[BR][NR + 1]>(smem);
 #pragma unroll
     for (int rb = 0; rb < RBN; ++rb)
 #pragma unroll
@@ -297,7 +341,7 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
         const int p = p0 + i;
         if (p >= pend) continue;
         float sum = 0.0f;
-        if (j < RCH * 16) sum = (s_acc[0][i][j] + s_acc[1][i][j]) + (s_acc[2][i][j] + s_acc[3][i][j]);
+        if (j < NR) sum = (s_acc[0][i][j] + s_acc[1][i][j]) + (s_acc[2][i][j] + s_acc[3][i][j]);
         if (partial) {
             partial[((size_t)blockIdx.y * T + p) * VS + j] = sum;
         } else {
@@ -378,21 +422,25 @@ lora_status_t launch_shrink(const void *x, int32_t T, const lora_pool_t *pools, 
     const int rc = (VS + 15) / 16;
     const int32_t *offsets = ws_ptr<int32_t>(ws, L.offsets);
     const dim3 grid(n_work_upper + row_blocks, split);
-#define LORA_SHRINK_GROUPED(RCV)                                                                  \
-    hipLaunchKernelGGL((k_shrink_grouped<RCV>), grid, dim3(256), 0, s, xe, T, p.d_in, ss,         \
+    // Stages: 3 for narrow rank sets streaming long K ranges (more bytes in
+    // flight per workgroup), else 2 (more workgroups resident per CU, which
+    // serves short K ranges and wide rank sets better).
+    const bool deep = rc <= 2 && k_chunk >= 8 * 128;
+#define LORA_SHRINK_GROUPED(RCV, NSV)                                                             \
+    hipLaunchKernelGGL((k_shrink_grouped<RCV, NSV>), grid, dim3(256), 0, s, xe, T, p.d_in, ss,    \
                        p.max_rank, perm, offsets, ws_ptr<int32_t>(ws, L.seg_id),                  \
                        ws_ptr<int32_t>(ws, L.seg_start), ws_ptr<int32_t>(ws, L.n_seg),            \
                        ws_ptr<int32_t>(ws, L.blk_start), ws_ptr<int32_t>(ws, L.blk_seg),          \
                        n_work_upper, k_chunk, v, partial, err)
     switch (rc) {
-        case 1: LORA_SHRINK_GROUPED(1); break;
-        case 2: LORA_SHRINK_GROUPED(2); break;
-        case 3: LORA_SHRINK_GROUPED(3); break;
-        case 4: LORA_SHRINK_GROUPED(4); break;
-        case 5: LORA_SHRINK_GROUPED(5); break;
-        case 6: LORA_SHRINK_GROUPED(6); break;
-        case 7: LORA_SHRINK_GROUPED(7); break;
-        default: LORA_SHRINK_GROUPED(8); break;
+        case 1: if (deep) LORA_SHRINK_GROUPED(1, 3); else LORA_SHRINK_GROUPED(1, 2); break;
+        case 2: if (deep) LORA_SHRINK_GROUPED(2, 3); else LORA_SHRINK_GROUPED(2, 2); break;
+        case 3: LORA_SHRINK_GROUPED(3, 2); break;
+        case 4: LORA_SHRINK_GROUPED(4, 2); break;
+        case 5: LORA_SHRINK_GROUPED(5, 2); break;
+        case 6: LORA_SHRINK_GROUPED(6, 2); break;
+        case 7: LORA_SHRINK_GROUPED(7, 2); break;
+        default: LORA_SHRINK_GROUPED(8, 2); break;
     }
 #undef LORA_SHRINK_GROUPED
     if (split > 1) {
