@@ -208,6 +208,9 @@ FWD_SHAPES = [
     (200, 1024, 4096, 32, [32, 17, 8, 0, 32]),  # decode-sized, larger rank
     (1500, 512, 512, 16, [16, 4, 16, 12]),      # SGMV-sized (AUTO picks SGMV at T >= 1024)
     (2048, 512, 3584, 8, [8, 8, 3]),            # 256x128 whole tiles with the fused expand
+    (1, 16, 8, 8, [8, 5]),                      # the smallest shape: one row, one K step, one column octet
+    (1, 4096, 4096, 16, [16, 16, 16]),          # one decode row
+    (5, 48, 24, 128, [128, 1, 77, 0]),          # max rank 128, ragged ranks, K and N far below a tile
 ]
 
 
@@ -216,10 +219,14 @@ def test_forward_fp8_every_row(T, K, N, R, ranks):
     rng = np.random.default_rng(T)
     n = len(ranks)
     ids = rng.integers(-1, n, size=T).astype(np.int32)
-    ids[[3, 7]] = [-3, n]                              # out of range: flagged, base rows
+    if T > 12:
+        ids[[3, 7]] = [-3, n]                          # out of range: flagged, base rows
     empty = [s for s, r in enumerate(ranks) if r == 0]
-    if empty:
+    if empty and T > 12:
         ids[12] = empty[0]                             # an empty slot: flagged too
+    if T <= 5:                                         # tiny batches: every row on a usable adapter, in turn
+        usable = [a for a in range(n) if ranks[a] > 0]
+        ids[:] = [usable[i % len(usable)] for i in range(T)]
     bad_rows = [t for t, a in enumerate(ids) if a != -1 and not (0 <= a < n and ranks[a] > 0)]
     c = Fp8Case(T, K, N, ranks, R, seed=T + 1, ids=ids)
     rows = None if T <= 512 else np.unique(np.concatenate([np.arange(0, T, 5), np.arange(T - 64, T)]))
