@@ -314,3 +314,41 @@ def test_decode_workload_full_size_sampled():
     # the low-rank terms (the decode values make them tiny next to |y|)
     tol = 2.0 ** -8 * np.abs(ref) + 2.0 ** -8 * np.abs(lo) + fp8_bound(xq, xs, wq, wsc) + 1e-30
     assert_within(y[torch.as_tensor(rows, device="cuda")], ref, tol, "decode workload fp8")
+
+
+def test_prefill_workload_full_size_sampled():
+    """The prefill workload (32 432 rows in 64 adapter segments, 4096 -> 14336,
+    r = 32) at full size through lora_linear_forward_fp8 (SGMV), every column
+    of a bounded row sample against the oracle."""
+    wl = make_workload("prefill_sgmv", device="cuda")
+    proj = wl.projections[0]
+    x = wl.x_for(proj)
+    pool = L.AdapterPool(wl.n_slots, proj.d_in, proj.d_out, wl.max_rank, wl.dtype)
+    for s in range(wl.n_slots):
+        r = int(wl.ranks[s])
+        if r > 0:
+            pool.upload(s, proj.A[s], proj.B[s], r, float(wl.alphas[s]), lda=wl.max_rank, ldb=proj.d_out)
+    wt = L.Fp8Weight(proj.W)
+    ids_dev = torch.as_tensor(wl.ids, device="cuda")
+    ws = L.Workspace(wl.T, wl.n_slots, wl.max_rank, proj.d_out, fp8_d_in=proj.d_in)
+    y = torch.empty(wl.T, proj.d_out, dtype=wl.dtype, device="cuda")
+    L.lora_linear_forward_fp8(x, wt.codes, wt.scale, y, wl.T, pool.pool, ids_dev, L.LORA_MODE_AUTO, 0, ws.buf)
+    torch.cuda.synchronize()
+    assert L.lora_get_device_error(ws.buf) == -1
+    rows = sample_rows(wl, max_rows=64)
+    wq, wsc = quantize_weight_e4m3(f32(proj.W))
+    xq, xs = quantize_rows_e4m3(f32(x)[rows])
+    base = oracle_fp8_base(xq, xs, wq, wsc)
+    used = sorted({int(wl.ids[r]) for r in rows if wl.ids[r] >= 0})
+    A = [None] * wl.n_slots
+    B = [None] * wl.n_slots
+    for s in used:
+        A[s] = to_oracle(wl.slot_A(proj, s))
+        B[s] = to_oracle(wl.slot_B(proj, s))
+    sc = [lora_scale(float(wl.alphas[s]), int(wl.ranks[s])) for s in range(wl.n_slots)]
+    lo = oracle_rows(BF16, to_oracle(x), np.zeros((proj.d_in, proj.d_out), np.uint16), wl.ids, A, B,
+                     [int(r) for r in wl.ranks], sc, rows=rows)["y"]
+    ref = base + lo
+    # fused expand: one rounding of y; |lo| stands in for the low-rank terms' magnitude
+    tol = 2.0 ** -8 * np.abs(ref) + 2.0 ** -6 * np.abs(lo) + fp8_bound(xq, xs, wq, wsc) + 1e-30
+    assert_within(y[torch.as_tensor(rows, device="cuda")], ref, tol, "prefill workload fp8")

@@ -153,3 +153,46 @@ def test_layer_sets_sampled(name, max_rows):
         assert_parity(y[rows_dev], ref["y"], wl.dtype, "%s %s" % (name, proj.name))
         del pool
     assert L.lora_get_device_error(ws.buf) == -1
+
+
+@pytest.mark.parametrize("name,max_rows", [("layer_8b", 120), ("stress_70b", 64)])
+def test_layer_sets_sliced_as_benchmarked(name, max_rows):
+    """The layer sets at full size in the launch configuration the benchmark
+    times: projections fed by the same input (q, k, v; gate, up) go through
+    one lora_linear_forward_sliced call (at most 4 slices and 128 summed
+    ranks), the others through lora_linear_forward; segments are built by the
+    first call and reused.  Every column of a bounded row sample of every
+    projection is checked against the oracle."""
+    wl = make_workload(name, device="cuda")
+    ids = torch.as_tensor(wl.ids, device="cuda")
+    rows = sample_rows(wl, max_rows=max_rows)
+    rows_dev = torch.as_tensor(rows, device="cuda")
+    R = wl.max_rank
+    groups = []
+    for k, pr in enumerate(wl.projections):
+        if (groups and wl.projections[groups[-1][0]].x_group == pr.x_group and len(groups[-1]) < 4
+                and (len(groups[-1]) + 1) * R <= 128):
+            groups[-1].append(k)
+        else:
+            groups.append([k])
+    assert any(len(g) > 1 for g in groups)
+    ws = L.Workspace(wl.T, wl.n_slots, R, max(p.d_out for p in wl.projections),
+                     n_slices=max(len(g) for g in groups))
+    for gi, grp in enumerate(groups):
+        projs = [wl.projections[k] for k in grp]
+        pools = [build_pool(wl, p) for p in projs]
+        ys = [torch.empty(wl.T, p.d_out, dtype=wl.dtype, device="cuda") for p in projs]
+        flags = L.LORA_FLAG_SEGMENTS_READY if gi > 0 else 0
+        x = wl.x_for(projs[0])
+        if len(grp) == 1:
+            L.lora_linear_forward(x, projs[0].W, ys[0], wl.T, pools[0].pool, ids, L.LORA_MODE_AUTO, flags, ws.buf)
+        else:
+            L.lora_linear_forward_sliced(x, [p.W for p in projs], ys, wl.T, [pl.pool for pl in pools], ids,
+                                         L.LORA_MODE_AUTO, flags, ws.buf)
+        torch.cuda.synchronize()
+        for p, y in zip(projs, ys):
+            ref = oracle_for(wl, p, rows)
+            assert_parity(y[rows_dev], ref["y"], wl.dtype, "%s %s (call %s)" % (
+                name, p.name, "+".join(q.name for q in projs)))
+        del pools
+    assert L.lora_get_device_error(ws.buf) == -1
