@@ -202,7 +202,7 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
 
     const int nk = (k_end - k_begin + BK - 1) / BK;
     constexpr int PER = XI + WI + AI;                     // DMA instructions per stage per wave
-    // fused shrink: thread = (row slot i, rank j, 16-k group gq) of a stage
+    // fused shrink: thread = (row slot i, rank j, k quarter gq) of a stage
     const int sh_i = tid / (4 * R), sh_j = (tid >> 2) % R, sh_gq = tid & 3;
     const int sh_t = SH ? tn + sh_i * g.n_tiles_n : -1;
     float sh_acc = 0.0f;
@@ -212,8 +212,8 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
         const uint16_t *as = xs + XSTAGE + WSTAGE;
         const int r = sh_t - m0;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int c = 2 * sh_gq + h;
+        for (int h = 0; h < BK / 32; ++h) {                // this thread's BK / 32 chunks of 8 k
+            const int c = (BK / 32) * sh_gq + h;
             const uint4 xq = *reinterpret_cast<const uint4 *>(xs + r * BK + 8 * (c ^ swz_x<BK>(r)));
             const uint4 aq = *reinterpret_cast<const uint4 *>(as + ((sh_i * R + sh_j) * ACH + c) * 8);
             float xf[8], af[8];
@@ -223,8 +223,11 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
             for (int e = 0; e < 8; ++e) sh_acc = fmaf(xf[e], af[e], sh_acc);
         }
     };
+    static_assert(5 * PER <= 63, "vmcnt counts at most 63 loads");
     auto wait_stage = [&](int ahead) {                    // later stages still in flight
-        if (ahead >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PER) : "memory");
+        if (ahead >= 5) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 * PER) : "memory");
+        else if (ahead == 4) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * PER) : "memory");
+        else if (ahead == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PER) : "memory");
         else if (ahead == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory");
         else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
