@@ -267,28 +267,6 @@ __device__ __forceinline__ void gemm_store_tile(const gemm_args &g, f32x16_t (&a
     }
 }
 
-// s * sum_j v[j] B[j][n..n+8] for one row: G rank octets of slot `id`, 8
-// consecutive columns starting at n (B in rank octets [R/8][N][8]).
-__device__ __forceinline__ void lora_delta8(const uint16_t *b, int32_t id, int32_t R, int32_t N,
-                                            int32_t n, int32_t G, const float *vrow, float *d) {
-    for (int gg = 0; gg < G; ++gg) {
-        const uint16_t *bp = b + ((int64_t)id * R * N + ((int64_t)gg * N + n) * 8);
-        const float4 v0 = *reinterpret_cast<const float4 *>(vrow + gg * 8);
-        const float4 v1 = *reinterpret_cast<const float4 *>(vrow + gg * 8 + 4);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            float bf[8];
-            vec16<LORA_BF16>::widen(ldg16(bp + c * 8), bf);
-            float a = d[c];
-            a = fmaf(v0.x, bf[0], a); a = fmaf(v0.y, bf[1], a);
-            a = fmaf(v0.z, bf[2], a); a = fmaf(v0.w, bf[3], a);
-            a = fmaf(v1.x, bf[4], a); a = fmaf(v1.y, bf[5], a);
-            a = fmaf(v1.z, bf[6], a); a = fmaf(v1.w, bf[7], a);
-            d[c] = a;
-        }
-    }
-}
-
 // Split-K reduction over the tiles of one split launch.  A workgroup takes
 // RW = 2048 / BN rows of one tile; a thread owns 8 consecutive columns of one
 // row: y[t][n..n+8] = bf16(sum_s partial[tile][s][r][c..c+8]
@@ -299,6 +277,8 @@ __device__ __forceinline__ void lora_delta8(const uint16_t *b, int32_t id, int32
 template <bool LORA, bool VP, int BM, int BN>
 __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g) {
     constexpr int RW = 2048 / BN, CPR = BN / 8, CHUNKS = BM / RW;
+    constexpr int SP = 4;                                 // split partials loaded ahead
+    constexpr int GP = 2;                                 // rank octets of B loaded ahead
     const int tidx = blockIdx.x / CHUNKS, chunk = blockIdx.x % CHUNKS;
     int tm, tn;
     grouped_tile(g.tile_base + tidx, g.n_tiles_m, g.n_tiles_n, tm, tn);
@@ -306,6 +286,36 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g) {
     const int r = chunk * RW + threadIdx.x / CPR, c = (threadIdx.x % CPR) * 8;
     const int p = tm * BM + r, n = tn * BN + c;
     __shared__ __attribute__((aligned(16))) float s_v[VP ? RW * 64 : 1];
+    // Loads that do not depend on the rank vector go out first (the first SP
+    // splits' partials, the row's adapter and its first GP rank octets of B),
+    // so their latency overlaps the summing of the rank partials below.
+    const int32_t t = (p < T && n < N) ? perm_row(g.perm, p, T) : -1;
+    int32_t raw = -1, rk = 0;
+    if (LORA && t >= 0) {
+        raw = g.ids[t];
+        if (raw >= 0 && raw < g.n_slots) rk = g.rank[raw];
+    }
+    const int G = (rk + 7) >> 3;
+    float4 pa[SP], pb[SP];
+    uint4 bq[GP][8];
+    if (t >= 0) {
+#pragma unroll
+        for (int sidx = 0; sidx < SP; ++sidx)
+            if (sidx < g.splits) {
+                const float *src = g.partial + (((int64_t)tidx * g.splits + sidx) * BM + r) * BN + c;
+                pa[sidx] = *reinterpret_cast<const float4 *>(src);
+                pb[sidx] = *reinterpret_cast<const float4 *>(src + 4);
+            }
+        if (LORA && rk > 0) {
+#pragma unroll
+            for (int gg = 0; gg < GP; ++gg)
+                if (gg < G) {
+                    const uint16_t *bp = g.b + ((int64_t)raw * R * N + ((int64_t)gg * N + n) * 8);
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) bq[gg][q] = ldg16(bp + q * 8);
+                }
+        }
+    }
     if (VP) {
         for (int e = threadIdx.x; e < RW * R; e += 256) {
             const int rr = e / R, j = e % R;
@@ -317,8 +327,8 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g) {
                     for (int sidx = 0; sidx < g.splits; ++sidx)
                         sum += g.vpart[((int64_t)sidx * T + tt) * R + j];
                     if (j == 0 && tn == 0) {
-                        const int32_t raw = g.ids[tt];
-                        const bool ok = raw == -1 || (raw >= 0 && raw < g.n_slots && g.rank[raw] > 0);
+                        const int32_t rid = g.ids[tt];
+                        const bool ok = rid == -1 || (rid >= 0 && rid < g.n_slots && g.rank[rid] > 0);
                         if (!ok) flag_bad_row(g.err, tt);
                     }
                 }
@@ -327,30 +337,53 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g) {
         }
         __syncthreads();
     }
-    if (p >= T || n >= N) return;
-    const int32_t t = perm_row(g.perm, p, T);
     if (t < 0) return;
+    // partials summed in split order
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int sidx = 0; sidx < g.splits; ++sidx) {
-        const float *src = g.partial + (((int64_t)tidx * g.splits + sidx) * BM + r) * BN + c;
-        const float4 a = *reinterpret_cast<const float4 *>(src);
-        const float4 b = *reinterpret_cast<const float4 *>(src + 4);
+        float4 a, b;
+        if (sidx < SP) {
+            a = pa[sidx];
+            b = pb[sidx];
+        } else {
+            const float *src = g.partial + (((int64_t)tidx * g.splits + sidx) * BM + r) * BN + c;
+            a = *reinterpret_cast<const float4 *>(src);
+            b = *reinterpret_cast<const float4 *>(src + 4);
+        }
         o[0] += a.x; o[1] += a.y; o[2] += a.z; o[3] += a.w;
         o[4] += b.x; o[5] += b.y; o[6] += b.z; o[7] += b.w;
     }
-    if (LORA) {
-        const int32_t raw = g.ids[t];
-        if (raw >= 0 && raw < g.n_slots) {
-            const int32_t rk = g.rank[raw];
-            if (rk > 0) {
-                float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                lora_delta8(g.b, raw, R, N, n, (rk + 7) >> 3,
-                            VP ? s_v + (r - chunk * RW) * R : g.v + (int64_t)t * g.v_stride, d);
-                const float sc = g.scale[raw];
+    if (LORA && rk > 0) {
+        // s * sum_j v[j] B[j][n..n+8]: rank octets in order, ranks of an octet in order
+        const float *vrow = VP ? s_v + (r - chunk * RW) * R : g.v + (int64_t)t * g.v_stride;
+        float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int gg = 0; gg < G; ++gg) {
+            const float4 v0 = *reinterpret_cast<const float4 *>(vrow + gg * 8);
+            const float4 v1 = *reinterpret_cast<const float4 *>(vrow + gg * 8 + 4);
+            const uint16_t *bp = g.b + ((int64_t)raw * R * N + ((int64_t)gg * N + n) * 8);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) o[q] = fmaf(sc, d[q], o[q]);
+            for (int q = 0; q < 8; ++q) {
+                uint4 bw;
+                if (gg < GP) {
+#pragma unroll
+                    for (int u = 0; u < GP; ++u)
+                        if (u == gg) bw = bq[u][q];
+                } else {
+                    bw = ldg16(bp + q * 8);
+                }
+                float bf[8];
+                vec16<LORA_BF16>::widen(bw, bf);
+                float a = d[q];
+                a = fmaf(v0.x, bf[0], a); a = fmaf(v0.y, bf[1], a);
+                a = fmaf(v0.z, bf[2], a); a = fmaf(v0.w, bf[3], a);
+                a = fmaf(v1.x, bf[4], a); a = fmaf(v1.y, bf[5], a);
+                a = fmaf(v1.z, bf[6], a); a = fmaf(v1.w, bf[7], a);
+                d[q] = a;
             }
         }
+        const float sc = g.scale[raw];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o[q] = fmaf(sc, d[q], o[q]);
     }
     stg16(g.y + (int64_t)t * N + n, vec16<LORA_BF16>::narrow(o));
 }
