@@ -304,8 +304,11 @@ lora_status_t lora_cache_destroy(lora_cache_t *cache);
 
 /* Register (or replace) an adapter in the host tier: host_a[p], host_b[p]
  * HOST pointers, one per pool, to lora_pack_host output of that pool's
- * shapes (page-locked memory lets the copies run asynchronously); they must
- * stay valid while the cache may copy from them.  rank <= max_rank
+ * shapes; they must stay valid, and unchanged, while the cache may copy from
+ * them.  Page-locked memory that the HIP runtime maps into the GPU's address
+ * space (hipHostMalloc, or a pinned torch tensor), 16-byte aligned, is read
+ * directly by a copy kernel on the copy stream (tens of GB/s); other memory
+ * is copied with hipMemcpyAsync.  rank <= max_rank
  * (LORA_ERR_RANK_EXCEEDS_MAX), s = alpha / rank.  Re-registering a resident
  * adapter drops its slot, so the next batch loads the new version. */
 lora_status_t lora_cache_register(lora_cache_t *cache, int32_t adapter, const void *const *host_a,

@@ -14,9 +14,14 @@
 // copy (registration drops residency).
 //
 // Registered adapters live in HOST memory already in the slot layout (see
-// lora_pack_host), so promotion is a plain asynchronous copy per buffer on
-// the caller's copy stream, overlapping compute; the slot's scale and rank
-// are written by a one-thread kernel after the copies.
+// lora_pack_host), so promotion is a plain copy per buffer on the caller's
+// copy stream, overlapping compute.  Buffers in page-locked memory that the
+// HIP runtime maps into the GPU's address space are copied by one gather
+// kernel per 32 buffers, reading them directly over the host link (an
+// asynchronous memory copy per buffer costs tens of microseconds of fixed
+// overhead, which dominates slot-sized buffers); other buffers go through
+// hipMemcpyAsync.  Scale and rank are published by one kernel per batch of
+// slots after the copies.
 #include <cstring>
 #include <new>
 #include <vector>
@@ -32,6 +37,8 @@ struct lora_cache {
         float alpha = 0.0f;
         const void *a[lora::kMaxCachePools] = {};
         const void *b[lora::kMaxCachePools] = {};
+        const void *dev_a[lora::kMaxCachePools] = {};   // device-visible address of a[p], or null
+        const void *dev_b[lora::kMaxCachePools] = {};
     };
     std::vector<adapter> adapters;
     std::vector<int32_t> slot_of;     // adapter -> slot, -1 if not resident
@@ -48,6 +55,22 @@ struct lora_cache {
 namespace {
 
 inline hipStream_t hs(lora_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+// The address at which a kernel can read host buffer p: page-locked host
+// memory that the runtime reports as mapped into the device's address
+// space, 16-byte aligned; else null (the buffer is copied by the runtime).
+const void *device_view(const void *p) {
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 15u)) return nullptr;
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+        (void)hipGetLastError();                      // pageable memory: not an error here
+        return nullptr;
+    }
+    if (at.type != hipMemoryTypeHost || !at.devicePointer) return nullptr;
+    const char *host_base = at.hostPointer ? static_cast<const char *>(at.hostPointer) : static_cast<const char *>(p);
+    const char *dev = static_cast<const char *>(at.devicePointer) + (static_cast<const char *>(p) - host_base);
+    return (reinterpret_cast<uintptr_t>(dev) & 15u) ? nullptr : dev;
+}
 
 }  // namespace
 
@@ -146,6 +169,8 @@ lora_status_t lora_cache_register(lora_cache_t *c, int32_t adapter, const void *
     for (int32_t p = 0; p < c->n_pools; ++p) {
         ad.a[p] = host_a[p];
         ad.b[p] = host_b[p];
+        ad.dev_a[p] = device_view(host_a[p]);
+        ad.dev_b[p] = device_view(host_b[p]);
     }
     // a new version of a resident adapter must not be served from the old copy
     const int32_t s = c->slot_of[adapter];
@@ -210,25 +235,49 @@ lora_status_t lora_cache_map(lora_cache_t *c, const int32_t *adapters, int32_t n
     for (int32_t i = 0; i < n; ++i) slots[i] = adapters[i] == -1 ? -1 : c->slot_of[adapters[i]];
     if (c->n_pools == 0 || uploads.empty()) return LORA_OK;
 
-    // device side: wait for the victims' last uses, then every copy (one
-    // run of DMA work), then one kernel per kMetaBatch slots that publishes
-    // scale and rank in all pools
+    // device side: wait for the victims' last uses, then every copy (gather
+    // kernels over mapped host memory, runtime copies for the rest), then one
+    // kernel per kMetaBatch slots that publishes scale and rank in all pools
     const hipStream_t cs = hs(copy), ks = hs(compute);
     const size_t eb = c->pools[0].dtype == LORA_F32 ? 4 : 2;
     for (const auto &u : uploads)
         if (c->used[u.first] && hipStreamWaitEvent(cs, c->last_use[u.first], 0) != hipSuccess)
             return LORA_ERR_HIP;
+    lora::copy_batch cb;
+    cb.n = 0;
+    cb.max_bytes = 0;
+    auto flush = [&]() -> lora_status_t {
+        const lora_status_t st = lora::launch_copy_batch(cb, cs);
+        cb.n = 0;
+        cb.max_bytes = 0;
+        return st;
+    };
+    // one buffer: into the gather kernel's batch if the kernel can read it, else a runtime copy
+    auto copy_one = [&](void *dst, const void *host, const void *dev, size_t bytes) -> lora_status_t {
+        if (dev && bytes < (size_t(1) << 31)) {
+            cb.src[cb.n] = dev;
+            cb.dst[cb.n] = dst;
+            cb.bytes[cb.n] = (uint32_t)bytes;
+            cb.max_bytes = cb.max_bytes > (uint32_t)bytes ? cb.max_bytes : (uint32_t)bytes;
+            return ++cb.n == lora::kCopyBatch ? flush() : LORA_OK;
+        }
+        return hipMemcpyAsync(dst, host, bytes, hipMemcpyHostToDevice, cs) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+    };
     for (const auto &u : uploads) {
         const int32_t s = u.first;
         const lora_cache::adapter &ad = c->adapters[u.second];
         for (int32_t p = 0; p < c->n_pools; ++p) {
             const lora_pool_t &q = c->pools[p];
             const size_t ab = (size_t)q.max_rank * q.d_in * eb, bb = (size_t)q.max_rank * q.d_out * eb;
-            if (hipMemcpyAsync((char *)q.a + (size_t)s * ab, ad.a[p], ab, hipMemcpyHostToDevice, cs) != hipSuccess ||
-                hipMemcpyAsync((char *)q.b + (size_t)s * bb, ad.b[p], bb, hipMemcpyHostToDevice, cs) != hipSuccess)
-                return LORA_ERR_HIP;
+            lora_status_t st = copy_one((char *)q.a + (size_t)s * ab, ad.a[p], ad.dev_a[p], ab);
+            if (st == LORA_OK) st = copy_one((char *)q.b + (size_t)s * bb, ad.b[p], ad.dev_b[p], bb);
+            if (st != LORA_OK) return st;
             c->bytes += (int64_t)(ab + bb);
         }
+    }
+    if (cb.n > 0) {
+        const lora_status_t st = flush();
+        if (st != LORA_OK) return st;
     }
     for (size_t i0 = 0; i0 < uploads.size(); i0 += lora::kMetaBatch) {
         lora::meta_batch m;

@@ -203,6 +203,19 @@ struct meta_batch {
     int32_t r[kMetaBatch];
 };
 lora_status_t launch_pool_meta_batch(const meta_batch &m, hipStream_t s);
+// Up to kCopyBatch copies of whole slot buffers in one launch: src[i] is a
+// device-visible address (page-locked host memory mapped into the GPU's
+// address space), dst[i] device memory, bytes[i] a multiple of 16.
+constexpr int32_t kCopyBatch = 32;
+constexpr uint32_t kCopyChunk = 64u << 10;     // bytes per workgroup
+struct copy_batch {
+    const void *src[kCopyBatch];
+    void *dst[kCopyBatch];
+    uint32_t bytes[kCopyBatch];
+    int32_t n;
+    uint32_t max_bytes;
+};
+lora_status_t launch_copy_batch(const copy_batch &c, hipStream_t s);
 lora_status_t launch_ws_init(void *ws, hipStream_t s);
 lora_status_t launch_segments(const int32_t *ids, int32_t T, int32_t n_slots, const ws_layout &L,
                               void *ws, hipStream_t s);

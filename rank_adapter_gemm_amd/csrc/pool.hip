@@ -109,6 +109,35 @@ lora_status_t launch_pool_meta_batch(const meta_batch &m, hipStream_t s) {
     return hip_status(hipGetLastError());
 }
 
+// Workgroup (chunk, i) copies bytes [64 KB chunk, +64 KB) of copy i; each
+// thread keeps four independent 16-byte loads in flight before storing them
+// (reads of mapped host memory cross the host link, so depth matters).
+__global__ void __launch_bounds__(256) k_copy_batch(copy_batch c) {
+    const int i = blockIdx.y;
+    if (i >= c.n) return;
+    const size_t begin = (size_t)blockIdx.x * kCopyChunk;
+    if (begin >= c.bytes[i]) return;
+    const size_t n16 = (min((size_t)c.bytes[i], begin + kCopyChunk) - begin) / 16;
+    const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const char *>(c.src[i]) + begin);
+    uint4 *dst = reinterpret_cast<uint4 *>(static_cast<char *>(c.dst[i]) + begin);
+    for (size_t i0 = threadIdx.x; i0 < n16; i0 += 4 * 256) {
+        uint4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i0 + u * 256 < n16) v[u] = src[i0 + u * 256];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i0 + u * 256 < n16) dst[i0 + u * 256] = v[u];
+    }
+}
+
+lora_status_t launch_copy_batch(const copy_batch &c, hipStream_t s) {
+    if (c.n <= 0) return LORA_OK;
+    const unsigned chunks = (unsigned)((c.max_bytes + kCopyChunk - 1) / kCopyChunk);
+    hipLaunchKernelGGL(k_copy_batch, dim3(chunks, c.n), dim3(256), 0, s, c);
+    return hip_status(hipGetLastError());
+}
+
 lora_status_t launch_pool_meta(const lora_pool_t &p, int32_t slot, float scale, int32_t rank, hipStream_t s) {
     hipLaunchKernelGGL(k_set_meta, dim3(1), dim3(64), 0, s, p.scale, p.rank, slot, scale, rank);
     return hip_status(hipGetLastError());

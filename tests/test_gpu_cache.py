@@ -1,9 +1,12 @@
 """GPU checks of the adapter residency cache: a host tier of 10 adapters
-(pinned, packed in the slot layout) served through 4 HBM slots of two pools
-kept in step.  Batches are mapped, computed and committed without any host
+(packed in the slot layout) served through 4 HBM slots of two pools kept in
+step.  Batches are mapped, computed and committed without any host
 synchronisation between them, so evictions overlap earlier batches' kernels;
 every batch's outputs are then checked against the fp64 oracle on the
-adapters' original weights, and the counters against the batch contents."""
+adapters' original weights, and the counters against the batch contents.
+The host tier is page-locked (copied by the gather kernel reading mapped
+host memory), or every other adapter is in pageable memory (copied by the
+runtime), so one map mixes both kinds of copy."""
 import numpy as np
 import pytest
 import torch
@@ -23,8 +26,9 @@ def _lib():
     L.load()
 
 
+@pytest.mark.parametrize("host", ["pinned", "mixed"])
 @pytest.mark.parametrize("mode", [L.LORA_MODE_BGMV, L.LORA_MODE_SGMV])
-def test_cache_serves_batches_through_few_slots(mode):
+def test_cache_serves_batches_through_few_slots(mode, host):
     torch.manual_seed(0)
     rng = np.random.default_rng(1)
     n_slots, n_adapters, R, d_in, d_outs, T = 4, 10, 16, 512, [256, 384], 200
@@ -39,8 +43,11 @@ def test_cache_serves_batches_through_few_slots(mode):
     for a in range(n_adapters):
         ha, hb = [], []
         for p, d in enumerate(d_outs):
-            sa = torch.empty(R * d_in, dtype=dt).pin_memory()
-            sb = torch.empty(R * d, dtype=dt).pin_memory()
+            pin = host == "pinned" or a % 2 == 0
+            sa = torch.empty(R * d_in, dtype=dt)
+            sb = torch.empty(R * d, dtype=dt)
+            if pin:
+                sa, sb = sa.pin_memory(), sb.pin_memory()
             L.lora_pack_host(d_in, d, R, L.LORA_BF16, A[p][a], B[p][a], ranks[a], sa, sb)
             ha.append(sa)
             hb.append(sb)
