@@ -154,7 +154,8 @@ def main():
             groups[-1].append(k)
         else:
             groups.append([k])
-    ws = L.Workspace(T, wl.n_slots, R, max(p.d_out for p in wl.projections), device=dev,
+    # d_out: the widest call (a sliced call plans its GEMM over all its slices)
+    ws = L.Workspace(T, wl.n_slots, R, max(sum(wl.projections[k].d_out for k in g) for g in groups), device=dev,
                      n_slices=max(len(g) for g in groups),
                      fp8_d_in=max(p.d_in for p in wl.projections) if fp8 else 0)
     v = torch.empty(T, R, dtype=torch.float32, device=dev)

@@ -153,8 +153,11 @@ lora_status_t lora_pool_clear(const lora_pool_t *pool, int32_t slot, lora_stream
  * output the workspace serves (0: none): with it the workspace also holds
  * fp32 partial tiles (at most 128 MiB) that let the GEMM split K -- for all
  * tiles of small batches, and for the last, mostly idle round of tiles of
- * larger ones; without it every tile runs whole (the two differ only in fp32
- * summation order).  Returns 0 on bad arguments. */
+ * larger ones; without it every tile runs whole.  The two differ in fp32
+ * summation order and in how the low-rank term is added: a whole tile feeds
+ * s_a * v to the matrix cores as two bf16 parts (about 16 significant
+ * bits), a split tile's reduction sums it in fp32.  Returns 0 on bad
+ * arguments. */
 size_t lora_workspace_bytes(int32_t T, int32_t n_slots, int32_t max_rank, int32_t d_out);
 
 /* Prepare a freshly allocated DEVICE workspace: clears the error word and
@@ -260,12 +263,20 @@ lora_status_t lora_shrink_sliced(const void *x, int32_t T, const lora_pool_t *po
 
 /* y[s] = x W[s] + s_a (x A_a^s) B_a^s for each slice s: W and y are HOST
  * arrays of n_slices DEVICE pointers ([d_in, pools[s].d_out] and
- * [T, pools[s].d_out]).  Same modes and flags as lora_linear_forward; the
- * results are bitwise those of n_slices lora_linear_forward calls.
- * Segments (SGMV) are built once, the shrink runs once for all slices, then
- * each slice's GEMM applies its expand.  A slice that lora_linear_forward
- * would run on its decode-sized fused path (the shrink inside the GEMM, on
- * the x it streams anyway) runs that way here too. */
+ * [T, pools[s].d_out]).  Same modes and flags as lora_linear_forward.
+ * Segments (SGMV) are built once and the shrink runs once for all slices.
+ * A slice that lora_linear_forward would run on its decode-sized fused path
+ * (the shrink inside the GEMM, on the x it streams anyway) runs that way
+ * here too, bitwise as that call.  The other slices of a bf16 pool share one
+ * GEMM launch whose grid spans every slice's column tiles (each with its own
+ * W, y and expand) when some of them alone would not fill the chip with the
+ * largest tiles; their results may then differ from lora_linear_forward's
+ * where a tile is computed whole in one call and split over K in the other
+ * (see lora_workspace_bytes; the GEMM is planned for all slices' tiles at
+ * once).  Otherwise, and for fp32 pools and LORA_FLAG_SEPARATE_EXPAND,
+ * each slice runs its own GEMM, bitwise as lora_linear_forward.  For the
+ * grouped GEMM's K split, size the workspace with d_out = the sum of the
+ * slices' widths (a smaller d_out only limits the split). */
 lora_status_t lora_linear_forward_sliced(const void *x, const void *const *W, void *const *y,
                                          int32_t T, const lora_pool_t *pools, int32_t n_slices,
                                          const int32_t *ids, lora_mode_t mode, uint32_t flags,

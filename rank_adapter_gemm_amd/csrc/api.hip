@@ -334,17 +334,37 @@ lora_status_t lora_linear_forward_sliced(const void *x, const void *const *W, vo
         st = launch_shrink(x, T, pools, n_slices, ids, sgmv, v, L, ws, s);   // one x read, one launch
         if (st != LORA_OK) return st;
     }
+    // bf16 slices on the shared shrink: one grouped GEMM with the fused
+    // expand, where that fills the chip better than one GEMM per slice
+    int32_t Ns[kMaxSlices], nn = 0;
+    for (int i = 0; i < n_slices; ++i)
+        if (!fused[i]) Ns[nn++] = pools[i].d_out;
+    const bool grouped = pools[0].dtype == LORA_BF16 && !(flags & LORA_FLAG_SEPARATE_EXPAND) &&
+                         gemm_grouping_pays(T, pools[0].d_in, Ns, nn, ws_bytes - L.gemm_partial);
+    const void *gW[kMaxSlices];
+    void *gy[kMaxSlices];
+    lora_pool_t gp[kMaxSlices];
+    int32_t goff[kMaxSlices], ng = 0;
     for (int i = 0; i < n_slices; ++i) {
         if (fused[i])
             st = launch_gemm_fused_shrink(x, W[i], y[i], T, &pools[i], ids, ws_ptr<float>(ws, L.partial),
                                           ws_ptr<int32_t>(ws, L.header), ws_ptr<float>(ws, L.gemm_partial),
                                           ws_bytes - L.gemm_partial, s);
-        else
+        else if (grouped) {
+            gW[ng] = W[i];
+            gy[ng] = y[i];
+            gp[ng] = pools[i];
+            goff[ng++] = i * R;
+        } else
             st = gemm_and_expand(x, W[i], y[i], T, pools[i], ids, v + i * R, VS, sgmv, flags, L, ws,
                                  ws_bytes, s);
         if (st != LORA_OK) return st;
     }
-    return LORA_OK;
+    if (ng > 0)
+        st = launch_gemm_grouped(x, gW, gy, T, gp, ng, ids, v, goff, VS,
+                                 sgmv ? ws_ptr<int32_t>(ws, L.perm) : nullptr, ws_ptr<float>(ws, L.gemm_partial),
+                                 ws_bytes - L.gemm_partial, s);
+    return st;
 }
 
 lora_status_t lora_quantize_rows_fp8(const void *x, int32_t T, int32_t d, uint8_t *xq, float *x_scale,

@@ -234,6 +234,11 @@ lora_status_t launch_gemm_fused_shrink(const void *x, const void *W, void *y, in
                                        const lora_pool_t *pool, const int32_t *ids, float *vpart,
                                        int32_t *err, float *partial, size_t partial_bytes,
                                        hipStream_t s);
+bool gemm_grouping_pays(int32_t T, int32_t K, const int32_t *Ns, int32_t n, size_t partial_bytes);
+lora_status_t launch_gemm_grouped(const void *x, const void *const *W, void *const *y, int32_t T,
+                                  const lora_pool_t *pools, int32_t n, const int32_t *ids, const float *v,
+                                  const int32_t *v_off, int32_t v_stride, const int32_t *perm, float *partial,
+                                  size_t partial_bytes, hipStream_t s);
 lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int32_t d_in,
                           int32_t d_out, int32_t dtype, const lora_pool_t *pool,
                           const int32_t *ids, const float *v, int32_t v_stride,

@@ -56,6 +56,7 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
     const int wm = w / (WV / WR), wn = w % (WV / WR);
     int tm, tn, split, tidx;
     tile_of(blockIdx.x, gridDim.x, g, tm, tn, split, tidx);
+    tn = select_slice(g, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int K = g.K, N = g.N, T = g.T;
     const int k_begin = SPLIT ? split * g.k_chunk : 0;
@@ -461,6 +462,66 @@ lora_status_t launch_gemm_fused_shrink(const void *x, const void *W, void *y, in
     hipLaunchKernelGGL((k_gemm_bf16<false, 256, 64, 64, 3, true, true>), dim3(pl.tail * pl.splits), dim3(256),
                        0, s, g);
     hipLaunchKernelGGL((k_splitk_reduce<true, true, 256, 64>), dim3(pl.tail * (256 / 32)), dim3(256), 0, s, g);
+    return hip_status(hipGetLastError());
+}
+
+// Whether slices of these widths gain from one grouped launch: not when each
+// alone already runs whole tiles of the largest size (measured: two 28672-
+// or 14336-wide slices run 3-9% slower grouped than one after the other),
+// but when some slice alone would take smaller tiles or split K.
+bool gemm_grouping_pays(int32_t T, int32_t K, const int32_t *Ns, int32_t n, size_t partial_bytes) {
+    if (n < 2) return false;
+    for (int i = 0; i < n; ++i) {
+        const gemm_plan pl = plan_gemm(T, K, Ns[i], partial_bytes);
+        if (pl.bm != 256 || pl.bn != 256 || pl.tail != 0) return true;
+    }
+    return false;
+}
+
+// Base products of several outputs that share x (projections of one
+// layer), each with its own adapter pool and rank columns v + v_off[i], in
+// one launch: the column tiles of all slices form one grid, so a layer of
+// narrow projections still fills the chip with large tiles.
+lora_status_t launch_gemm_grouped(const void *x, const void *const *W, void *const *y, int32_t T,
+                                  const lora_pool_t *pools, int32_t n, const int32_t *ids, const float *v,
+                                  const int32_t *v_off, int32_t v_stride, const int32_t *perm, float *partial,
+                                  size_t partial_bytes, hipStream_t s) {
+    if (n < 1 || n > kMaxSlices || pools[0].dtype != LORA_BF16) return LORA_ERR_INVALID_ARGUMENT;
+    int32_t Ns[kMaxSlices];
+    for (int i = 0; i < n; ++i) Ns[i] = pools[i].d_out;
+    gemm_args g{};
+    g.x = (const uint16_t *)x;
+    g.T = T;
+    g.K = pools[0].d_in;
+    g.perm = perm;
+    g.n_slots = pools[0].n_slots;
+    g.max_rank = pools[0].max_rank;
+    g.ids = ids;
+    g.v = v;
+    g.v_stride = v_stride;
+    const gemm_plan pl = plan_gemm(T, g.K, Ns, n, partial ? partial_bytes : 0);
+    g.n_slices = n;
+    int tn0 = 0;
+    for (int i = 0; i < n; ++i) {
+        g.sl[i] = gemm_slice{(const uint16_t *)W[i], (uint16_t *)y[i], Ns[i], tn0, (const uint16_t *)pools[i].b,
+                             pools[i].scale, pools[i].rank, v_off[i]};
+        tn0 += ceil_div(Ns[i], pl.bn);
+    }
+    // fields a slice overrides start at slice 0 (never read before selection)
+    g.W = g.sl[0].W;
+    g.y = g.sl[0].y;
+    g.N = g.sl[0].N;
+    g.b = g.sl[0].b;
+    g.scale = g.sl[0].scale;
+    g.rank = g.sl[0].rank;
+    g.n_tiles_m = ceil_div(T, pl.bm);
+    g.n_tiles_n = tn0;
+    g.partial = partial;
+    if (pl.bm == 256 && pl.bn == 256) launch_cfg<256, 256, 2, 8>(g, pl, true, s);
+    else if (pl.bm == 256 && pl.bn == 128) launch_cfg<256, 128, 2, 8>(g, pl, true, s);
+    else if (pl.bm == 256) launch_cfg<256, 64, 3>(g, pl, true, s);
+    else if (pl.bn == 128) launch_cfg<128, 128>(g, pl, true, s);
+    else launch_cfg<128, 64>(g, pl, true, s);
     return hip_status(hipGetLastError());
 }
 

@@ -7,6 +7,19 @@
 
 namespace lora {
 
+// One output slice of a grouped launch (projections that share x): its
+// weight, output, width, first column tile in the launch's tile numbering,
+// adapter pool (B, scale, rank) and the offset of its rank columns in v.
+struct gemm_slice {
+    const uint16_t *W;
+    uint16_t *y;
+    int32_t N, tn0;
+    const uint16_t *b;
+    const float *scale;
+    const int32_t *rank;
+    int32_t v_off;
+};
+
 struct gemm_args {
     const uint16_t *x;
     const uint16_t *W;
@@ -31,7 +44,29 @@ struct gemm_args {
     const uint8_t *wq;             // FP8 base: E4M3 codes of the W columns [N][K]
     const float *xs;               // FP8 base: row scales [T] (powers of two)
     const float *wsc;              // FP8 base: column scales [N] (powers of two)
+    int32_t n_slices;              // grouped launch: 0 (one output), else slices sl[0..n_slices)
+    gemm_slice sl[kMaxSlices];     // column tiles numbered slice after slice
 };
+
+// Grouped launch: point g at the slice that owns global column tile tn and
+// return the tile's index within that slice (identity without slices).  The
+// slice is chosen with constant indices only, so the arguments stay in
+// registers.
+__device__ __forceinline__ int select_slice(gemm_args &g, int tn) {
+    if (g.n_slices <= 0) return tn;
+    gemm_slice q = g.sl[0];
+#pragma unroll
+    for (int i = 1; i < kMaxSlices; ++i)
+        if (i < g.n_slices && tn >= g.sl[i].tn0) q = g.sl[i];
+    g.W = q.W;
+    g.y = q.y;
+    g.N = q.N;
+    g.b = q.b;
+    g.scale = q.scale;
+    g.rank = q.rank;
+    if (g.v) g.v += q.v_off;
+    return tn - q.tn0;
+}
 
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs (each
 // with its own L2), so workgroup b runs on XCD b % 8.  Give each XCD a
@@ -275,13 +310,15 @@ __device__ __forceinline__ void gemm_store_tile(const gemm_args &g, f32x16_t (&a
 // With VP (fused shrink) the rows' v are first summed from the K-range rank
 // partials (in range order) into LDS, and the first column tile flags bad ids.
 template <bool LORA, bool VP, int BM, int BN>
-__global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g) {
+__global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g0) {
     constexpr int RW = 2048 / BN, CPR = BN / 8, CHUNKS = BM / RW;
     constexpr int SP = 4;                                 // split partials loaded ahead
     constexpr int GP = 2;                                 // rank octets of B loaded ahead
     const int tidx = blockIdx.x / CHUNKS, chunk = blockIdx.x % CHUNKS;
     int tm, tn;
-    grouped_tile(g.tile_base + tidx, g.n_tiles_m, g.n_tiles_n, tm, tn);
+    grouped_tile(g0.tile_base + tidx, g0.n_tiles_m, g0.n_tiles_n, tm, tn);
+    gemm_args g = g0;
+    tn = select_slice(g, tn);
     const int T = g.T, N = g.N, R = g.max_rank;
     const int r = chunk * RW + threadIdx.x / CPR, c = (threadIdx.x % CPR) * 8;
     const int p = tm * BM + r, n = tn * BN + c;
@@ -404,11 +441,17 @@ inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 // stay small (few token rows) split K for all tiles.  Split-K needs room for
 // the fp32 partials in the workspace.  K ranges are multiples of kgran
 // elements (one K step of the kernel).
-inline gemm_plan plan_gemm(int T, int K, int N, size_t partial_bytes, int kgran = 64) {
+inline int tiles_n(const int32_t *Ns, int nN, int bn) {
+    int t = 0;
+    for (int i = 0; i < nN; ++i) t += ceil_div(Ns[i], bn);
+    return t;
+}
+
+inline gemm_plan plan_gemm(int T, int K, const int32_t *Ns, int nN, size_t partial_bytes, int kgran = 64) {
     static const int cfg[4][2] = {{256, 256}, {256, 128}, {128, 128}, {128, 64}};
     for (int c = 0; c < 4; ++c) {
         const int bm = cfg[c][0], bn = cfg[c][1];
-        const int tiles = ceil_div(T, bm) * ceil_div(N, bn);
+        const int tiles = ceil_div(T, bm) * tiles_n(Ns, nN, bn);
         if (tiles < 224) continue;
         gemm_plan p{bm, bn, tiles, 0, 1, K};
         const int full = tiles / 256 * 256, rem = tiles - full;
@@ -428,18 +471,24 @@ inline gemm_plan plan_gemm(int T, int K, int N, size_t partial_bytes, int kgran 
     // so W is read once; narrow 64-column tiles keep the number of fp32
     // partial copies (written and read back) low for the same grid size.
     const int bm = T <= 256 ? 256 : 128, bn = T <= 256 ? 64 : 128;
-    const int tiles = ceil_div(T, bm) * ceil_div(N, bn);
+    const int tiles = ceil_div(T, bm) * tiles_n(Ns, nN, bn);
     int splits = ceil_div(256, tiles);
     const int max_by_k = K / 256 > 0 ? K / 256 : 1;
     if (splits > max_by_k) splits = max_by_k;
     if (splits > kMaxGemmSplit) splits = kMaxGemmSplit;
     while (splits > 1 && (size_t)splits * tiles * bm * bn * 4 > partial_bytes) --splits;
     if (splits <= 1) {
-        const int t2 = ceil_div(T, 128) * ceil_div(N, 64);
+        const int t2 = ceil_div(T, 128) * tiles_n(Ns, nN, 64);
         return t2 > tiles ? gemm_plan{128, 64, t2, 0, 1, K} : gemm_plan{bm, bn, tiles, 0, 1, K};
     }
     const int k_chunk = ceil_div(ceil_div(K, splits), kgran) * kgran;
     return {bm, bn, 0, tiles, ceil_div(K, k_chunk), k_chunk};
+}
+
+// One output of width N.
+inline gemm_plan plan_gemm(int T, int K, int N, size_t partial_bytes, int kgran = 64) {
+    const int32_t n = N;
+    return plan_gemm(T, K, &n, 1, partial_bytes, kgran);
 }
 
 }  // namespace lora

@@ -176,7 +176,7 @@ def test_layer_sets_sliced_as_benchmarked(name, max_rows):
         else:
             groups.append([k])
     assert any(len(g) > 1 for g in groups)
-    ws = L.Workspace(wl.T, wl.n_slots, R, max(p.d_out for p in wl.projections),
+    ws = L.Workspace(wl.T, wl.n_slots, R, max(sum(wl.projections[k].d_out for k in g) for g in groups),
                      n_slices=max(len(g) for g in groups))
     for gi, grp in enumerate(groups):
         projs = [wl.projections[k] for k in grp]
