@@ -62,6 +62,8 @@ def parse():
                     help="also measure the adapter cache's host-to-HBM promotion rate")
     ap.add_argument("--fp8-base", action="store_true",
                     help="E4M3 base weights (lora_linear_forward_fp8); reported apart from the bf16 headline")
+    ap.add_argument("--single-adapter", action="store_true",
+                    help="context run: every row that has an adapter uses the batch's most frequent one")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain fp32 copy kernel of known size (for counter scaling)")
     return ap.parse_args()
@@ -99,6 +101,12 @@ def main():
     sgmv = mode == L.LORA_MODE_SGMV or (mode == L.LORA_MODE_AUTO and wl.T >= 1024)
     eb = 4 if wl.dtype == torch.float32 else 2
     T, R = wl.T, wl.max_rank
+    if args.single_adapter:
+        # same rows, same base-only rows; one adapter (the batch's most used) for the rest
+        live = (wl.ids >= 0) & (wl.ids < wl.n_slots)
+        if live.any():
+            top = int(np.bincount(wl.ids[live]).argmax())
+            wl.ids = np.where(live, top, wl.ids).astype(np.int32)
     ids = torch.as_tensor(wl.ids, device=dev)
 
     # ---- pools (one per projection) ----
@@ -228,6 +236,9 @@ def main():
         names = (["segments"] if sgmv else []) + ["shrink", "gemm", "expand"]
     if fp8:
         names = (["segments"] if sgmv else []) + ["quantize", "shrink", "gemm_fp8"]
+    # the base product alone (no adapters), for the LoRA overhead
+    if "gemm" not in names and not fp8:
+        names.append("gemm")
     smode = L.LORA_MODE_SGMV if sgmv else L.LORA_MODE_BGMV
 
     def call(name, k, i):
@@ -384,6 +395,10 @@ def main():
     roof["algorithmic_bytes_per_launch"] = int(by_d)
     roof["algorithmic_flops_per_launch"] = int(fl_d)
     roof["traffic"] = stored_traffic("forward_fp8" if fp8 else "forward", args.workload, roof["projection"])
+    # LoRA overhead: the step's forward calls against the base products alone
+    base_ms = sum(per_launch[(n_, k)] for (n_, k) in per_launch if n_ in ("gemm", "gemm_fp8", "quantize"))
+    overhead = dict(forward_us=round(1e3 * sum(fwd.values()), 3), base_only_us=round(1e3 * base_ms, 3),
+                    overhead=round(sum(fwd.values()) / base_ms - 1.0, 4) if base_ms else None)
     breakdown["forward"] = dict(us_per_step=round(1e3 * sum(fwd.values()), 3),
                                 per_call_us={"+".join(wl.projections[k].name for k in groups[gi]):
                                              round(1e3 * v, 3) for gi, v in fwd.items()})
@@ -426,10 +441,12 @@ def main():
             "base": ("fp8 e4m3 (per-row x, per-column W scales); bf16 adapters" if fp8 else
                      ("fp32" if wl.dtype == torch.float32 else "bf16")),
             "calls": ["+".join(wl.projections[k].name for k in g) for g in groups],
+            "adapters": "single (most frequent)" if args.single_adapter else "mixed",
             "cold_sets": n_sets, "working_set_MB": round(set_bytes / 1e6, 1),
         },
         "roofline": roof,
         "breakdown": breakdown,
+        "lora_overhead": overhead,
         "cpu_baseline": cpu,
     }
     if residency is not None:

@@ -243,7 +243,7 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
     // the first stages load.  (Split-K tiles leave it to the reduction, whose
     // one-thread-per-row-chunk layout hides the per-row loads of B.)
     if (LORA && !SPLIT)
-        lora_pass_impl<RB, CB, (RB >= 2 ? 2 : 1), 1>(g, acc, s_meta_t, s_meta_id, n0, wm * WM, n0 + wn * WN,
+        lora_pass_impl<RB, CB, (RB >= 2 ? 2 : 1), 1, (RB >= 2 ? 2 : 1)>(g, acc, s_meta_t, s_meta_id, n0, wm * WM, n0 + wn * WN,
                                                     lane);
     wait_stage(min(NS - 1, nk - 1));
     __builtin_amdgcn_s_barrier();

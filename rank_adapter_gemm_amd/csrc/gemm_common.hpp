@@ -189,17 +189,24 @@ __device__ __forceinline__ void lora_step_mfma(f32x16_t (&acc)[CB], float sa, bo
 // segment order): the operands of KB rank steps of RG blocks are loaded
 // before any of their MFMAs, so the wavefront waits for memory once per
 // group, not once per block and step.  Rows of further adapters in a block
-// (unsorted batches) are then taken one adapter at a time.  Per block the
-// MFMAs run in the same order either way: adapters by lowest row, ranks
-// ascending.
-template <int RB, int CB, int RG = 1, int KB = 1>
+// (unsorted batches, or the short segments of decode rows in a sorted one)
+// are then taken one adapter per block and round, for RF blocks at a time,
+// so RF blocks' loads are in flight together; before that loop each lane
+// loads its own row's slot rank and scale, and the loop takes an adapter's
+// from the lane of its lowest row, so finding the next adapter needs no
+// memory access.  RF = 0 keeps one block and one adapter at a time, with
+// the slot's rank and scale read per adapter (kernels with no registers to
+// spare).  Per block the MFMAs run in the same order either way: adapters
+// by lowest row, ranks ascending.
+template <int RB, int CB, int RG = 1, int KB = 1, int RF = 1>
 __device__ __forceinline__ void lora_pass_impl(const gemm_args &g, f32x16_t (&acc)[RB][CB],
                                                const int32_t *s_t, const int32_t *s_id, int n0,
                                                int wrow0, int wcol0, int lane) {
-    static_assert(RB % RG == 0, "row blocks come in whole groups");
+    static_assert(RB % RG == 0 && (RF == 0 || RB % RF == 0), "row blocks come in whole groups");
+    constexpr int RFG = RF > 0 ? RF : 1;
     const int half = lane >> 5;
-    int32_t my_id[RB], my_t[RB], a0[RB], ra0[RB];
-    float sa0[RB];
+    int32_t my_id[RB], my_t[RB], my_r[RB], a0[RB], ra0[RB];
+    float my_s[RB], sa0[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const int row = wrow0 + rb * 32 + (lane & 31);
@@ -234,22 +241,78 @@ __device__ __forceinline__ void lora_pass_impl(const gemm_args &g, f32x16_t (&ac
                                            v0[i][u], v1[i][u], bq[i][u]);
         }
     }
-    // further adapters of a block, one at a time
+    if (RF == 0) {
+        // further adapters of a block, one at a time (kernels at their
+        // register limit: no per-row rank and scale)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            uint64_t pend = __ballot(my_id[rb] >= 0 && my_id[rb] != a0[rb]) & 0xffffffffull;
+            while (pend) {
+                const int first = __ffsll((long long)pend) - 1;
+                const int32_t a = __shfl(my_id[rb], first, 64);
+                pend &= ~(__ballot(my_id[rb] == a) & 0xffffffffull);
+                const int32_t ra = g.rank[a];
+                const float sa = g.scale[a];
+                const bool mine = my_id[rb] == a;
+                for (int ks = 0; ks * 16 < ra; ++ks) {
+                    float4 v0, v1;
+                    uint4 bq[CB];
+                    lora_step_load<CB>(g, a, ra, mine, my_t[rb], ks, half, wcol0, lane, v0, v1, bq);
+                    lora_step_mfma<CB>(acc[rb], sa, mine && 16 * ks + 8 * half < ra, v0, v1, bq);
+                }
+            }
+        }
+        return;
+    }
+    // further adapters of the blocks, RF blocks at a time
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        uint64_t pend = __ballot(my_id[rb] >= 0 && my_id[rb] != a0[rb]) & 0xffffffffull;
-        while (pend) {
-            const int first = __ffsll((long long)pend) - 1;
-            const int32_t a = __shfl(my_id[rb], first, 64);
-            pend &= ~(__ballot(my_id[rb] == a) & 0xffffffffull);
-            const int32_t ra = g.rank[a];
-            const float sa = g.scale[a];
-            const bool mine = my_id[rb] == a;
-            for (int ks = 0; ks * 16 < ra; ++ks) {
-                float4 v0, v1;
-                uint4 bq[CB];
-                lora_step_load<CB>(g, a, ra, mine, my_t[rb], ks, half, wcol0, lane, v0, v1, bq);
-                lora_step_mfma<CB>(acc[rb], sa, mine && 16 * ks + 8 * half < ra, v0, v1, bq);
+        my_r[rb] = my_id[rb] >= 0 ? g.rank[my_id[rb]] : 0;
+        my_s[rb] = my_id[rb] >= 0 ? g.scale[my_id[rb]] : 0.0f;
+    }
+#pragma unroll
+    for (int r0 = 0; r0 < RB; r0 += RFG) {
+        uint64_t pend[RFG];
+        uint64_t any = 0;
+#pragma unroll
+        for (int i = 0; i < RFG; ++i) {
+            pend[i] = __ballot(my_id[r0 + i] >= 0 && my_id[r0 + i] != a0[r0 + i]) & 0xffffffffull;
+            any |= pend[i];
+        }
+        while (any) {                                       // wave-uniform
+            int32_t a[RFG], ra[RFG];
+            float sa[RFG];
+            bool mine[RFG];
+            int nks = 0;
+            any = 0;
+#pragma unroll
+            for (int i = 0; i < RFG; ++i) {
+                a[i] = -1;
+                ra[i] = 0;
+                sa[i] = 0.0f;
+                if (pend[i]) {
+                    const int first = __ffsll((long long)pend[i]) - 1;
+                    a[i] = __shfl(my_id[r0 + i], first, 64);
+                    ra[i] = __shfl(my_r[r0 + i], first, 64);
+                    sa[i] = __shfl(my_s[r0 + i], first, 64);
+                    pend[i] &= ~(__ballot(my_id[r0 + i] == a[i]) & 0xffffffffull);
+                }
+                mine[i] = a[i] >= 0 && my_id[r0 + i] == a[i];
+                nks = max(nks, (ra[i] + 15) >> 4);
+                any |= pend[i];
+            }
+            for (int ks = 0; ks < nks; ++ks) {
+                float4 v0[RFG], v1[RFG];
+                uint4 bq[RFG][CB];
+#pragma unroll
+                for (int i = 0; i < RFG; ++i)
+                    lora_step_load<CB>(g, a[i], ra[i], mine[i], my_t[r0 + i], ks, half, wcol0, lane, v0[i], v1[i],
+                                       bq[i]);
+#pragma unroll
+                for (int i = 0; i < RFG; ++i)
+                    if (16 * ks < ra[i])                   // wave-uniform
+                        lora_step_mfma<CB>(acc[r0 + i], sa[i], mine[i] && 16 * ks + 8 * half < ra[i], v0[i], v1[i],
+                                           bq[i]);
             }
         }
     }

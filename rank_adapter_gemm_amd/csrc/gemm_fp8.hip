@@ -328,7 +328,7 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_fp8(gemm_args g) {
     // The low-rank term goes into the accumulators before the K loop, while
     // the first stages load (split-K tiles leave it to the reduction).
     if (LORA && !SPLIT)
-        lora_pass_impl<RB, CB, (RB >= 4 ? RB : 1), 1>(g, acc, s_meta_t, s_meta_id, n0, wm * WM, n0 + wn * WN, lane);
+        lora_pass_impl<RB, CB, (RB >= 4 ? RB : 1), 1, 0>(g, acc, s_meta_t, s_meta_id, n0, wm * WM, n0 + wn * WN, lane);
     wait_stage(min(NS - 1, nk - 1));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
