@@ -516,6 +516,7 @@ lora_status_t launch_gemm_grouped(const void *x, const void *const *W, void *con
     g.rank = g.sl[0].rank;
     g.n_tiles_m = ceil_div(T, pl.bm);
     g.n_tiles_n = tn0;
+    g.col_strips = col_strips_pay(T, tn0 * pl.bn, tn0);
     g.partial = partial;
     if (pl.bm == 256 && pl.bn == 256) launch_cfg<256, 256, 2, 8>(g, pl, true, s);
     else if (pl.bm == 256 && pl.bn == 128) launch_cfg<256, 128, 2, 8>(g, pl, true, s);
@@ -549,6 +550,7 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
         const gemm_plan pl = plan_gemm(T, d_in, d_out, partial ? partial_bytes : 0);
         g.n_tiles_m = ceil_div(T, pl.bm);
         g.n_tiles_n = ceil_div(d_out, pl.bn);
+        g.col_strips = col_strips_pay(T, d_out, g.n_tiles_n);
         g.partial = partial;
         g.a = nullptr;
         g.vpart = nullptr;

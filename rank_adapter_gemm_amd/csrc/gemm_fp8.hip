@@ -432,6 +432,7 @@ lora_status_t launch_gemm_fp8(const uint8_t *xq, const float *xs, const uint8_t 
     const gemm_plan pl = plan_gemm(T, d_in, d_out, partial ? partial_bytes : 0, 128);
     g.n_tiles_m = ceil_div(T, pl.bm);
     g.n_tiles_n = ceil_div(d_out, pl.bn);
+    g.col_strips = col_strips_pay(T, d_out, g.n_tiles_n);
     g.partial = partial;
     const bool lora = pool != nullptr;
     if (pl.bm == 256 && pl.bn == 256) launch_fp8_cfg<256, 256, 2, 4>(g, pl, lora, s);
