@@ -175,6 +175,8 @@ GEMM_SHAPES = [
     (37, 2048, 1024),   # 256x64 split-K (decode-sized)
     (2048, 512, 3584),  # 256x128 whole tiles
     (4352, 1024, 4096), # 256x256 whole tiles plus a split-K tail round
+    (300, 256, 16408),  # 256x128 in column bands (129 column tiles, the last band one tile wide)
+    (520, 1024, 16384), # column bands with a split-K tail round
 ]
 
 
@@ -211,6 +213,7 @@ FWD_SHAPES = [
     (1, 16, 8, 8, [8, 5]),                      # the smallest shape: one row, one K step, one column octet
     (1, 4096, 4096, 16, [16, 16, 16]),          # one decode row
     (5, 48, 24, 128, [128, 1, 77, 0]),          # max rank 128, ragged ranks, K and N far below a tile
+    (520, 1024, 16384, 16, [16, 9, 0, 16]),     # column bands, split-K tail, expand fused and in the reduction
 ]
 
 
