@@ -19,7 +19,8 @@
 //      entry (key, tile) becomes the first output position of that tile's rows
 //      with that key; offsets[], then the compaction of non-empty keys >= 1
 //   3. per tile, each row's rank among the earlier rows of its tile with the
-//      same key (stable), perm[base + rank] = t.
+//      same key (stable: the tile's (key, row) pairs sorted in LDS),
+//      perm[base + rank] = t.
 #include "common.hpp"
 
 namespace lora {
@@ -83,6 +84,77 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *s_wa
     return res;
 }
 
+// Compaction of non-empty adapter keys (k >= 1) in ascending order, and the
+// shrink work table: segment i covers work blocks [blk_start[i],
+// blk_start[i+1]) of kShrinkRows rows each.  s_off: the keys' first output
+// positions (s_off[nb] = T), in LDS; every thread of the block calls it.
+__device__ void compact_segments(const int32_t *s_off, int32_t nb, int32_t T, int32_t *s_wave,
+                                 int32_t *__restrict__ seg_id, int32_t *__restrict__ seg_start,
+                                 int32_t *__restrict__ n_seg, int32_t *__restrict__ blk_start,
+                                 int32_t *__restrict__ blk_seg) {
+    int32_t seg_carry = 0, blk_carry = 0;
+    for (int32_t k0 = 1; k0 < nb; k0 += blockDim.x) {
+        const int32_t k = k0 + threadIdx.x;
+        const int32_t len = (k < nb) ? (s_off[k + 1] - s_off[k]) : 0;
+        const int32_t nonempty = len > 0;
+        const int32_t nblk = (len + kShrinkRows - 1) / kShrinkRows;
+        int32_t tot, btot;
+        const int32_t idx = block_exclusive_scan(nonempty, s_wave, &tot) + seg_carry;
+        const int32_t bidx = block_exclusive_scan(nblk, s_wave, &btot) + blk_carry;
+        if (nonempty) {
+            seg_id[idx] = k - 1;
+            seg_start[idx] = s_off[k];
+            blk_start[idx] = bidx;
+            for (int32_t b = 0; b < nblk; ++b) blk_seg[bidx + b] = idx;
+        }
+        seg_carry += tot;
+        blk_carry += btot;
+    }
+    if (threadIdx.x == 0) {
+        seg_start[seg_carry] = T;
+        blk_start[seg_carry] = blk_carry;
+        *n_seg = seg_carry;
+    }
+}
+
+// The (key, row) pairs of one tile of kSegTile rows (rows t0 ...), sorted
+// ascending in LDS by a bitonic network; rows are distinct, so the order is
+// total and rows of one key stay in row order (stable).  Returns thread i's
+// sorted key (INT32_MAX for padding past T) and row, and the key's first
+// sorted position, so i - first is the row's rank among the tile's rows of
+// its key.  Every thread of the block (kSegTile of them) calls it.
+__device__ void sort_tile(const int32_t *__restrict__ ids, int32_t T, int32_t n_slots, int32_t t0,
+                          int32_t *s_key, int32_t *s_row, int32_t &key, int32_t &row, int32_t &first) {
+    const int i = threadIdx.x;
+    const int32_t t = t0 + i;
+    s_key[i] = (t < T) ? row_key(ids[t], n_slots) : INT32_MAX;         // padding sorts last
+    s_row[i] = t;
+    __syncthreads();
+    for (int k = 2; k <= kSegTile; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const int p = i ^ j;
+            if (p > i) {
+                const int32_t ka = s_key[i], kb = s_key[p], ra = s_row[i], rb = s_row[p];
+                const bool a_gt_b = ka > kb || (ka == kb && ra > rb);
+                if (a_gt_b == ((i & k) == 0)) {                      // ascending where bit k of i is clear
+                    s_key[i] = kb; s_key[p] = ka;
+                    s_row[i] = rb; s_row[p] = ra;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    key = s_key[i];
+    row = s_row[i];
+    int lo = 0, hi = i;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_key[mid] < key) lo = mid + 1;
+        else hi = mid;
+    }
+    first = lo;
+}
+
 constexpr int kScanItems = 4;
 
 __global__ void __launch_bounds__(1024) k_seg_scan(int32_t *__restrict__ tile_hist, int32_t n_slots,
@@ -124,49 +196,18 @@ __global__ void __launch_bounds__(1024) k_seg_scan(int32_t *__restrict__ tile_hi
     __syncthreads();
     for (int32_t k = threadIdx.x; k <= nb; k += blockDim.x) offsets[k] = s_off[k];
 
-    // Compaction of non-empty adapter keys (k >= 1) in ascending order, and
-    // the shrink work table: segment i covers work blocks
-    // [blk_start[i], blk_start[i+1]) of kShrinkRows rows each.
-    int32_t seg_carry = 0, blk_carry = 0;
-    for (int32_t k0 = 1; k0 < nb; k0 += blockDim.x) {
-        const int32_t k = k0 + threadIdx.x;
-        const int32_t len = (k < nb) ? (s_off[k + 1] - s_off[k]) : 0;
-        const int32_t nonempty = len > 0;
-        const int32_t nblk = (len + kShrinkRows - 1) / kShrinkRows;
-        int32_t tot, btot;
-        const int32_t idx = block_exclusive_scan(nonempty, s_wave, &tot) + seg_carry;
-        const int32_t bidx = block_exclusive_scan(nblk, s_wave, &btot) + blk_carry;
-        if (nonempty) {
-            seg_id[idx] = k - 1;
-            seg_start[idx] = s_off[k];
-            blk_start[idx] = bidx;
-            for (int32_t b = 0; b < nblk; ++b) blk_seg[bidx + b] = idx;
-        }
-        seg_carry += tot;
-        blk_carry += btot;
-    }
-    if (threadIdx.x == 0) {
-        seg_start[seg_carry] = T;
-        blk_start[seg_carry] = blk_carry;
-        *n_seg = seg_carry;
-    }
+    compact_segments(s_off, nb, T, s_wave, seg_id, seg_start, n_seg, blk_start, blk_seg);
 }
 
 __global__ void __launch_bounds__(1024) k_seg_scatter(const int32_t *__restrict__ ids, int32_t T,
                                                       int32_t n_slots,
                                                       const int32_t *__restrict__ tile_hist,
                                                       int32_t n_tiles, int32_t *__restrict__ perm) {
-    __shared__ int32_t keys[kSegTile];
-    const int32_t tile = blockIdx.x, i = threadIdx.x;
-    const int32_t t = tile * kSegTile + i;
-    const int32_t key = (t < T) ? row_key(ids[t], n_slots) : -1;
-    keys[i] = key;
-    __syncthreads();
-    if (t >= T) return;
-    // Stable rank: earlier rows of this tile with the same key.
-    int32_t rank = 0;
-    for (int32_t j = 0; j < i; ++j) rank += (keys[j] == key);
-    perm[tile_hist[(size_t)key * n_tiles + tile] + rank] = t;
+    __shared__ int32_t s_key[kSegTile], s_row[kSegTile];
+    int32_t key, row, first;
+    sort_tile(ids, T, n_slots, blockIdx.x * kSegTile, s_key, s_row, key, row, first);
+    if (key == INT32_MAX) return;
+    perm[tile_hist[(size_t)key * n_tiles + blockIdx.x] + ((int)threadIdx.x - first)] = row;
 }
 
 lora_status_t launch_ws_init(void *ws, hipStream_t s) {

@@ -51,7 +51,8 @@ def test_segments_examples_and_random():
     _seg_check([1, -1, 0, 1, 0, -1], 2)
     rng = np.random.default_rng(0)
     for T, n_slots in [(1, 1), (7, 3), (1023, 5), (1024, 5), (1025, 5), (3000, 1000),
-                       (5000, 16000), (70000, 32), (2240, 1000)]:
+                       (5000, 16000), (70000, 32), (2240, 1000), (8192, 8190), (8193, 100),
+                       (8192, 8191)]:
         ids = rng.integers(-1, n_slots, size=T).astype(np.int32)
         _seg_check(ids, n_slots)
     _seg_check(np.full(2000, -1, np.int32), 7)
