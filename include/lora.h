@@ -43,8 +43,9 @@
  *     read (and cleared) by lora_get_device_error.
  *   - No function keeps hidden state; all are reentrant.  Two calls that
  *     share a workspace must be ordered (same stream or events).
- *   - Results are deterministic: the same inputs give bitwise the same
- *     outputs (no floating-point atomics).
+ *   - Results are deterministic: the same inputs and workspace size give
+ *     bitwise the same outputs (no floating-point atomics; the workspace
+ *     size can change how the GEMM splits K, see lora_workspace_bytes).
  */
 #ifndef LORA_H_
 #define LORA_H_
