@@ -392,25 +392,31 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g0) {
     constexpr int RW = 2048 / BN, CPR = BN / 8, CHUNKS = BM / RW;
     constexpr int SP = 4;                                 // split partials loaded ahead
     constexpr int GP = 2;                                 // rank octets of B loaded ahead
-    const int tidx = blockIdx.x / CHUNKS, chunk = blockIdx.x % CHUNKS;
+    // Each XCD takes a contiguous range of (tile, row chunk) items, so it
+    // owns whole tiles: the B columns of a tile are fetched into one L2 for
+    // all of its rows (with chunk = XCD, every XCD read B for every column).
+    const int per = gridDim.x / kXcds, rem = gridDim.x % kXcds;
+    const int xcd = blockIdx.x % kXcds;
+    const int item = xcd * per + min(xcd, rem) + blockIdx.x / kXcds;
+    const int tidx = item / CHUNKS, chunk = item % CHUNKS;
     int tm, tn;
     grouped_tile(g0.tile_base + tidx, g0.n_tiles_m, g0.n_tiles_n, g0.col_strips, tm, tn);
     gemm_args g = g0;
     tn = select_slice(g, tn);
     const int T = g.T, N = g.N, R = g.max_rank;
-    const int r = chunk * RW + threadIdx.x / CPR, c = (threadIdx.x % CPR) * 8;
+    const int rloc = threadIdx.x / CPR, c = (threadIdx.x % CPR) * 8;
+    const int r = chunk * RW + rloc;                      // row within the tile
     const int p = tm * BM + r, n = tn * BN + c;
     __shared__ __attribute__((aligned(16))) float s_v[VP ? RW * 64 : 1];
-    // Loads that do not depend on the rank vector go out first (the first SP
-    // splits' partials, the row's adapter and its first GP rank octets of B),
-    // so their latency overlaps the summing of the rank partials below.
+    // Loads that do not depend on the rank vector go out first, so their
+    // latency overlaps the summing of the rank partials below: the row's
+    // adapter, the first SP splits' partials, and the adapter's first GP rank
+    // octets of B.  The B loads need the slot only, not its rank (a slot's
+    // ranks past its own are zero in the pool and are not summed), so they
+    // wait for one round trip (the id), not two.
     const int32_t t = (p < T && n < N) ? perm_row(g.perm, p, T) : -1;
-    int32_t raw = -1, rk = 0;
-    if (LORA && t >= 0) {
-        raw = g.ids[t];
-        if (raw >= 0 && raw < g.n_slots) rk = g.rank[raw];
-    }
-    const int G = (rk + 7) >> 3;
+    const int32_t raw = (LORA && t >= 0) ? g.ids[t] : -1;
+    const bool slot_ok = raw >= 0 && raw < g.n_slots;
     float4 pa[SP], pb[SP];
     uint4 bq[GP][8];
     if (t >= 0) {
@@ -421,16 +427,23 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g0) {
                 pa[sidx] = *reinterpret_cast<const float4 *>(src);
                 pb[sidx] = *reinterpret_cast<const float4 *>(src + 4);
             }
-        if (LORA && rk > 0) {
+        if (LORA && slot_ok) {
 #pragma unroll
             for (int gg = 0; gg < GP; ++gg)
-                if (gg < G) {
+                if (8 * gg < R) {
                     const uint16_t *bp = g.b + ((int64_t)raw * R * N + ((int64_t)gg * N + n) * 8);
 #pragma unroll
                     for (int q = 0; q < 8; ++q) bq[gg][q] = ldg16(bp + q * 8);
                 }
         }
     }
+    int32_t rk = 0;
+    float sc = 0.0f;
+    if (LORA && t >= 0 && slot_ok) {
+        rk = g.rank[raw];
+        sc = g.scale[raw];
+    }
+    const int G = (rk + 7) >> 3;
     if (VP) {
         for (int e = threadIdx.x; e < RW * R; e += 256) {
             const int rr = e / R, j = e % R;
@@ -470,7 +483,7 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g0) {
     }
     if (LORA && rk > 0) {
         // s * sum_j v[j] B[j][n..n+8]: rank octets in order, ranks of an octet in order
-        const float *vrow = VP ? s_v + (r - chunk * RW) * R : g.v + (int64_t)t * g.v_stride;
+        const float *vrow = VP ? s_v + rloc * R : g.v + (int64_t)t * g.v_stride;
         float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int gg = 0; gg < G; ++gg) {
             const float4 v0 = *reinterpret_cast<const float4 *>(vrow + gg * 8);
@@ -496,7 +509,6 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g0) {
                 d[q] = a;
             }
         }
-        const float sc = g.scale[raw];
 #pragma unroll
         for (int q = 0; q < 8; ++q) o[q] = fmaf(sc, d[q], o[q]);
     }
