@@ -91,6 +91,8 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
     // t = tn + i * n_tiles_n (i < 64 / R).  The A^T slices of those rows'
     // adapters ride along in every DMA stage (chunk c: row i, rank j, 8 k),
     // so x, already in LDS for the base product, is read from HBM once.
+    // All max_rank rows of a slot's A^T are loaded: those past the slot's
+    // rank are zero in the pool, so the first DMA waits on the ids alone.
     int64_t arow[AI > 0 ? AI : 1];
     int acol[AI > 0 ? AI : 1];
     const int R = g.max_rank;
@@ -104,10 +106,22 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
             int64_t off = -1;
             if (t < T) {
                 const int32_t id = g.ids[t];
-                if (id >= 0 && id < g.n_slots && j < g.rank[id]) off = ((int64_t)id * R + j) * K;
+                if (id >= 0 && id < g.n_slots) off = ((int64_t)id * R + j) * K;
             }
             arow[jj] = off;
             acol[jj] = 8 * q;
+        }
+    }
+    // Bad ids of those rows (outside [-1, n_slots) or an empty slot) are
+    // flagged once, by the first K range; the slot's rank is loaded now and
+    // checked after the K loop.
+    int32_t fl_t = -1, fl_id = -1, fl_rank = 1;
+    if (SH && split == 0 && tid < 64 / R) {
+        const int t = tn + tid * g.n_tiles_n;
+        if (t < T) {
+            fl_t = t;
+            fl_id = g.ids[t];
+            if (fl_id >= 0 && fl_id < g.n_slots) fl_rank = g.rank[fl_id];
         }
     }
     auto dma_stage = [&](int kt, int buf) {
@@ -291,6 +305,8 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
         vsum += __shfl_xor(vsum, 1, 64);
         vsum += __shfl_xor(vsum, 2, 64);
         if (sh_gq == 0 && sh_t < T) g.vpart[((int64_t)split * T + sh_t) * R + sh_j] = vsum;
+        if (fl_t >= 0 && fl_id != -1 && !(fl_id >= 0 && fl_id < g.n_slots && fl_rank > 0))
+            flag_bad_row(g.err, fl_t);
     }
 
     gemm_store_tile<BM, BN, WV, WR, SPLIT>(g, acc, reinterpret_cast<float *>(smem), s_meta_t, n0, w, lane,

@@ -386,7 +386,7 @@ __device__ __forceinline__ void gemm_store_tile(const gemm_args &g, f32x16_t (&a
 //                          (+ s_a * sum_j v[t][j] B_a[j][n..n+8])), t = perm[p].
 // The partials of an element are summed in split order (deterministic).
 // With VP (fused shrink) the rows' v are first summed from the K-range rank
-// partials (in range order) into LDS, and the first column tile flags bad ids.
+// partials (in range order) into LDS (the GEMM has flagged bad ids).
 template <bool LORA, bool VP, int BM, int BN>
 __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g0) {
     constexpr int RW = 2048 / BN, CPR = BN / 8, CHUNKS = BM / RW;
@@ -451,15 +451,9 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g0) {
             float sum = 0.0f;
             if (pp < T) {
                 const int32_t tt = perm_row(g.perm, pp, T);
-                if (tt >= 0) {
+                if (tt >= 0)
                     for (int sidx = 0; sidx < g.splits; ++sidx)
                         sum += g.vpart[((int64_t)sidx * T + tt) * R + j];
-                    if (j == 0 && tn == 0) {
-                        const int32_t rid = g.ids[tt];
-                        const bool ok = rid == -1 || (rid >= 0 && rid < g.n_slots && g.rank[rid] > 0);
-                        if (!ok) flag_bad_row(g.err, tt);
-                    }
-                }
             }
             s_v[rr * R + j] = sum;
         }
