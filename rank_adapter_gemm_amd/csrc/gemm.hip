@@ -221,7 +221,11 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
     const int sh_i = tid / (4 * R), sh_j = (tid >> 2) % R, sh_gq = tid & 3;
     const int sh_t = SH ? tn + sh_i * g.n_tiles_n : -1;
     float sh_acc = 0.0f;
-    auto shrink_stage = [&](int buf) {
+    // A stage's shrink operands are read from LDS at the stage hand-off and
+    // multiplied after the stage's first MFMA group, so the FMAs never wait
+    // on LDS in front of the matrix cores.
+    uint4 sh_xq[BK / 32], sh_aq[BK / 32];
+    auto shrink_load = [&](int buf) {
         if (!SH || sh_t >= T) return;
         const uint16_t *xs = smem + buf * STAGE;
         const uint16_t *as = xs + XSTAGE + WSTAGE;
@@ -229,11 +233,17 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
 #pragma unroll
         for (int h = 0; h < BK / 32; ++h) {                // this thread's BK / 32 chunks of 8 k
             const int c = (BK / 32) * sh_gq + h;
-            const uint4 xq = *reinterpret_cast<const uint4 *>(xs + r * BK + 8 * (c ^ swz_x<BK>(r)));
-            const uint4 aq = *reinterpret_cast<const uint4 *>(as + ((sh_i * R + sh_j) * ACH + c) * 8);
+            sh_xq[h] = *reinterpret_cast<const uint4 *>(xs + r * BK + 8 * (c ^ swz_x<BK>(r)));
+            sh_aq[h] = *reinterpret_cast<const uint4 *>(as + ((sh_i * R + sh_j) * ACH + c) * 8);
+        }
+    };
+    auto shrink_fma = [&]() {
+        if (!SH || sh_t >= T) return;
+#pragma unroll
+        for (int h = 0; h < BK / 32; ++h) {
             float xf[8], af[8];
-            vec16<LORA_BF16>::widen(xq, xf);
-            vec16<LORA_BF16>::widen(aq, af);
+            vec16<LORA_BF16>::widen(sh_xq[h], xf);
+            vec16<LORA_BF16>::widen(sh_aq[h], af);
 #pragma unroll
             for (int e = 0; e < 8; ++e) sh_acc = fmaf(xf[e], af[e], sh_acc);
         }
@@ -263,7 +273,7 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     load_frags(0, 0, af[0], bfr[0]);
-    if (SH && nk > 0) shrink_stage(0);
+    if (SH && nk > 0) shrink_load(0);
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt % NS;
 #pragma unroll
@@ -273,6 +283,7 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
                 load_frags(buf, ks + 1, af[nxt], bfr[nxt]);
                 mfmas(af[cur], bfr[cur], 0, RB);
                 sched_interleave<NREAD, RB * CB>();
+                if (SH && ks == 0) shrink_fma();
             } else {
                 // Stage hand-off, between the two halves of the last MFMAs of
                 // this stage: every wave has finished reading this stage from
@@ -290,7 +301,7 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
                 if (kt + NS < nk) dma_stage(kt + NS, buf);
                 __builtin_amdgcn_sched_barrier(0);
                 load_frags((kt + 1) % NS, 0, af[nxt], bfr[nxt]);
-                if (SH && kt + 1 < nk) shrink_stage((kt + 1) % NS);
+                if (SH && kt + 1 < nk) shrink_load((kt + 1) % NS);
                 mfmas(af[cur], bfr[cur], RB / 2, RB);
                 sched_interleave<NREAD, RB / 2 * CB>();
                 __builtin_amdgcn_sched_barrier(0);
