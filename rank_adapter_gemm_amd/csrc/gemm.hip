@@ -102,9 +102,9 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
             const int c = (w * AI + jj) * 64 + lane;
             const int i = c / (R * ACH), rem = c % (R * ACH);
             const int j = rem / ACH, q = rem % ACH;
-            const int t = tn + i * g.n_tiles_n;
+            const int t = m0 + tn + i * g.n_tiles_n;
             int64_t off = -1;
-            if (t < T) {
+            if (t < T && t - m0 < BM) {
                 const int32_t id = g.ids[t];
                 if (id >= 0 && id < g.n_slots) off = ((int64_t)id * R + j) * K;
             }
@@ -117,8 +117,8 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
     // checked after the K loop.
     int32_t fl_t = -1, fl_id = -1, fl_rank = 1;
     if (SH && split == 0 && tid < 64 / R) {
-        const int t = tn + tid * g.n_tiles_n;
-        if (t < T) {
+        const int t = m0 + tn + tid * g.n_tiles_n;
+        if (t < T && t - m0 < BM) {
             fl_t = t;
             fl_id = g.ids[t];
             if (fl_id >= 0 && fl_id < g.n_slots) fl_rank = g.rank[fl_id];
@@ -201,25 +201,32 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
     };
     constexpr int NREAD = RB + 2 * CB;                  // LDS reads per k-substep
 
-    // Per-row metadata of the tile (token row; usable adapter slot or -1).
-    __shared__ int32_t s_meta_t[BM], s_meta_id[BM];
-    for (int i = tid; i < BM; i += WV * 64) {
-        const int p = m0 + i;
-        const int32_t t = (p < T) ? perm_row(g.perm, p, T) : -1;
-        int32_t id = -1;
-        if (LORA && t >= 0) {
-            const int32_t raw = g.ids[t];
-            if (raw >= 0 && raw < g.n_slots && g.rank[raw] > 0) id = raw;
+    // Per-row metadata of a whole tile (token row; usable adapter slot or
+    // -1).  Split pieces keep none: they write every row of their partial
+    // tile (rows past T hold zeros) and the reduction skips those rows.
+    int32_t *s_meta_t = nullptr, *s_meta_id = nullptr;
+    if constexpr (!SPLIT) {
+        __shared__ int32_t s_meta_t_buf[BM], s_meta_id_buf[BM];
+        s_meta_t = s_meta_t_buf;
+        s_meta_id = s_meta_id_buf;
+        for (int i = tid; i < BM; i += WV * 64) {
+            const int p = m0 + i;
+            const int32_t t = (p < T) ? perm_row(g.perm, p, T) : -1;
+            int32_t id = -1;
+            if (LORA && t >= 0) {
+                const int32_t raw = g.ids[t];
+                if (raw >= 0 && raw < g.n_slots && g.rank[raw] > 0) id = raw;
+            }
+            s_meta_t[i] = t;
+            s_meta_id[i] = id;
         }
-        s_meta_t[i] = t;
-        s_meta_id[i] = id;
     }
 
     const int nk = (k_end - k_begin + BK - 1) / BK;
     constexpr int PER = XI + WI + AI;                     // DMA instructions per stage per wave
     // fused shrink: thread = (row slot i, rank j, k quarter gq) of a stage
     const int sh_i = tid / (4 * R), sh_j = (tid >> 2) % R, sh_gq = tid & 3;
-    const int sh_t = SH ? tn + sh_i * g.n_tiles_n : -1;
+    const int sh_t = SH && tn + sh_i * g.n_tiles_n < BM ? m0 + tn + sh_i * g.n_tiles_n : T;
     float sh_acc = 0.0f;
     // A stage's shrink operands are read from LDS at the stage hand-off and
     // multiplied after the stage's first MFMA group, so the FMAs never wait
@@ -413,7 +420,8 @@ __global__ void __launch_bounds__(256) k_gemm_f32(gemm_f32_args g) {
     }
 }
 
-template <int BM, int BN, int NS = 2, int WV = 4, int WR = 2, int BK = 64>
+// NST: stages of the split-K pieces (their LDS holds no row tables).
+template <int BM, int BN, int NS = 2, int WV = 4, int WR = 2, int BK = 64, int NST = NS>
 static void launch_cfg(gemm_args g, const gemm_plan &pl, bool lora, hipStream_t s) {
     if (pl.n_dp > 0) {
         g.tile_base = 0;
@@ -432,7 +440,7 @@ static void launch_cfg(gemm_args g, const gemm_plan &pl, bool lora, hipStream_t 
         g.n_tiles = pl.tail;
         g.splits = pl.splits;
         g.k_chunk = pl.k_chunk;
-        hipLaunchKernelGGL((k_gemm_bf16<false, BM, BN, BK, NS, true, false, WV, WR>), dim3(pl.tail * pl.splits),
+        hipLaunchKernelGGL((k_gemm_bf16<false, BM, BN, BK, NST, true, false, WV, WR>), dim3(pl.tail * pl.splits),
                            dim3(WV * 64), 0, s, g);
         const dim3 rgrid(pl.tail * (BM / (2048 / BN)));
         if (lora)
@@ -442,17 +450,28 @@ static void launch_cfg(gemm_args g, const gemm_plan &pl, bool lora, hipStream_t 
     }
 }
 
-// The fused shrink applies to the decode-sized split-K plan (one 256-row
-// tile, 64-column tiles): every row must be one of the 64 / R rows that some
-// column tile takes on.
-bool gemm_fused_shrink_ok(int32_t T, int32_t d_in, int32_t d_out, int32_t max_rank,
-                          size_t partial_bytes) {
+// The fused shrink applies to decode-sized split-K plans (T <= 256): every
+// row of a row tile must be one of the 64 / R rows that some column tile
+// takes on.  128 x 128 tiles (four stages in LDS) where their column tiles
+// cover the rows, else one 256-row tile of 64-column tiles (twice the
+// column tiles: max ranks 32 and 64 with narrower outputs).
+static bool fused_shrink_plan(int32_t T, int32_t d_in, int32_t d_out, int32_t max_rank, size_t partial_bytes,
+                              gemm_plan &pl) {
     if (T <= 0 || T > 256) return false;
     if (max_rank != 8 && max_rank != 16 && max_rank != 32 && max_rank != 64) return false;
-    const gemm_plan pl = plan_gemm(T, d_in, d_out, partial_bytes);
-    if (pl.n_dp != 0 || pl.splits <= 1 || pl.bm != 256 || pl.bn != 64) return false;
-    if (pl.splits > kMaxKSplit) return false;
-    return (int64_t)ceil_div(d_out, pl.bn) * (64 / max_rank) >= T;
+    for (int sq = 1; sq >= 0; --sq) {
+        pl = plan_gemm(T, d_in, d_out, partial_bytes, 64, sq == 1);
+        if (pl.n_dp != 0 || pl.splits <= 1 || pl.splits > kMaxKSplit) continue;
+        if (!(pl.bm == 128 && pl.bn == 128) && !(pl.bm == 256 && pl.bn == 64)) continue;
+        if ((int64_t)ceil_div(d_out, pl.bn) * (64 / max_rank) >= (T < pl.bm ? T : pl.bm)) return true;
+    }
+    return false;
+}
+
+bool gemm_fused_shrink_ok(int32_t T, int32_t d_in, int32_t d_out, int32_t max_rank,
+                          size_t partial_bytes) {
+    gemm_plan pl;
+    return fused_shrink_plan(T, d_in, d_out, max_rank, partial_bytes, pl);
 }
 
 lora_status_t launch_gemm_fused_shrink(const void *x, const void *W, void *y, int32_t T,
@@ -475,7 +494,8 @@ lora_status_t launch_gemm_fused_shrink(const void *x, const void *W, void *y, in
     g.ids = ids;
     g.v = nullptr;
     g.v_stride = pool->max_rank;
-    const gemm_plan pl = plan_gemm(T, g.K, g.N, partial_bytes);
+    gemm_plan pl;
+    if (!fused_shrink_plan(T, g.K, g.N, g.max_rank, partial_bytes, pl)) return LORA_ERR_UNSUPPORTED;
     g.n_tiles_m = ceil_div(T, pl.bm);
     g.n_tiles_n = ceil_div(g.N, pl.bn);
     g.tile_base = 0;
@@ -486,9 +506,17 @@ lora_status_t launch_gemm_fused_shrink(const void *x, const void *W, void *y, in
     g.a = (const uint16_t *)pool->a;
     g.vpart = vpart;
     g.err = err;
-    hipLaunchKernelGGL((k_gemm_bf16<false, 256, 64, 64, 3, true, true>), dim3(pl.tail * pl.splits), dim3(256),
-                       0, s, g);
-    hipLaunchKernelGGL((k_splitk_reduce<true, true, 256, 64>), dim3(pl.tail * (256 / 32)), dim3(256), 0, s, g);
+    if (pl.bm == 128) {
+        hipLaunchKernelGGL((k_gemm_bf16<false, 128, 128, 64, 4, true, true>), dim3(pl.tail * pl.splits),
+                           dim3(256), 0, s, g);
+        hipLaunchKernelGGL((k_splitk_reduce<true, true, 128, 128>), dim3(pl.tail * (128 / 16)), dim3(256), 0, s,
+                           g);
+    } else {
+        hipLaunchKernelGGL((k_gemm_bf16<false, 256, 64, 64, 3, true, true>), dim3(pl.tail * pl.splits),
+                           dim3(256), 0, s, g);
+        hipLaunchKernelGGL((k_splitk_reduce<true, true, 256, 64>), dim3(pl.tail * (256 / 32)), dim3(256), 0, s,
+                           g);
+    }
     return hip_status(hipGetLastError());
 }
 
@@ -499,7 +527,7 @@ lora_status_t launch_gemm_fused_shrink(const void *x, const void *W, void *y, in
 bool gemm_grouping_pays(int32_t T, int32_t K, const int32_t *Ns, int32_t n, size_t partial_bytes) {
     if (n < 2) return false;
     for (int i = 0; i < n; ++i) {
-        const gemm_plan pl = plan_gemm(T, K, Ns[i], partial_bytes);
+        const gemm_plan pl = plan_gemm(T, K, Ns[i], partial_bytes, 64, true);
         if (pl.bm != 256 || pl.bn != 256 || pl.tail != 0) return true;
     }
     return false;
@@ -526,7 +554,7 @@ lora_status_t launch_gemm_grouped(const void *x, const void *const *W, void *con
     g.ids = ids;
     g.v = v;
     g.v_stride = v_stride;
-    const gemm_plan pl = plan_gemm(T, g.K, Ns, n, partial ? partial_bytes : 0);
+    const gemm_plan pl = plan_gemm(T, g.K, Ns, n, partial ? partial_bytes : 0, 64, true);
     g.n_slices = n;
     int tn0 = 0;
     for (int i = 0; i < n; ++i) {
@@ -548,7 +576,7 @@ lora_status_t launch_gemm_grouped(const void *x, const void *const *W, void *con
     if (pl.bm == 256 && pl.bn == 256) launch_cfg<256, 256, 2, 8>(g, pl, true, s);
     else if (pl.bm == 256 && pl.bn == 128) launch_cfg<256, 128, 2, 8>(g, pl, true, s);
     else if (pl.bm == 256) launch_cfg<256, 64, 3>(g, pl, true, s);
-    else if (pl.bn == 128) launch_cfg<128, 128>(g, pl, true, s);
+    else if (pl.bn == 128) launch_cfg<128, 128, 2, 4, 2, 64, 4>(g, pl, true, s);
     else launch_cfg<128, 64>(g, pl, true, s);
     return hip_status(hipGetLastError());
 }
@@ -574,7 +602,7 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
         g.ids = ids;
         g.v = v;
         g.v_stride = v_stride;
-        const gemm_plan pl = plan_gemm(T, d_in, d_out, partial ? partial_bytes : 0);
+        const gemm_plan pl = plan_gemm(T, d_in, d_out, partial ? partial_bytes : 0, 64, true);
         g.n_tiles_m = ceil_div(T, pl.bm);
         g.n_tiles_n = ceil_div(d_out, pl.bn);
         g.col_strips = col_strips_pay(T, d_out, g.n_tiles_n);
@@ -588,7 +616,7 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
         if (pl.bm == 256 && pl.bn == 256) launch_cfg<256, 256, 2, 8>(g, pl, lora, s);
         else if (pl.bm == 256 && pl.bn == 128) launch_cfg<256, 128, 2, 8>(g, pl, lora, s);
         else if (pl.bm == 256) launch_cfg<256, 64, 3>(g, pl, lora, s);
-        else if (pl.bn == 128) launch_cfg<128, 128>(g, pl, lora, s);
+        else if (pl.bn == 128) launch_cfg<128, 128, 2, 4, 2, 64, 4>(g, pl, lora, s);
         else launch_cfg<128, 64>(g, pl, lora, s);
     } else {
         gemm_f32_args g;

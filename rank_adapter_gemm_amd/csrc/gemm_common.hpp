@@ -363,7 +363,7 @@ __device__ __forceinline__ void gemm_store_tile(const gemm_args &g, f32x16_t (&a
 #pragma unroll
         for (int k = 0; k < PASSES; ++k) {
             const int i = wm * WM + rb * 32 + rr + RPP * k;
-            const int32_t tk = s_meta_t[i];
+            const int32_t tk = s_meta_t ? s_meta_t[i] : 0;   // no row table: every row of a partial tile
             if (tk < 0 || n >= N) continue;
             const float *src = stage + (rr + RPP * k) * SLD + 8 * q;
             const float4 o0 = *reinterpret_cast<const float4 *>(src);
@@ -536,7 +536,8 @@ inline int tiles_n(const int32_t *Ns, int nN, int bn) {
     return t;
 }
 
-inline gemm_plan plan_gemm(int T, int K, const int32_t *Ns, int nN, size_t partial_bytes, int kgran = 64) {
+inline gemm_plan plan_gemm(int T, int K, const int32_t *Ns, int nN, size_t partial_bytes, int kgran = 64,
+                           bool square_small = false) {
     static const int cfg[4][2] = {{256, 256}, {256, 128}, {128, 128}, {128, 64}};
     for (int c = 0; c < 4; ++c) {
         const int bm = cfg[c][0], bn = cfg[c][1];
@@ -557,9 +558,13 @@ inline gemm_plan plan_gemm(int T, int K, const int32_t *Ns, int nN, size_t parti
         return p;
     }
     // Small grid (decode-sized T): split K.  One 256-row tile covers T <= 256,
-    // so W is read once; narrow 64-column tiles keep the number of fp32
-    // partial copies (written and read back) low for the same grid size.
-    const int bm = T <= 256 ? 256 : 128, bn = T <= 256 ? 64 : 128;
+    // so W is read once from HBM; narrow 64-column tiles keep the number of
+    // fp32 partial copies (written and read back) low for the same grid size.
+    // square_small (bf16): 128 x 128 tiles instead, whose stages are a sixth
+    // smaller (x and W 32 KB against 40), so four fit in LDS; the two row
+    // tiles of a column run on one XCD and share W through its L2.
+    const bool wide = T <= 256 && !square_small;
+    const int bm = wide ? 256 : 128, bn = wide ? 64 : 128;
     const int tiles = ceil_div(T, bm) * tiles_n(Ns, nN, bn);
     int splits = ceil_div(256, tiles);
     const int max_by_k = K / 256 > 0 ? K / 256 : 1;
@@ -575,9 +580,10 @@ inline gemm_plan plan_gemm(int T, int K, const int32_t *Ns, int nN, size_t parti
 }
 
 // One output of width N.
-inline gemm_plan plan_gemm(int T, int K, int N, size_t partial_bytes, int kgran = 64) {
+inline gemm_plan plan_gemm(int T, int K, int N, size_t partial_bytes, int kgran = 64,
+                           bool square_small = false) {
     const int32_t n = N;
-    return plan_gemm(T, K, &n, 1, partial_bytes, kgran);
+    return plan_gemm(T, K, &n, 1, partial_bytes, kgran, square_small);
 }
 
 }  // namespace lora

@@ -1,6 +1,7 @@
 """GPU parity of the decode-sized path where the shrink runs inside the
-split-K base GEMM (batches of at most 256 rows in BGMV mode, 64-column
-tiles): every row against the fp64 oracle, for each supported max rank,
+split-K base GEMM (batches of at most 256 rows in BGMV mode; 128 x 128
+tiles, or one 256-row tile of 64-column tiles where the wider column tiles
+are too few to cover the rows): every row against the fp64 oracle, for each supported max rank,
 with ranks below the maximum, base rows, an empty slot and out-of-range ids
 (which must be flagged and computed as base rows), plus bitwise determinism
 and agreement with the unfused path (separate shrink kernel)."""
@@ -23,14 +24,14 @@ def _lib():
     L.load()
 
 
-# (T, d_in, d_out, max_rank, ranks): each shape gives a split-K plan of one
-# 256-row tile by 64-column tiles with at least T / (64 / max_rank) tiles.
+# (T, d_in, d_out, max_rank, ranks): each shape gives a split-K plan whose
+# column tiles, 64 / max_rank rows each, cover a row tile.
 CASES = [
-    (256, 1024, 4096, 16, [16, 16, 7, 16, 0, 12]),
-    (200, 2048, 2048, 8, [8, 3, 0, 5]),
-    (100, 1024, 4096, 32, [32, 17, 8, 0, 32]),
-    (37, 2048, 4096, 64, [64, 8, 33, 0]),
-    (1, 512, 1024, 16, [16, 4]),
+    (256, 1024, 4096, 16, [16, 16, 7, 16, 0, 12]),   # 128 x 128, two row tiles
+    (200, 2048, 2048, 8, [8, 3, 0, 5]),              # 128 x 128, ragged second row tile
+    (100, 1024, 4096, 32, [32, 17, 8, 0, 32]),       # 256 x 64 (32 wide tiles x 2 rows < 100)
+    (37, 2048, 4096, 64, [64, 8, 33, 0]),            # 256 x 64
+    (1, 512, 1024, 16, [16, 4]),                     # 128 x 128, one row
 ]
 
 
