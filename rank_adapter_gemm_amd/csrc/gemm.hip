@@ -37,7 +37,7 @@ template <int BM, int BN, int BK, int NS, bool SH, int WV = 4, int WR = 2> struc
     static constexpr int ACH = BK / 8, ASTAGE = SH ? 64 * BK : 0;
     static constexpr int STAGE = XSTAGE + WSTAGE + ASTAGE;  // uint16 elements per ring stage
     static constexpr int XI = BM * XCH / (64 * WV), WI = BK * WCH / (64 * WV);   // DMA instructions per wave
-    static constexpr int AI = SH ? BK / 32 : 0;
+    static constexpr int AI = SH ? BK / (8 * WV) : 0;              // A^T stage: 8 BK chunks over WV waves
     static constexpr int SLD = WN + 4;                      // epilogue staging row stride (floats)
     static constexpr int EPI = WV * 32 * SLD * 4;            // epilogue LDS bytes
     static constexpr int LDS = NS * STAGE * 2 > EPI ? NS * STAGE * 2 : EPI;
@@ -46,7 +46,7 @@ template <int BM, int BN, int BK, int NS, bool SH, int WV = 4, int WR = 2> struc
 template <bool LORA, int BM, int BN, int BK, int NS, bool SPLIT, bool SH = false, int WV = 4, int WR = 2>
 __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
     static_assert(!SH || SPLIT, "the fused shrink runs in split-K mode");
-    static_assert(!SH || WV == 4, "the fused shrink maps 256 threads");
+    static_assert(!SH || (WV == 4 || WV == 8), "the fused shrink maps 4 or 8 threads to a (row, rank) pair");
     typedef gemm_cfg<BM, BN, BK, NS, SH, WV, WR> C;
     constexpr int WM = C::WM, WN = C::WN, RB = C::RB, CB = C::CB;
     constexpr int XCH = C::XCH, WCH = C::WCH, XSTAGE = C::XSTAGE, WSTAGE = C::WSTAGE;
@@ -225,21 +225,23 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
     const int nk = (k_end - k_begin + BK - 1) / BK;
     constexpr int PER = XI + WI + AI;                     // DMA instructions per stage per wave
     // fused shrink: thread = (row slot i, rank j, k quarter gq) of a stage
-    const int sh_i = tid / (4 * R), sh_j = (tid >> 2) % R, sh_gq = tid & 3;
+    // (64 pairs of row slot and rank; WV k groups per pair)
+    const int sh_i = tid / (WV * R), sh_j = (tid / WV) % R, sh_gq = tid % WV;
     const int sh_t = SH && tn + sh_i * g.n_tiles_n < BM ? m0 + tn + sh_i * g.n_tiles_n : T;
     float sh_acc = 0.0f;
     // A stage's shrink operands are read from LDS at the stage hand-off and
     // multiplied after the stage's first MFMA group, so the FMAs never wait
     // on LDS in front of the matrix cores.
-    uint4 sh_xq[BK / 32], sh_aq[BK / 32];
+    constexpr int SHC = ACH / WV;                        // chunks of 8 k per thread and stage
+    uint4 sh_xq[SHC], sh_aq[SHC];
     auto shrink_load = [&](int buf) {
         if (!SH || sh_t >= T) return;
         const uint16_t *xs = smem + buf * STAGE;
         const uint16_t *as = xs + XSTAGE + WSTAGE;
         const int r = sh_t - m0;
 #pragma unroll
-        for (int h = 0; h < BK / 32; ++h) {                // this thread's BK / 32 chunks of 8 k
-            const int c = (BK / 32) * sh_gq + h;
+        for (int h = 0; h < SHC; ++h) {                    // this thread's chunks of 8 k
+            const int c = SHC * sh_gq + h;
             sh_xq[h] = *reinterpret_cast<const uint4 *>(xs + r * BK + 8 * (c ^ swz_x<BK>(r)));
             sh_aq[h] = *reinterpret_cast<const uint4 *>(as + ((sh_i * R + sh_j) * ACH + c) * 8);
         }
@@ -247,7 +249,7 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
     auto shrink_fma = [&]() {
         if (!SH || sh_t >= T) return;
 #pragma unroll
-        for (int h = 0; h < BK / 32; ++h) {
+        for (int h = 0; h < SHC; ++h) {
             float xf[8], af[8];
             vec16<LORA_BF16>::widen(sh_xq[h], xf);
             vec16<LORA_BF16>::widen(sh_aq[h], af);
@@ -318,10 +320,10 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (SH) {
-        // rank partial of this K range: sum the four 16-k groups (adjacent lanes)
+        // rank partial of this K range: sum the WV k groups (adjacent lanes)
         float vsum = sh_acc;
-        vsum += __shfl_xor(vsum, 1, 64);
-        vsum += __shfl_xor(vsum, 2, 64);
+#pragma unroll
+        for (int o = 1; o < WV; o <<= 1) vsum += __shfl_xor(vsum, o, 64);
         if (sh_gq == 0 && sh_t < T) g.vpart[((int64_t)split * T + sh_t) * R + sh_j] = vsum;
         if (fl_t >= 0 && fl_id != -1 && !(fl_id >= 0 && fl_id < g.n_slots && fl_rank > 0))
             flag_bad_row(g.err, fl_t);
@@ -420,8 +422,9 @@ __global__ void __launch_bounds__(256) k_gemm_f32(gemm_f32_args g) {
     }
 }
 
-// NST: stages of the split-K pieces (their LDS holds no row tables).
-template <int BM, int BN, int NS = 2, int WV = 4, int WR = 2, int BK = 64, int NST = NS>
+// NST, WVT: stages and wavefronts of the split-K pieces (their LDS holds no
+// row tables).
+template <int BM, int BN, int NS = 2, int WV = 4, int WR = 2, int BK = 64, int NST = NS, int WVT = WV>
 static void launch_cfg(gemm_args g, const gemm_plan &pl, bool lora, hipStream_t s) {
     if (pl.n_dp > 0) {
         g.tile_base = 0;
@@ -440,8 +443,8 @@ static void launch_cfg(gemm_args g, const gemm_plan &pl, bool lora, hipStream_t 
         g.n_tiles = pl.tail;
         g.splits = pl.splits;
         g.k_chunk = pl.k_chunk;
-        hipLaunchKernelGGL((k_gemm_bf16<false, BM, BN, BK, NST, true, false, WV, WR>), dim3(pl.tail * pl.splits),
-                           dim3(WV * 64), 0, s, g);
+        hipLaunchKernelGGL((k_gemm_bf16<false, BM, BN, BK, NST, true, false, WVT, WR>), dim3(pl.tail * pl.splits),
+                           dim3(WVT * 64), 0, s, g);
         const dim3 rgrid(pl.tail * (BM / (2048 / BN)));
         if (lora)
             hipLaunchKernelGGL((k_splitk_reduce<true, false, BM, BN>), rgrid, dim3(256), 0, s, g);
@@ -507,8 +510,8 @@ lora_status_t launch_gemm_fused_shrink(const void *x, const void *W, void *y, in
     g.vpart = vpart;
     g.err = err;
     if (pl.bm == 128) {
-        hipLaunchKernelGGL((k_gemm_bf16<false, 128, 128, 64, 4, true, true>), dim3(pl.tail * pl.splits),
-                           dim3(256), 0, s, g);
+        hipLaunchKernelGGL((k_gemm_bf16<false, 128, 128, 64, 4, true, true, 8, 2>), dim3(pl.tail * pl.splits),
+                           dim3(512), 0, s, g);
         hipLaunchKernelGGL((k_splitk_reduce<true, true, 128, 128>), dim3(pl.tail * (128 / 16)), dim3(256), 0, s,
                            g);
     } else {
@@ -576,7 +579,7 @@ lora_status_t launch_gemm_grouped(const void *x, const void *const *W, void *con
     if (pl.bm == 256 && pl.bn == 256) launch_cfg<256, 256, 2, 8>(g, pl, true, s);
     else if (pl.bm == 256 && pl.bn == 128) launch_cfg<256, 128, 2, 8>(g, pl, true, s);
     else if (pl.bm == 256) launch_cfg<256, 64, 3>(g, pl, true, s);
-    else if (pl.bn == 128) launch_cfg<128, 128, 2, 4, 2, 64, 4>(g, pl, true, s);
+    else if (pl.bn == 128) launch_cfg<128, 128, 2, 4, 2, 64, 4, 8>(g, pl, true, s);
     else launch_cfg<128, 64>(g, pl, true, s);
     return hip_status(hipGetLastError());
 }
@@ -616,7 +619,7 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
         if (pl.bm == 256 && pl.bn == 256) launch_cfg<256, 256, 2, 8>(g, pl, lora, s);
         else if (pl.bm == 256 && pl.bn == 128) launch_cfg<256, 128, 2, 8>(g, pl, lora, s);
         else if (pl.bm == 256) launch_cfg<256, 64, 3>(g, pl, lora, s);
-        else if (pl.bn == 128) launch_cfg<128, 128, 2, 4, 2, 64, 4>(g, pl, lora, s);
+        else if (pl.bn == 128) launch_cfg<128, 128, 2, 4, 2, 64, 4, 8>(g, pl, lora, s);
         else launch_cfg<128, 64>(g, pl, lora, s);
     } else {
         gemm_f32_args g;
