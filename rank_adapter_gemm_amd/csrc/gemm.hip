@@ -578,7 +578,6 @@ lora_status_t launch_gemm_grouped(const void *x, const void *const *W, void *con
     g.partial = partial;
     if (pl.bm == 256 && pl.bn == 256) launch_cfg<256, 256, 2, 8>(g, pl, true, s);
     else if (pl.bm == 256 && pl.bn == 128) launch_cfg<256, 128, 2, 8>(g, pl, true, s);
-    else if (pl.bm == 256) launch_cfg<256, 64, 3>(g, pl, true, s);
     else if (pl.bn == 128) launch_cfg<128, 128, 2, 4, 2, 64, 4, 8>(g, pl, true, s);
     else launch_cfg<128, 64>(g, pl, true, s);
     return hip_status(hipGetLastError());
@@ -618,7 +617,6 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
         // the other waits on LDS or the barrier); smaller tiles 4.
         if (pl.bm == 256 && pl.bn == 256) launch_cfg<256, 256, 2, 8>(g, pl, lora, s);
         else if (pl.bm == 256 && pl.bn == 128) launch_cfg<256, 128, 2, 8>(g, pl, lora, s);
-        else if (pl.bm == 256) launch_cfg<256, 64, 3>(g, pl, lora, s);
         else if (pl.bn == 128) launch_cfg<128, 128, 2, 4, 2, 64, 4, 8>(g, pl, lora, s);
         else launch_cfg<128, 64>(g, pl, lora, s);
     } else {

@@ -369,7 +369,8 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_fp8(gemm_args g) {
                                          tidx, split);
 }
 
-template <int BM, int BN, int NS = 2, int WV = 4, int WR = 2>
+// NST, WVT: stages and wavefronts of the split-K pieces.
+template <int BM, int BN, int NS = 2, int WV = 4, int WR = 2, int NST = NS, int WVT = WV>
 static void launch_fp8_cfg(gemm_args g, const gemm_plan &pl, bool lora, hipStream_t s) {
     if (pl.n_dp > 0) {
         g.tile_base = 0;
@@ -386,8 +387,8 @@ static void launch_fp8_cfg(gemm_args g, const gemm_plan &pl, bool lora, hipStrea
         g.n_tiles = pl.tail;
         g.splits = pl.splits;
         g.k_chunk = pl.k_chunk;
-        hipLaunchKernelGGL((k_gemm_fp8<false, BM, BN, NS, true, WV, WR>), dim3(pl.tail * pl.splits), dim3(WV * 64),
-                           0, s, g);
+        hipLaunchKernelGGL((k_gemm_fp8<false, BM, BN, NST, true, WVT, WR>), dim3(pl.tail * pl.splits),
+                           dim3(WVT * 64), 0, s, g);
         const dim3 rgrid(pl.tail * (BM / (2048 / BN)));
         if (lora)
             hipLaunchKernelGGL((k_splitk_reduce<true, false, BM, BN>), rgrid, dim3(256), 0, s, g);
@@ -429,7 +430,7 @@ lora_status_t launch_gemm_fp8(const uint8_t *xq, const float *xs, const uint8_t 
     g.ids = ids;
     g.v = v;
     g.v_stride = v_stride;
-    const gemm_plan pl = plan_gemm(T, d_in, d_out, partial ? partial_bytes : 0, 128);
+    const gemm_plan pl = plan_gemm(T, d_in, d_out, partial ? partial_bytes : 0, 128, true);
     g.n_tiles_m = ceil_div(T, pl.bm);
     g.n_tiles_n = ceil_div(d_out, pl.bn);
     g.col_strips = col_strips_pay(T, d_out, g.n_tiles_n);
@@ -437,8 +438,7 @@ lora_status_t launch_gemm_fp8(const uint8_t *xq, const float *xs, const uint8_t 
     const bool lora = pool != nullptr;
     if (pl.bm == 256 && pl.bn == 256) launch_fp8_cfg<256, 256, 2, 4>(g, pl, lora, s);
     else if (pl.bm == 256 && pl.bn == 128) launch_fp8_cfg<256, 128, 2, 8>(g, pl, lora, s);
-    else if (pl.bm == 256) launch_fp8_cfg<256, 64, 3>(g, pl, lora, s);
-    else if (pl.bn == 128) launch_fp8_cfg<128, 128>(g, pl, lora, s);
+    else if (pl.bn == 128) launch_fp8_cfg<128, 128, 2, 4, 2, 4, 8>(g, pl, lora, s);
     else launch_fp8_cfg<128, 64>(g, pl, lora, s);
     return hip_status(hipGetLastError());
 }

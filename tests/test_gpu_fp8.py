@@ -11,8 +11,9 @@ adapters) against the fp64 oracle in oracle/fp8.py.
   |s| sum_j |u_j| |B_jn|) and the matrix cores' accumulation of FP8
   products (below 2^-12 of each 64-product block's largest term, so 2^-11
   of S = s_x s_w sum_k |dq(xq) dq(wq)|).
-  Shapes are chosen so every tile plan runs: 128x64 whole tiles, 128x128 and
-  256x64 split-K, 256x128 whole tiles, 256x256 whole tiles plus a split tail.
+  Shapes are chosen so every tile plan runs: 128x64 whole tiles, 128x128
+  split-K (eight wavefronts), 256x128 whole tiles, 256x256 whole tiles plus a
+  split tail.
 * The low-rank term is really added (a delta-sensitive check), bad ids are
   flagged and computed as base rows, T = 0 is a no-op, and the decode-sized
   workload at full size matches on sampled rows in the benchmark's launch
@@ -83,7 +84,7 @@ def test_quantize_weight_bitwise(K, N):
 GEMM_SHAPES = [
     (300, 208, 264),    # 128x64 whole tiles (K too short to split), ragged T and N
     (300, 1040, 264),   # 128x128 split-K, ragged K
-    (37, 2048, 1024),   # 256x64 split-K (decode-sized)
+    (37, 2048, 1024),   # 128x128 split-K (decode-sized, eight K ranges)
     (2048, 512, 3584),  # 256x128 whole tiles
     (4352, 1024, 4096), # 256x256 whole tiles plus a split-K tail round
     (300, 256, 16408),  # 256x128 in column bands (129 column tiles, the last band one tile wide)
