@@ -462,8 +462,8 @@ static bool fused_shrink_plan(int32_t T, int32_t d_in, int32_t d_out, int32_t ma
                               gemm_plan &pl) {
     if (T <= 0 || T > 256) return false;
     if (max_rank != 8 && max_rank != 16 && max_rank != 32 && max_rank != 64) return false;
-    for (int sq = 1; sq >= 0; --sq) {
-        pl = plan_gemm(T, d_in, d_out, partial_bytes, 64, sq == 1);
+    for (int wide = 0; wide <= 1; ++wide) {
+        pl = plan_gemm(T, d_in, d_out, partial_bytes, 64, wide == 1);
         if (pl.n_dp != 0 || pl.splits <= 1 || pl.splits > kMaxKSplit) continue;
         if (!(pl.bm == 128 && pl.bn == 128) && !(pl.bm == 256 && pl.bn == 64)) continue;
         if ((int64_t)ceil_div(d_out, pl.bn) * (64 / max_rank) >= (T < pl.bm ? T : pl.bm)) return true;
@@ -530,7 +530,7 @@ lora_status_t launch_gemm_fused_shrink(const void *x, const void *W, void *y, in
 bool gemm_grouping_pays(int32_t T, int32_t K, const int32_t *Ns, int32_t n, size_t partial_bytes) {
     if (n < 2) return false;
     for (int i = 0; i < n; ++i) {
-        const gemm_plan pl = plan_gemm(T, K, Ns[i], partial_bytes, 64, true);
+        const gemm_plan pl = plan_gemm(T, K, Ns[i], partial_bytes);
         if (pl.bm != 256 || pl.bn != 256 || pl.tail != 0) return true;
     }
     return false;
@@ -557,7 +557,7 @@ lora_status_t launch_gemm_grouped(const void *x, const void *const *W, void *con
     g.ids = ids;
     g.v = v;
     g.v_stride = v_stride;
-    const gemm_plan pl = plan_gemm(T, g.K, Ns, n, partial ? partial_bytes : 0, 64, true);
+    const gemm_plan pl = plan_gemm(T, g.K, Ns, n, partial ? partial_bytes : 0);
     g.n_slices = n;
     int tn0 = 0;
     for (int i = 0; i < n; ++i) {
@@ -604,7 +604,7 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
         g.ids = ids;
         g.v = v;
         g.v_stride = v_stride;
-        const gemm_plan pl = plan_gemm(T, d_in, d_out, partial ? partial_bytes : 0, 64, true);
+        const gemm_plan pl = plan_gemm(T, d_in, d_out, partial ? partial_bytes : 0);
         g.n_tiles_m = ceil_div(T, pl.bm);
         g.n_tiles_n = ceil_div(d_out, pl.bn);
         g.col_strips = col_strips_pay(T, d_out, g.n_tiles_n);
@@ -613,8 +613,9 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
         g.vpart = nullptr;
         g.err = nullptr;
         const bool lora = pool != nullptr;
-        // 256-row tiles run 8 wavefronts (two per SIMD: one issues MFMAs while
-        // the other waits on LDS or the barrier); smaller tiles 4.
+        // 256-row tiles and the 128 x 128 split pieces run 8 wavefronts (two
+        // per SIMD: one issues MFMAs while the other waits on LDS or the
+        // barrier); other tiles 4.
         if (pl.bm == 256 && pl.bn == 256) launch_cfg<256, 256, 2, 8>(g, pl, lora, s);
         else if (pl.bm == 256 && pl.bn == 128) launch_cfg<256, 128, 2, 8>(g, pl, lora, s);
         else if (pl.bn == 128) launch_cfg<128, 128, 2, 4, 2, 64, 4, 8>(g, pl, lora, s);

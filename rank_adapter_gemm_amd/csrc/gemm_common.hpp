@@ -537,7 +537,7 @@ inline int tiles_n(const int32_t *Ns, int nN, int bn) {
 }
 
 inline gemm_plan plan_gemm(int T, int K, const int32_t *Ns, int nN, size_t partial_bytes, int kgran = 64,
-                           bool square_small = false) {
+                           bool wide_small = false) {
     static const int cfg[4][2] = {{256, 256}, {256, 128}, {128, 128}, {128, 64}};
     for (int c = 0; c < 4; ++c) {
         const int bm = cfg[c][0], bn = cfg[c][1];
@@ -557,13 +557,13 @@ inline gemm_plan plan_gemm(int T, int K, const int32_t *Ns, int nN, size_t parti
         }
         return p;
     }
-    // Small grid (decode-sized T): split K.  One 256-row tile covers T <= 256,
-    // so W is read once from HBM; narrow 64-column tiles keep the number of
-    // fp32 partial copies (written and read back) low for the same grid size.
-    // square_small (bf16): 128 x 128 tiles instead, whose stages are a sixth
-    // smaller (x and W 32 KB against 40), so four fit in LDS; the two row
-    // tiles of a column run on one XCD and share W through its L2.
-    const bool wide = T <= 256 && !square_small;
+    // Small grid (decode-sized T): split K, on 128 x 128 tiles.  Their x and
+    // W stages are 32 KB, a fifth less than one 256-row tile of 64 columns
+    // (which reads W once but x four times as often), so four stages fit in
+    // LDS; the two row tiles of a column run on one XCD and share W through
+    // its L2.  wide_small asks for the 256 x 64 tiles (T <= 256): twice the
+    // column tiles, which the fused shrink needs for max ranks 32 and 64.
+    const bool wide = T <= 256 && wide_small;
     const int bm = wide ? 256 : 128, bn = wide ? 64 : 128;
     const int tiles = ceil_div(T, bm) * tiles_n(Ns, nN, bn);
     int splits = ceil_div(256, tiles);
@@ -581,9 +581,9 @@ inline gemm_plan plan_gemm(int T, int K, const int32_t *Ns, int nN, size_t parti
 
 // One output of width N.
 inline gemm_plan plan_gemm(int T, int K, int N, size_t partial_bytes, int kgran = 64,
-                           bool square_small = false) {
+                           bool wide_small = false) {
     const int32_t n = N;
-    return plan_gemm(T, K, &n, 1, partial_bytes, kgran, square_small);
+    return plan_gemm(T, K, &n, 1, partial_bytes, kgran, wide_small);
 }
 
 }  // namespace lora

@@ -430,7 +430,7 @@ lora_status_t launch_gemm_fp8(const uint8_t *xq, const float *xs, const uint8_t 
     g.ids = ids;
     g.v = v;
     g.v_stride = v_stride;
-    const gemm_plan pl = plan_gemm(T, d_in, d_out, partial ? partial_bytes : 0, 128, true);
+    const gemm_plan pl = plan_gemm(T, d_in, d_out, partial ? partial_bytes : 0, 128);
     g.n_tiles_m = ceil_div(T, pl.bm);
     g.n_tiles_n = ceil_div(d_out, pl.bn);
     g.col_strips = col_strips_pay(T, d_out, g.n_tiles_n);
