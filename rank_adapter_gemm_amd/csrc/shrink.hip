@@ -89,21 +89,20 @@ __global__ void __launch_bounds__(512) k_shrink_rows(const typename elem<DT>::T 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int32_t id = ids[t];
     const bool in_range = id >= 0 && id < n_slots;
-    bool any_empty = false;
-    if (in_range)
-        for (int sl = 0; sl < ss.n; ++sl) any_empty |= ss.rank[sl][id] <= 0;
-    if (tid == 0 && ((id < -1 || id >= n_slots) || (in_range && any_empty))) flag_bad_row(err, t);
     const int VS = ss.n * max_rank;                       // v row stride
     const E *xt = x + (size_t)t * d_in;
     // One slice after the other: x[t] comes from HBM for the first and from
     // the cache for the rest.
     for (int sl = 0; sl < ss.n; ++sl) {
-    const int32_t r = in_range ? ss.rank[sl][id] : 0;
     float *vt = v + (size_t)t * VS + sl * max_rank;
-    if (r <= 0) {                                         // uniform: no adapter in this slice
+    if (!in_range) {                                      // uniform: a base row (or a bad id)
         for (int j = tid; j < max_rank; j += NW * 64) vt[j] = 0.0f;
         continue;
     }
+    // The slot's rank only masks the sums: the loads cover max_rank rows
+    // (a slot's rows past its rank are zero in the pool), so they go out
+    // together with the rank's, one round trip after the id.
+    const int32_t r = ss.rank[sl][id];
     const E *At = reinterpret_cast<const E *>(ss.a[sl]) + (size_t)id * max_rank * d_in;
     float acc[RM];
 #pragma unroll
@@ -114,13 +113,13 @@ __global__ void __launch_bounds__(512) k_shrink_rows(const typename elem<DT>::T 
         float xf[VN];
 #pragma unroll
         for (int c = 0; c < RM; c += RC) {
-            if (c < r) {                                  // uniform: rows left in this slot
-                // RC independent loads in flight; rows past the rank re-read
-                // row r-1 (a cache hit) and are masked out below.
+            if (c < max_rank) {                           // uniform: rows left in the slot
+                // RC independent loads in flight; rows past max_rank re-read
+                // the last row (a cache hit) and are masked out below.
                 uint4 aq[RC];
 #pragma unroll
                 for (int j = 0; j < RC; ++j) {
-                    const int row = min(c + j, r - 1);
+                    const int row = min(c + j, max_rank - 1);
                     aq[j] = ldg16(At + (size_t)row * d_in + (size_t)kv * VN);
                 }
                 if (c == 0) vec16<DT>::widen(xq, xf);
@@ -152,6 +151,14 @@ __global__ void __launch_bounds__(512) k_shrink_rows(const typename elem<DT>::T 
         vt[j] = sum;
     }
     __syncthreads();                                      // s_red is reused by the next slice
+    }
+    // Bad ids (out of range, or a slot empty in some slice), flagged last so
+    // that no load above waits on the ranks.
+    if (tid == 0) {
+        bool any_empty = false;
+        if (in_range)
+            for (int sl = 0; sl < ss.n; ++sl) any_empty |= ss.rank[sl][id] <= 0;
+        if ((id < -1 || id >= n_slots) || any_empty) flag_bad_row(err, t);
     }
 }
 
