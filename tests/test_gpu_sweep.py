@@ -121,7 +121,7 @@ class Layer:
                            rows=rows)["y"]
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(64))
 def test_sweep_forward(seed):
     c = draw_case(seed)
     dtype = torch.float32 if c["rng"].random() < 0.25 else torch.bfloat16
@@ -146,7 +146,7 @@ def test_sweep_forward(seed):
             assert L.lora_get_device_error(ws.buf) == c["first_bad"], w
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(20))
 def test_sweep_sliced(seed):
     rng = np.random.default_rng(20_000 + seed)
     n = int(rng.integers(2, 5))
@@ -176,7 +176,7 @@ def test_sweep_sliced(seed):
             assert L.lora_get_device_error(ws.buf) == c["first_bad"], what
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(20))
 def test_sweep_fp8(seed):
     c = draw_case(200 + seed, k_quant=16)
     what = describe(c, " fp8")
