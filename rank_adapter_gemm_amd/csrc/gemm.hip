@@ -224,8 +224,8 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
 
     const int nk = (k_end - k_begin + BK - 1) / BK;
     constexpr int PER = XI + WI + AI;                     // DMA instructions per stage per wave
-    // fused shrink: thread = (row slot i, rank j, k quarter gq) of a stage
-    // (64 pairs of row slot and rank; WV k groups per pair)
+    // fused shrink: thread = (row slot i, rank j, k group gq) of a stage:
+    // 64 pairs of row slot and rank, WV groups of the stage's k per pair
     const int sh_i = tid / (WV * R), sh_j = (tid / WV) % R, sh_gq = tid % WV;
     const int sh_t = SH && tn + sh_i * g.n_tiles_n < BM ? m0 + tn + sh_i * g.n_tiles_n : T;
     float sh_acc = 0.0f;
