@@ -94,7 +94,8 @@ typedef enum { LORA_MODE_AUTO = 0, LORA_MODE_BGMV = 1, LORA_MODE_SGMV = 2 } lora
  * Internal layout, per slot s (the library's choice, documented for tools):
  *   a: A transposed, [max_rank][d_in]           -- rank rows contiguous over d_in
  *   b: B in rank octets, [max_rank/8][d_out][8] -- 8 ranks of one column contiguous
- * rows/octets at and beyond the slot's rank are zero.
+ * rows/octets at and beyond the slot's rank are zero.  The kernels rely on
+ * that: some read a slot's max_rank rows whole and mask by its rank later.
  */
 typedef struct {
     int32_t n_slots, d_in, d_out, max_rank;
