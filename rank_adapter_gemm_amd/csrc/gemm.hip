@@ -86,13 +86,14 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
         wrow[j] = k;
         wcol[j] = n0 + 8 * (slot ^ swz_w<BN>(k));
     }
-    // Fused shrink (decode-sized batches, one M tile): this workgroup also
-    // computes the rank partials v[t][j] over its K range for the rows
-    // t = tn + i * n_tiles_n (i < 64 / R).  The A^T slices of those rows'
-    // adapters ride along in every DMA stage (chunk c: row i, rank j, 8 k),
-    // so x, already in LDS for the base product, is read from HBM once.
-    // All max_rank rows of a slot's A^T are loaded: those past the slot's
-    // rank are zero in the pool, so the first DMA waits on the ids alone.
+    // Fused shrink (decode-sized batches): this workgroup also computes the
+    // rank partials v[t][j] over its K range for the rows
+    // t = m0 + tn + i * n_tiles_n (i < 64 / R) that fall in its row tile.
+    // The A^T slices of those rows' adapters ride along in every DMA stage
+    // (chunk c: row i, rank j, 8 k), so x, already in LDS for the base
+    // product, is read from HBM once.  All max_rank rows of a slot's A^T are
+    // loaded: those past the slot's rank are zero in the pool, so the first
+    // DMA waits on the ids alone.
     int64_t arow[AI > 0 ? AI : 1];
     int acol[AI > 0 ? AI : 1];
     const int R = g.max_rank;
