@@ -423,10 +423,15 @@ lora_status_t lora_linear_forward_fp8(const void *x, const uint8_t *wq, const fl
     }
     uint8_t *xq = ws_ptr<uint8_t>(ws, L.xq);
     float *xs = ws_ptr<float>(ws, L.xs);
-    st = launch_quant_rows_fp8(x, T, pool->d_in, xq, xs, s);
-    if (st != LORA_OK) return st;
     float *v = ws_ptr<float>(ws, L.v);
-    st = launch_shrink(x, T, pool, 1, ids, sgmv, v, L, ws, s);
+    if (sgmv) {
+        st = launch_quant_rows_fp8(x, T, pool->d_in, xq, xs, s);
+        if (st != LORA_OK) return st;
+        st = launch_shrink(x, T, pool, 1, ids, sgmv, v, L, ws, s);
+    } else {
+        // decode rows: quantize each row in the workgroup that shrinks it
+        st = launch_quant_shrink_rows(x, T, pool, ids, v, xq, xs, ws_ptr<int32_t>(ws, L.header), s);
+    }
     if (st != LORA_OK) return st;
     const int32_t *perm = sgmv ? ws_ptr<int32_t>(ws, L.perm) : nullptr;
     float *partial = ws_ptr<float>(ws, L.gemm_partial);

@@ -246,6 +246,9 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
 // FP8 base (E4M3 codes, fp32 scales): per-row and per-column quantizers and
 // y = s_x s_w (xq wq^T) (+ s v B when pool != nullptr), bf16 y.
 lora_status_t launch_quant_rows_fp8(const void *x, int32_t T, int32_t K, uint8_t *xq, float *xs, hipStream_t s);
+// The BGMV shrink of bf16 rows and their E4M3 quantization (codes xq, scales xs) in one launch.
+lora_status_t launch_quant_shrink_rows(const void *x, int32_t T, const lora_pool_t *pool, const int32_t *ids,
+                                       float *v, uint8_t *xq, float *xs, int32_t *err, hipStream_t s);
 lora_status_t launch_quant_cols_fp8(const void *W, int32_t K, int32_t N, uint8_t *wq, float *wsc, hipStream_t s);
 lora_status_t launch_gemm_fp8(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *wsc, void *y,
                               int32_t T, int32_t d_in, int32_t d_out, const lora_pool_t *pool,

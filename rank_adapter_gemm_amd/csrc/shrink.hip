@@ -9,8 +9,8 @@
 //
 // Two kernels:
 //  * k_shrink_rows  (BGMV): one 512-thread workgroup per token row; x[t] is
-//    read once with 16-byte coalesced loads, the slot's A^T rows (only the
-//    first r) are gathered in batches of independent loads, each lane keeps
+//    read once with 16-byte coalesced loads, the slot's A^T rows (max_rank
+//    of them, masked by its rank) are gathered in batches of independent loads, each lane keeps
 //    per-rank partial sums, which are reduced across the wavefront with a
 //    transposing butterfly of cross-lane swaps and then across the 8
 //    wavefronts through LDS.  fp32 or bf16 inputs.
@@ -19,6 +19,7 @@
 //    K is split over the 4 wavefronts (LDS reduction) and optionally over
 //    workgroups (partials, then a fixed-order reduction: deterministic).
 #include "common.hpp"
+#include "fp8_common.hpp"
 
 namespace lora {
 
@@ -71,13 +72,19 @@ __device__ __forceinline__ int owned_index(int lane) {
     return idx;
 }
 
-template <int DT, int RM>
+// Q8 (FP8-base forward, bf16 rows, no perm): the workgroup also writes the
+// row's E4M3 codes and power-of-two scale, as k_quant_rows_fp8 does (amax
+// over the row, then the codes), after the shrink, with x from cache: one
+// launch and one HBM read of x for both.
+template <int DT, int RM, bool Q8 = false>
 __global__ void __launch_bounds__(512) k_shrink_rows(const typename elem<DT>::T *__restrict__ x,
                                                      int32_t T, int32_t d_in, slice_set ss,
                                                      int32_t n_slots, int32_t max_rank,
                                                      const int32_t *__restrict__ ids,
                                                      const int32_t *__restrict__ perm,
-                                                     float *__restrict__ v, int32_t *err) {
+                                                     float *__restrict__ v, int32_t *err,
+                                                     uint8_t *__restrict__ xq, float *__restrict__ xs) {
+    static_assert(!Q8 || DT == LORA_BF16, "the FP8 base quantizes bf16 rows");
     typedef typename elem<DT>::T E;
     constexpr int VN = vec16<DT>::n;
     constexpr int NW = 8;                                 // wavefronts per workgroup
@@ -159,6 +166,36 @@ __global__ void __launch_bounds__(512) k_shrink_rows(const typename elem<DT>::T 
         if (in_range)
             for (int sl = 0; sl < ss.n; ++sl) any_empty |= ss.rank[sl][id] <= 0;
         if ((id < -1 || id >= n_slots) || any_empty) flag_bad_row(err, t);
+    }
+    if constexpr (Q8) {
+        __shared__ float s_max[NW];
+        const int nch = d_in / 8;
+        float m = 0.0f;
+        for (int c = tid; c < nch; c += NW * 64) {
+            float f[8];
+            vec16<LORA_BF16>::widen(ldg16(xt + 8 * c), f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        if (lane == 0) s_max[wave] = m;
+        __syncthreads();
+        float amax = s_max[0];
+#pragma unroll
+        for (int w2 = 1; w2 < NW; ++w2) amax = fmaxf(amax, s_max[w2]);
+        const int e = scale_exp(amax);
+        const float inv = exp2i(-e);
+        if (tid == 0) xs[t] = exp2i(e);
+        uint8_t *out = xq + (size_t)t * d_in;
+        for (int c = tid; c < nch; c += NW * 64) {
+            float f[8];
+            vec16<LORA_BF16>::widen(ldg16(xt + 8 * c), f);
+            uint2 q;
+            q.x = e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+            q.y = e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+            *reinterpret_cast<uint2 *>(out + 8 * c) = q;
+        }
     }
 }
 
@@ -386,13 +423,35 @@ static void launch_rows(const void *x, int32_t T, const lora_pool_t &p, const sl
     const E *xe = (const E *)x;
 #define LORA_SHRINK_ROWS(RMV)                                                                   \
     hipLaunchKernelGGL((k_shrink_rows<DT, RMV>), dim3(T), dim3(512), 0, s, xe, T, p.d_in, ss,   \
-                       p.n_slots, p.max_rank, ids, perm, v, err)
+                       p.n_slots, p.max_rank, ids, perm, v, err, nullptr, nullptr)
     if (p.max_rank <= 8) LORA_SHRINK_ROWS(8);
     else if (p.max_rank <= 16) LORA_SHRINK_ROWS(16);
     else if (p.max_rank <= 32) LORA_SHRINK_ROWS(32);
     else if (p.max_rank <= 64) LORA_SHRINK_ROWS(64);
     else LORA_SHRINK_ROWS(128);
 #undef LORA_SHRINK_ROWS
+}
+
+// FP8-base forward, BGMV rows: the shrink and the row quantizer in one launch.
+lora_status_t launch_quant_shrink_rows(const void *x, int32_t T, const lora_pool_t *pool, const int32_t *ids,
+                                       float *v, uint8_t *xq, float *xs, int32_t *err, hipStream_t s) {
+    slice_set ss;
+    ss.n = 1;
+    for (int i = 0; i < kMaxSlices; ++i) {
+        ss.a[i] = pool->a;
+        ss.rank[i] = pool->rank;
+    }
+    const uint16_t *xe = (const uint16_t *)x;
+#define LORA_QSHRINK_ROWS(RMV)                                                                            \
+    hipLaunchKernelGGL((k_shrink_rows<LORA_BF16, RMV, true>), dim3(T), dim3(512), 0, s, xe, T, pool->d_in, ss, \
+                       pool->n_slots, pool->max_rank, ids, nullptr, v, err, xq, xs)
+    if (pool->max_rank <= 8) LORA_QSHRINK_ROWS(8);
+    else if (pool->max_rank <= 16) LORA_QSHRINK_ROWS(16);
+    else if (pool->max_rank <= 32) LORA_QSHRINK_ROWS(32);
+    else if (pool->max_rank <= 64) LORA_QSHRINK_ROWS(64);
+    else LORA_QSHRINK_ROWS(128);
+#undef LORA_QSHRINK_ROWS
+    return hip_status(hipGetLastError());
 }
 
 lora_status_t launch_shrink(const void *x, int32_t T, const lora_pool_t *pools, int32_t n_slices,

@@ -185,6 +185,26 @@ def test_forward_fp8_delta_is_applied():
             assert np.all(np.abs(d_gpu - d_ref) <= bound + 1e-30), "mode %d flags %d" % (mode, flags)
 
 
+@pytest.mark.parametrize("T,K,N,mode", [(256, 1024, 4096, L.LORA_MODE_BGMV), (37, 2048, 1024, L.LORA_MODE_BGMV),
+                                         (300, 208, 264, L.LORA_MODE_AUTO), (1500, 512, 512, L.LORA_MODE_SGMV)])
+def test_forward_fp8_codes_match_the_row_quantizer(T, K, N, mode):
+    """The forward quantizes x itself (for BGMV rows inside the shrink's
+    launch): with every row a base row its y depends on the codes and
+    scales alone, so it must equal, bitwise, the standalone row quantizer
+    followed by lora_gemm_fp8 on the same workspace size."""
+    c = Fp8Case(T, K, N, [16, 8], 16, seed=T + N, ids=np.full(T, -1, np.int32))
+    y, ws = c.run(mode, 0)
+    xq = torch.empty(T, K, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(T, device="cuda")
+    L.lora_quantize_rows_fp8(c.x, T, K, xq, xs)
+    y_ref = torch.full((T, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    ws2 = L.Workspace(T, c.n_slots, c.R, N, fp8_d_in=K)
+    L.lora_gemm_fp8(xq, xs, c.wt.codes, c.wt.scale, y_ref, T, K, N, ws2.buf)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    assert L.lora_get_device_error(ws.buf) == -1
+
+
 def test_forward_fp8_empty_batch():
     c = Fp8Case(4, 64, 64, [8], 8, seed=9)
     y, ws = c.run(L.LORA_MODE_AUTO, 0, T=0)
