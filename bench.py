@@ -38,11 +38,12 @@ RIDGE = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
 RIDGE_FP8 = MFMA_FP8_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
 MALL_BYTES = 256 * 2 ** 20
 CSRC = os.path.join(ROOT, "rank_adapter_gemm_amd", "csrc")
-KERNEL_SOURCE = {"gemm_expand": ["gemm.hip", "gemm_common.hpp"], "shrink": ["shrink.hip"],
+KERNEL_SOURCE = {"gemm_expand": ["gemm.hip", "gemm_common.hpp"], "shrink": ["shrink.hip", "fp8_common.hpp"],
                  "segments": ["segments.hip"], "expand": ["expand.hip"],
-                 "forward": ["api.hip", "gemm.hip", "gemm_common.hpp", "shrink.hip", "segments.hip", "expand.hip"],
-                 "forward_fp8": ["api.hip", "gemm_fp8.hip", "gemm_common.hpp", "shrink.hip", "segments.hip",
-                                 "expand.hip"]}
+                 "forward": ["api.hip", "gemm.hip", "gemm_common.hpp", "shrink.hip", "fp8_common.hpp",
+                             "segments.hip", "expand.hip"],
+                 "forward_fp8": ["api.hip", "gemm_fp8.hip", "gemm_common.hpp", "fp8_common.hpp", "shrink.hip",
+                                 "segments.hip", "expand.hip"]}
 
 
 def parse():
