@@ -220,7 +220,8 @@ def test_host_errors_enqueue_nothing():
 
 @pytest.mark.parametrize("T,d_in,d_out", [(256, 4096, 4096), (64, 1032, 520), (2240, 4096, 1024),
                                           (300, 2048, 264), (4096, 512, 256), (2240, 1024, 4096),
-                                          (520, 1024, 8192), (300, 256, 16408), (520, 1024, 16384)])
+                                          (520, 1024, 8192), (300, 256, 16408), (520, 1024, 16384),
+                                          (3328, 256, 4096)])
 def test_split_k_and_tile_configs(T, d_in, d_out):
     """Small batches split the GEMM over K when the workspace holds the fp32
     partials, and larger ones split only a mostly idle last round of tiles
@@ -232,7 +233,8 @@ def test_split_k_and_tile_configs(T, d_in, d_out):
     300 x 256 x 16408 is 2 x 129 tiles of 256 x 128 (the last band one tile
     wide, the last tile 24 columns), 520 x 1024 x 16384 is 3 x 128 tiles of
     256 x 128 whose last 128 are split in two, so the reduction walks the
-    same order."""
+    same order.  3328 x 256 x 4096 is 208 tiles of 256 x 256: one round,
+    taken over 416 tiles of 256 x 128."""
     c = Case(T=T, d_in=d_in, d_out=d_out, ranks=[16, 8, 16, 4], max_rank=16, dtype=torch.bfloat16,
              seed=12)
     ref = c.oracle()
