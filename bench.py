@@ -1,16 +1,23 @@
 """Benchmark of the mixed-adapter LoRA layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_bgmv]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload stress_70b]
+    python bench.py --trace-summary DIR     (summarise a rocprofv3 kernel trace)
+
+The default workload is the largest one that fits one GPU: the 70B-shaped
+layer set with heterogeneous ranks (4608 rows: 512 decode tokens and two
+prefill chunks of 2048; q, o, gate, up, down; 256 adapter slots of ranks
+8-64 padded to 64).
 
 One step = one pass of the whole layer over one batch: every projection of
 the workload through lora_linear_forward (segments built once per batch and
 reused across projections in SGMV mode).  The timed region holds exactly K
-steps bracketed by device synchronisations; inputs are resident in HBM.
-Workloads whose working set fits in the 256 MB Infinity Cache rotate through
-several copies of (x, W, pool, y) so every step reads HBM.
+steps (and is preceded by exactly W warm-up steps), bracketed by device
+synchronisations; inputs are resident in HBM.  Workloads whose working set
+fits in the 256 MB Infinity Cache rotate through several copies of
+(x, W, pool, y) so every step reads HBM.
 
 Prints ONE JSON line: tokens/s of the whole step, plus
-  roofline:     the dominant kernel's algorithmic bytes (or flops) per launch
+  roofline:     the dominant kernel's algorithmic flops (or bytes) per launch
                 over its average duration, measured with HIP events on the
                 stream it runs on, against the MI355X peak;
   cpu_baseline: the fp64 CPU oracle on a bounded row sample of the same batch.
@@ -51,7 +58,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode_bgmv")
+    ap.add_argument("--workload", default="stress_70b")
     ap.add_argument("--mode", default="auto", choices=["auto", "bgmv", "sgmv"])
     ap.add_argument("--separate-expand", action="store_true")
     ap.add_argument("--no-slices", action="store_true",
@@ -67,6 +74,20 @@ def parse():
                     help="context run: every row that has an adapter uses the batch's most frequent one")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain fp32 copy kernel of known size (for counter scaling)")
+    ap.add_argument("--packed-pool", action="store_true",
+                    help="packed adapter pools (each slot its adapter's rank rows, no padding to max_rank)")
+    ap.add_argument("--no-breakdown", action="store_true",
+                    help="skip the per-entry-point timings (short profiling runs); the roofline "
+                         "kernel and the forward calls are still timed")
+    ap.add_argument("--counter-summary", default=None, metavar="DIR",
+                    help="print per-kernel means of a rocprofv3 --pmc csv output directory and exit")
+    ap.add_argument("--record-traffic", nargs=6, default=None,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "KEY", "KERNEL_SUBSTRING", "GRID", "SOURCE"),
+                    help="store one kernel's HBM bytes per launch (counter runs with --calib-copy) in "
+                         "profiles/traffic.json and exit")
+    ap.add_argument("--trace-summary", default=None, metavar="DIR",
+                    help="print a per-kernel, per-grid summary of a rocprofv3 --kernel-trace output "
+                         "directory and exit (no GPU use)")
     return ap.parse_args()
 
 
@@ -78,8 +99,130 @@ def source_sha(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
+def trace_summary(path: str) -> None:
+    """Per-kernel, per-grid summary of a rocprofv3 --kernel-trace run: the
+    kernel_stats file groups launches by name only, which mixes the shapes of
+    one template; this groups them by (name, grid size) as well."""
+    import csv
+    import glob
+    import statistics
+
+    import sqlite3
+
+    files = sorted(glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True))
+    dbs = sorted(glob.glob(os.path.join(path, "**", "*_results.db"), recursive=True))
+    if not files and not dbs:
+        print("no *kernel_trace.csv or *_results.db under %s" % path, file=sys.stderr)
+        sys.exit(1)
+    groups = {}
+    for f in files:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                name = row.get("Kernel_Name", "?")
+                grid = row.get("Grid_Size_X") or row.get("Grid_Size") or "?"
+                wg = row.get("Workgroup_Size_X") or row.get("Workgroup_Size") or "?"
+                dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+                groups.setdefault((name, grid, wg), []).append(dur)
+    for f in dbs:                      # rocpd output (the default format of rocprofv3)
+        con = sqlite3.connect(f)
+        for name, grid, wg, start, end in con.execute(
+                "select name, grid_x, workgroup_x, start, end from kernels"):
+            groups.setdefault((name, str(grid), str(wg)), []).append((end - start) / 1e3)
+        con.close()
+    print("| calls | avg us | min us | max us | total us | grid | wg | kernel |")
+    print("|---|---|---|---|---|---|---|---|")
+    for (name, grid, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        short = name if len(name) <= 110 else name[:107] + "..."
+        print("| %d | %.3f | %.3f | %.3f | %.1f | %s | %s | `%s` |" % (
+            len(d), statistics.fmean(d), min(d), max(d), sum(d), grid, wg, short))
+
+
+def _counter_rows(path: str):
+    """(kernel name, grid size, counter, value, duration us) of every dispatch
+    in a rocprofv3 --pmc --output-format csv directory."""
+    import csv
+    import glob
+
+    files = sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        print("no *counter_collection.csv under %s" % path, file=sys.stderr)
+        sys.exit(1)
+    for f in files:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                yield (row["Kernel_Name"], row["Grid_Size"], row["Counter_Name"], float(row["Counter_Value"]),
+                       (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
+
+
+def counter_summary(path: str) -> None:
+    """Per-kernel, per-grid means of each counter of a rocprofv3 --pmc run
+    (kernels of this library, and the calibration copy)."""
+    import statistics
+
+    groups = {}
+    for name, grid, ctr, val, dur in _counter_rows(path):
+        if "lora::" not in name and "AUnaryFunctor" not in name:
+            continue
+        if any(k in name for k in ("k_upload", "k_fill", "k_set_meta", "k_ws_init")):
+            continue
+        groups.setdefault((name, grid, ctr), []).append((val, dur))
+    print("| calls | mean value | mean us | counter | grid | kernel |")
+    print("|---|---|---|---|---|---|")
+    for (name, grid, ctr), v in sorted(groups.items(), key=lambda kv: (kv[0][2], -statistics.fmean(x[1] for x in kv[1]))):
+        short = name if len(name) <= 100 else name[:97] + "..."
+        print("| %d | %.1f | %.1f | %s | %s | `%s` |" % (len(v), statistics.fmean(x[0] for x in v),
+                                                       statistics.fmean(x[1] for x in v), ctr, grid, short))
+
+
+def record_traffic(fetch_dir: str, write_dir: str, key: str, kernel_sub: str, grid: str, source: str) -> None:
+    """HBM bytes per launch of one kernel (matched by a name substring and its
+    grid size) from a FETCH_SIZE run and a WRITE_SIZE run, each scaled by what
+    the same counter reads for the 1 GiB calibration copy of --calib-copy,
+    stored in profiles/traffic.json under `key` with the hash of the kernel's
+    source files (KERNEL_SOURCE[source])."""
+    import statistics
+
+    def mean_of(path, ctr):
+        vals, calib = [], []
+        for name, g, c, val, dur in _counter_rows(path):
+            if c != ctr:
+                continue
+            if kernel_sub in name and g == grid:
+                vals.append(val)
+            elif "AUnaryFunctor" in name and g == "67108864":
+                calib.append(val)
+        if not vals or not calib:
+            print("%s: no matching dispatches (kernel %d, calibration %d)" % (path, len(vals), len(calib)),
+                  file=sys.stderr)
+            sys.exit(1)
+        # the calibration copy moves 1 GiB each way; the counter reads KiB
+        factor = (1 << 30) / (statistics.fmean(calib) * 1024)
+        return statistics.fmean(vals) * 1024 * factor, factor
+
+    fetch, ff = mean_of(fetch_dir, "FETCH_SIZE")
+    write, wf = mean_of(write_dir, "WRITE_SIZE")
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data[key] = {"hbm_bytes_per_launch": int(round(fetch + write)), "fetch_bytes": int(round(fetch)),
+                 "write_bytes": int(round(write)), "fetch_factor": round(ff, 3), "write_factor": round(wf, 3),
+                 "kernel": kernel_sub, "grid": grid, "source_sha": source_sha(source)}
+    with open(path, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps({key: data[key]}))
+
+
 def main():
     args = parse()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer is built and measured on a single "
               "MI355X (rows are independent; see the sharding notes in the design document). "
@@ -112,8 +255,10 @@ def main():
 
     # ---- pools (one per projection) ----
     pools = []
+    # packed pools: each slot holds its adapter's rank rows, rounded up to 8
+    capacity = ([max(8, (int(r) + 7) // 8 * 8) for r in wl.ranks] if args.packed_pool else None)
     for pr in wl.projections:
-        pool = L.AdapterPool(wl.n_slots, pr.d_in, pr.d_out, R, wl.dtype, device=dev)
+        pool = L.AdapterPool(wl.n_slots, pr.d_in, pr.d_out, R, wl.dtype, device=dev, capacity=capacity)
         for s in range(wl.n_slots):
             r = int(wl.ranks[s])
             if r > 0:
@@ -147,9 +292,11 @@ def main():
             ps, keep = [], []
             for pl in pools:
                 a, b, sc, rk = pl.a.clone(), pl.b.clone(), pl.scale.clone(), pl.rank.clone()
-                keep += [a, b, sc, rk]
+                r0 = pl.row0.clone() if pl.row0 is not None else None
+                keep += [a, b, sc, rk, r0]
                 q = L.lora_pool_t(pl.pool.n_slots, pl.pool.d_in, pl.pool.d_out, pl.pool.max_rank,
-                                  pl.pool.dtype, a.data_ptr(), b.data_ptr(), sc.data_ptr(), rk.data_ptr())
+                                  pl.pool.dtype, a.data_ptr(), b.data_ptr(), sc.data_ptr(), rk.data_ptr(),
+                                  r0.data_ptr() if r0 is not None else None, pl.pool.row0_host)
                 ps.append(q)
         ys = [torch.empty(T, p.d_out, dtype=wl.dtype, device=dev) for p in wl.projections]
         W8 = [L.Fp8Weight(W) for W in Ws] if fp8 else None
@@ -194,37 +341,60 @@ def main():
         for gi in range(len(groups)):
             forward_group(gi, i)
 
-    # The step is captured into HIP graphs (one graph replays every working-set
-    # copy once) so host-side launch overhead is not part of the timing.
-    graph_steps = n_sets if n_sets > 1 else 4
+    # The step is captured into HIP graphs so host-side launch overhead is not
+    # part of the timing: one graph per working-set copy (one step each), and
+    # for rotated sets one graph that replays every copy once.  Step i runs
+    # on copy i % n_sets; exactly the requested number of steps is run.
     step(0)
     torch.cuda.synchronize()
-    g_step = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_step):
-        for i in range(graph_steps):
-            step(i)
+    g_one = []
+    for j in range(n_sets):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(j)
+        g_one.append(g)
+    g_all = None
+    if n_sets > 1:
+        g_all = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_all):
+            for j in range(n_sets):
+                step(j)
     torch.cuda.synchronize()
 
-    # default step counts: about 2 s of timed work
-    t0 = time.perf_counter()
-    g_step.replay()
-    torch.cuda.synchronize()
-    est = max((time.perf_counter() - t0) / graph_steps, 1e-6)
-    steps = args.steps if args.steps is not None else int(min(20000, max(20, 2.0 / est)))
-    steps = max(graph_steps, (steps // graph_steps) * graph_steps)
-    warmup = args.warmup if args.warmup is not None else int(min(200, max(graph_steps, steps // 10)))
-    warmup = max(graph_steps, (warmup // graph_steps) * graph_steps)
+    def run_steps(n, i0=0):
+        i = i0
+        while n > 0:
+            if g_all is not None and i % n_sets == 0 and n >= n_sets:
+                g_all.replay()
+                i += n_sets
+                n -= n_sets
+            else:
+                g_one[i % n_sets].replay()
+                i += 1
+                n -= 1
+        return i
 
-    for _ in range(warmup // graph_steps):
-        g_step.replay()
+    if args.steps is None:
+        # default counts: at least 50 timed steps and 100 ms, 10 warm-up steps
+        t0 = time.perf_counter()
+        run_steps(max(n_sets, 2))
+        torch.cuda.synchronize()
+        est = max((time.perf_counter() - t0) / max(n_sets, 2), 1e-6)
+    steps = args.steps if args.steps is not None else int(min(20000, max(50, math.ceil(0.1 / est))))
+    warmup = args.warmup if args.warmup is not None else 10
+    if steps < 1 or warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
+
+    i_next = run_steps(warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps // graph_steps):
-        g_step.replay()
+    run_steps(steps, i_next)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = 1e3 * elapsed / steps
     value = T * steps / elapsed
+    est = max(elapsed / steps, 1e-6)
     assert L.lora_get_device_error(ws.buf) == -1
 
     # ---- per-kernel durations ----
@@ -240,6 +410,8 @@ def main():
     # the base product alone (no adapters), for the LoRA overhead
     if "gemm" not in names and not fp8:
         names.append("gemm")
+    if args.no_breakdown:             # only what the roofline needs
+        names = ["gemm_fp8"] if fp8 else ["gemm_expand"]
     smode = L.LORA_MODE_SGMV if sgmv else L.LORA_MODE_BGMV
 
     def call(name, k, i):
@@ -265,7 +437,7 @@ def main():
     if sgmv:
         L.lora_build_segments(ids, T, wl.n_slots, R, ws.buf)
     per_launch = {}          # (name, proj) -> average ms per launch
-    reps = max(n_sets, 8)
+    reps = n_sets if args.no_breakdown else max(n_sets, 8)
     for name in names:
         projs = [0] if name == "segments" else range(len(wl.projections))
         for k in projs:
@@ -280,7 +452,7 @@ def main():
             torch.cuda.synchronize()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
-            n_rep = max(3, int(0.2 / max(est, 1e-6) / reps))
+            n_rep = 2 if args.no_breakdown else max(3, int(0.2 / max(est, 1e-6) / reps))
             e0.record()
             for _ in range(n_rep):
                 g.replay()
@@ -304,7 +476,7 @@ def main():
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        n_rep = max(3, int(0.2 / max(est, 1e-6) / reps))
+        n_rep = 2 if args.no_breakdown else max(3, int(0.2 / max(est, 1e-6) / reps))
         e0.record()
         for _ in range(n_rep):
             g.replay()
@@ -374,8 +546,13 @@ def main():
         breakdown[name] = dict(us_per_step=round(1e3 * tot_ms, 3), bytes=tot_b, flops=tot_f,
                                gbs=round(tot_b / (tot_ms * 1e-3) / 1e9, 1) if tot_ms else None,
                                tflops=round(tot_f / (tot_ms * 1e-3) / 1e12, 2) if tot_ms else None)
-    # Roofline of the step's dominant launch group: the lora_linear_forward
-    # call of the slowest projection (all the kernels that call enqueues).
+    # Roofline.  The slowest forward call of the step (all the kernels that
+    # one lora_linear_forward call enqueues) is reported as `forward_call`.
+    # Where that call is MFMA-bound (bf16), the roofline unit is its dominant
+    # kernel alone: the base GEMM with the fused expand of its slowest
+    # projection (one k_gemm_bf16 launch, timed through lora_gemm_expand in
+    # the same launch configuration).  Otherwise (HBM-bound decode, fp32,
+    # FP8) it is the forward call.
     kd = max(fwd, key=lambda k: fwd[k])
     by_d, fl_d = fwd_work(kd)
     t_d = fwd[kd] * 1e-3
@@ -396,9 +573,26 @@ def main():
     roof["algorithmic_bytes_per_launch"] = int(by_d)
     roof["algorithmic_flops_per_launch"] = int(fl_d)
     roof["traffic"] = stored_traffic("forward_fp8" if fp8 else "forward", args.workload, roof["projection"])
+    forward_call = dict(roof)
+    if roof["bound"] == "mfma" and not fp8:
+        cand = [(per_launch[("gemm_expand", k)], k) for k in groups[kd] if ("gemm_expand", k) in per_launch]
+        t_k, kk = max(cand)
+        pk = wl.projections[kk]
+        b_k, f_k = work("gemm_expand", pk)
+        roof = dict(bound="mfma", achieved=round(f_k / (t_k * 1e-3) / 1e12, 2), peak=MFMA_BF16_PEAK_TFS,
+                    unit="TFLOP/s")
+        roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+        roof["kernel"] = "k_gemm_bf16 (base GEMM + fused expand)"
+        roof["projection"] = pk.name
+        roof["shape"] = [T, pk.d_in, pk.d_out]
+        roof["launches_per_step"] = sum(1 for p in wl.projections if (p.d_in, p.d_out) == (pk.d_in, pk.d_out))
+        roof["avg_launch_us"] = round(t_k * 1e3, 3)
+        roof["algorithmic_bytes_per_launch"] = int(b_k)
+        roof["algorithmic_flops_per_launch"] = int(f_k)
+        roof["traffic"] = stored_traffic("gemm_expand", args.workload, pk.name)
     # LoRA overhead: the step's forward calls against the base products alone
     base_ms = sum(per_launch[(n_, k)] for (n_, k) in per_launch if n_ in ("gemm", "gemm_fp8", "quantize"))
-    overhead = dict(forward_us=round(1e3 * sum(fwd.values()), 3), base_only_us=round(1e3 * base_ms, 3),
+    overhead = dict(forward_us=round(1e3 * sum(fwd.values()), 3), base_only_us=round(1e3 * base_ms, 3) if base_ms else None,
                     overhead=round(sum(fwd.values()) / base_ms - 1.0, 4) if base_ms else None)
     breakdown["forward"] = dict(us_per_step=round(1e3 * sum(fwd.values()), 3),
                                 per_call_us={"+".join(wl.projections[k].name for k in groups[gi]):
@@ -443,9 +637,11 @@ def main():
                      ("fp32" if wl.dtype == torch.float32 else "bf16")),
             "calls": ["+".join(wl.projections[k].name for k in g) for g in groups],
             "adapters": "single (most frequent)" if args.single_adapter else "mixed",
+            "pool": "packed (slot = its rank rows)" if args.packed_pool else "padded to max_rank",
             "cold_sets": n_sets, "working_set_MB": round(set_bytes / 1e6, 1),
         },
         "roofline": roof,
+        "forward_call": forward_call,
         "breakdown": breakdown,
         "lora_overhead": overhead,
         "cpu_baseline": cpu,
@@ -527,17 +723,16 @@ def cpu_baseline(wl, target_s):
     import numpy as np
     import torch
 
-    from oracle import BF16, F32, lora_scale, oracle_rows
+    from oracle import BF16, F32, affinity_cores, default_threads, lora_scale, oracle_rows
 
     def host(t):
         t = t.detach().contiguous().cpu()
         return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
+    # every core of the affinity mask, within the host's declared CPU share
+    # (OMP_NUM_THREADS) where one is set
+    cores = default_threads()
+    mask = affinity_cores()
     code = F32 if wl.dtype == torch.float32 else BF16
     # The adapters were released after upload: redraw them the same way (same seed) on the host side
     from rank_adapter_gemm_amd.workloads import make_workload
@@ -569,10 +764,12 @@ def cpu_baseline(wl, target_s):
             elapsed += time.perf_counter() - t0
         rows_done += len(take)
         n = min(2 * n, 4096)
+    share = os.environ.get("OMP_NUM_THREADS")
     return {"value": round(rows_done / elapsed, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "affinity_cores": mask, "cpu_share": int(share) if share and share.isdigit() else None,
             "sample": "%d token rows drawn from the %d-row %s batch (seeded order, cycled), all %d "
-                      "projection(s), fp64 C oracle, %.1f s" % (rows_done, wl.T, wl.name,
-                                                                len(wl2.projections), elapsed)}
+                      "projection(s), fp64 C oracle, %d threads, %.1f s" % (
+                          rows_done, wl.T, wl.name, len(wl2.projections), cores, elapsed)}
 
 
 if __name__ == "__main__":

@@ -88,22 +88,38 @@ typedef enum { LORA_MODE_AUTO = 0, LORA_MODE_BGMV = 1, LORA_MODE_SGMV = 2 } lora
 #define LORA_FLAG_SEPARATE_EXPAND 0x2 /* expand as its own read-modify-write pass, not in the GEMM epilogue */
 
 /*
- * The HBM adapter pool of one projection: n_slots stacked, rank-padded slots
- * (the stacked buffers of "Serving LoRA adapters ...", Step 3/4).  A plain
- * descriptor filled by lora_pool_create and not modified afterwards.
- * Internal layout, per slot s (the library's choice, documented for tools):
- *   a: A transposed, [max_rank][d_in]           -- rank rows contiguous over d_in
- *   b: B in rank octets, [max_rank/8][d_out][8] -- 8 ranks of one column contiguous
- * rows/octets at and beyond the slot's rank are zero.  The kernels rely on
- * that: some read a slot's max_rank rows whole and mask by its rank later.
+ * The HBM adapter pool of one projection: n_slots stacked slots (the stacked
+ * buffers of "Serving LoRA adapters ...", Step 3/4).  A plain descriptor
+ * filled by lora_pool_create or lora_pool_create_packed and not modified
+ * afterwards.  Two forms:
+ *   padded (lora_pool_create): every slot holds max_rank rank rows, so any
+ *     adapter of rank <= max_rank fits any slot (the slots sized for the
+ *     maximum rank of "Serving LoRA adapters ...", Step 3, and of "Serving
+ *     multiple LoRAs ...", section "Scheduling the adapters");
+ *   packed (lora_pool_create_packed): slot s holds c_s rank rows, c_s a
+ *     multiple of 8 chosen per slot, stored back to back with no padding to
+ *     max_rank (the heterogeneous-rank, non-contiguous layout of "Multi-LoRA
+ *     Serving: Architecture for Thousands of Adapters", section
+ *     "Heterogeneous batching and rank"); row0[s] is the first rank row of
+ *     slot s and row0[n_slots] the total.
+ * Internal layout of slot s, whose rank rows start at R0 = s * max_rank
+ * (padded) or row0[s] (packed) and number C = max_rank or c_s (the library's
+ * choice, documented for tools):
+ *   a: A transposed, rank rows R0 .. R0+C-1 of d_in elements each
+ *   b: B in rank octets, rows R0/8 .. (R0+C)/8-1 of [d_out][8] elements
+ *      (8 ranks of one output column are 16 contiguous bytes in bf16)
+ * Rank rows at and beyond the slot's rank are zero.  Kernels read only the
+ * rank rows (octets) below the rank of the slot they serve.
  */
 typedef struct {
     int32_t n_slots, d_in, d_out, max_rank;
     int32_t dtype;     /* lora_dtype_t */
-    void *a;           /* DEVICE, lora_pool_bytes(...).a_bytes */
-    void *b;           /* DEVICE, lora_pool_bytes(...).b_bytes */
+    void *a;           /* DEVICE, lora_pool_bytes[_packed](...).a_bytes */
+    void *b;           /* DEVICE, lora_pool_bytes[_packed](...).b_bytes */
     float *scale;      /* DEVICE [n_slots], s = alpha / r (0 for an empty slot) */
     int32_t *rank;     /* DEVICE [n_slots], true rank, 0 = empty slot */
+    int32_t *row0;     /* packed: DEVICE [n_slots + 1] first rank row per slot; padded: NULL */
+    const int32_t *row0_host;  /* packed: HOST copy of row0 (caller-owned, kept valid); padded: NULL */
 } lora_pool_t;
 
 /* Device views of the segment metadata held in a workspace (see
@@ -133,12 +149,34 @@ lora_status_t lora_pool_create(lora_pool_t *pool, int32_t n_slots, int32_t d_in,
                                int32_t max_rank, lora_dtype_t dtype, void *a, void *b,
                                float *scale, int32_t *rank, lora_stream_t stream);
 
+/* A packed pool: slot s holds capacity[s] rank rows (HOST [n_slots], each a
+ * multiple of 8 in [8, max_rank]; max_rank is the largest).  Bytes of the
+ * caller-allocated a and b buffers (HOST outputs), for rows
+ * sum_s capacity[s] instead of n_slots * max_rank. */
+lora_status_t lora_pool_bytes_packed(int32_t n_slots, int32_t d_in, int32_t d_out, const int32_t *capacity,
+                                     lora_dtype_t dtype, size_t *a_bytes, size_t *b_bytes);
+
+/* Fill *pool (HOST) as a packed pool: writes the prefix sums of capacity
+ * (HOST [n_slots]) into row0_host (HOST [n_slots + 1], caller-owned; it must
+ * stay valid and unchanged while the pool is used: uploads validate against
+ * it) and copies them to row0 (DEVICE [n_slots + 1]) on `stream`, then zeroes
+ * every slot as lora_pool_create does.  max_rank (the v row width of every
+ * call on this pool) must be at least the largest capacity.  Errors:
+ * LORA_ERR_INVALID_ARGUMENT for a capacity that is not a multiple of 8 in
+ * [8, max_rank], or the conditions of lora_pool_create. */
+lora_status_t lora_pool_create_packed(lora_pool_t *pool, int32_t n_slots, int32_t d_in, int32_t d_out,
+                                      int32_t max_rank, lora_dtype_t dtype, const int32_t *capacity,
+                                      int32_t *row0_host, void *a, void *b, float *scale, int32_t *rank,
+                                      int32_t *row0, lora_stream_t stream);
+
 /* Copy one adapter into `slot` (activation of an adapter into a slot):
  *   A: DEVICE [d_in, r] row-major with row stride lda >= r elements,
  *   B: DEVICE [r, d_out] row-major with row stride ldb >= d_out elements,
- * both in the pool's dtype.  Ranks r..max_rank-1 of the slot are zeroed,
- * scale[slot] = alpha / r (computed in fp32), rank[slot] = r.
- * Errors: LORA_ERR_SLOT_OUT_OF_RANGE, LORA_ERR_RANK_EXCEEDS_MAX (r > max_rank),
+ * both in the pool's dtype.  The slot's rank rows r.. (up to max_rank, or
+ * to its capacity in a packed pool) are zeroed, scale[slot] = alpha / r
+ * (computed in fp32), rank[slot] = r.
+ * Errors: LORA_ERR_SLOT_OUT_OF_RANGE, LORA_ERR_RANK_EXCEEDS_MAX (r > max_rank,
+ * or r above the slot's capacity in a packed pool),
  * LORA_ERR_INVALID_ARGUMENT (r < 1, null, lda < r, ldb < d_out). */
 lora_status_t lora_pool_upload(const lora_pool_t *pool, int32_t slot, const void *A, int32_t lda,
                                const void *B, int32_t ldb, int32_t r, float alpha,
@@ -183,8 +221,12 @@ lora_status_t lora_build_segments(const int32_t *ids, int32_t T, int32_t n_slots
 
 /* ---- a4: shrink ------------------------------------------------------------- */
 
-/* v[t, 0:r_a] = x[t,:] A_a for rows with a usable adapter a = ids[t]; all
- * other entries of v[t, 0:max_rank] are zero.
+/* The first of the two low-rank products, per row: v[t, 0:r_a] = x[t,:] A_a
+ * for rows with a usable adapter a = ids[t]; all other entries of
+ * v[t, 0:max_rank] are zero ("Serving multiple LoRAs ...", section "Not
+ * merging the weights, computing in batches": the rank-r intermediate xA,
+ * per request (BGMV) or per adapter segment (SGMV); "Serving LoRA adapters
+ * ...", Step 4: the shrink writes an fp32 buffer of rank width).
  *   x: DEVICE [T, d_in] (pool dtype);  v: DEVICE fp32 [T, max_rank].
  * SGMV requires lora_build_segments on the same ids and ws beforehand. */
 lora_status_t lora_shrink(const void *x, int32_t T, const lora_pool_t *pool, const int32_t *ids,
@@ -193,8 +235,13 @@ lora_status_t lora_shrink(const void *x, int32_t T, const lora_pool_t *pool, con
 
 /* ---- a5: expand ------------------------------------------------------------- */
 
-/* y[t,:] += s_a * v[t, 0:r_a] B_a for rows with a usable adapter a = ids[t];
- * other rows are not touched.  A read-modify-write of y (bf16 y is rounded
+/* The second low-rank product, added to the output:
+ * y[t,:] += s_a * v[t, 0:r_a] B_a for rows with a usable adapter a = ids[t];
+ * other rows are not touched ("Serving multiple LoRAs ...", section "Not
+ * merging the weights, computing in batches": (xA)B added to the base row;
+ * "LoRAX, in depth", section "Computing a batch that mixes adapters": the
+ * scale multiplies that product; "Serving LoRA adapters ...", Step 4: the
+ * expand is added to the base layer's output).  A read-modify-write of y (bf16 y is rounded
  * once, to nearest even, after the fp32 sum).
  *   v: DEVICE fp32 [T, max_rank];  y: DEVICE [T, d_out] (pool dtype).
  * SGMV requires lora_build_segments on the same ids and ws beforehand. */
@@ -204,7 +251,11 @@ lora_status_t lora_expand(const float *v, int32_t T, const lora_pool_t *pool, co
 
 /* ---- a3: base GEMM ---------------------------------------------------------- */
 
-/* y = x W (no adapters): x DEVICE [T, d_in], W DEVICE [d_in, d_out],
+/* The shared base product, once over every token row of the batch
+ * ("Multi-LoRA Serving: Architecture for Thousands of Adapters", section "How
+ * multi-LoRA serving works"; "LoRAX, in depth", section "Computing a batch
+ * that mixes adapters": the base output of all rows first).
+ * y = x W (no adapters): x DEVICE [T, d_in], W DEVICE [d_in, d_out],
  * y DEVICE [T, d_out], all of `dtype`; fp32 accumulation, one rounding.
  * ws (DEVICE, may be NULL) is scratch for a K split of small batches, used
  * only if ws_bytes holds the fp32 partials. */
@@ -225,7 +276,14 @@ lora_status_t lora_gemm_expand(const void *x, const void *W, void *y, int32_t T,
 
 /* ---- a3-a8: the whole layer -------------------------------------------------- */
 
-/* y = x W + s_a (x A_a) B_a per row (a = ids[t], -1 = none).
+/* The mixed-adapter LoRA linear layer ("Serving multiple LoRAs ...", section
+ * "Not merging the weights, computing in batches": y = xW + s (xA) B with
+ * each request's own adapter, by BGMV or SGMV; "LoRAX, in depth", section
+ * "Computing a batch that mixes adapters": one base product over all rows,
+ * then the low-rank term per adapter segment, none for rows without one;
+ * "Serving LoRA adapters ...", Steps 4 and 5: the wrapped layer and the
+ * token-to-slot mapping with -1 for no adapter):
+ * y = x W + s_a (x A_a) B_a per row (a = ids[t], -1 = none).
  * x DEVICE [T, pool->d_in], W DEVICE [d_in, d_out], y DEVICE [T, d_out]
  * (overwritten), ids DEVICE int32 [T].  `mode` picks BGMV/SGMV (AUTO by T);
  * in SGMV the segments are built in `ws` unless LORA_FLAG_SEGMENTS_READY says
@@ -304,7 +362,7 @@ lora_status_t lora_pack_host(int32_t d_in, int32_t d_out, int32_t max_rank, lora
 /* A residency cache over slots 0..n_slots-1 of n_pools pools (the projections
  * of one layer set, kept in step: slot s holds the same adapter in every pool;
  * every pool has at least n_slots slots, and all share one max_rank and one
- * dtype) for adapter ids
+ * dtype; packed pools are not supported: LORA_ERR_UNSUPPORTED) for adapter ids
  * 0..max_adapters-1.  n_pools == 0 gives a planning-only cache: the same
  * bookkeeping with no GPU work (for tests and schedulers).  The cache object
  * is host memory owned by the library until lora_cache_destroy; it creates

@@ -8,6 +8,6 @@ Every function here cites the passage of the pages it follows (see
 ``oracle.fp8``) holds the E4M3 quantization and the FP8-base layer.
 """
 from .oracle import (  # noqa: F401
-    BF16, F32, adapter_param_count, bf16_bits_from_f32, build_oracle, default_threads,
+    BF16, F32, adapter_param_count, affinity_cores, bf16_bits_from_f32, build_oracle, default_threads,
     f32_from_bf16_bits, lora_scale, oracle_rows, oracle_segmented, oracle_segments,
 )

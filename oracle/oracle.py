@@ -7,7 +7,7 @@ the HIP library under ``rank_adapter_gemm_amd/`` and never imports it.
 Contents
 --------
 ``lora_scale(alpha, r)``
-    s = alpha / r ("LoRAX, in depth", section "Computing a batch that mixes
+    s = alpha / r, one fp32 value per adapter ("LoRAX, in depth", section "Computing a batch that mixes
     adapters"; the value 2.0 = alpha / r in the example of "Serving multiple
     LoRAs ...", section "Not merging the weights, computing in batches").
 ``adapter_param_count(d_in, d_out, r)``
@@ -81,18 +81,35 @@ def _load():
     return _lib
 
 
-def default_threads() -> int:
+def affinity_cores() -> int:
+    """Cores in this process's affinity mask."""
     try:
         return max(1, len(os.sched_getaffinity(0)))
     except AttributeError:  # pragma: no cover
         return max(1, os.cpu_count() or 1)
 
 
+def default_threads() -> int:
+    """Worker threads: every core of the affinity mask, but no more than the
+    host's declared CPU share (OMP_NUM_THREADS) where one is set."""
+    n = affinity_cores()
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return n
+
+
 def lora_scale(alpha: float, r: int) -> float:
-    """s = alpha / r, in double, with the adapter's true rank."""
+    """s = alpha / r with the adapter's true rank ("LoRAX, in depth", section
+    "Computing a batch that mixes adapters"), held as one fp32 value per
+    adapter: alpha as an fp32 number divided by r in IEEE fp32 (one correctly
+    rounded quotient), then widened exactly to double.  The pages fix no
+    precision for s; a per-slot fp32 scale is the reading used for the whole
+    layer.  For alpha = 2r (and every scale the workloads use) s is a power
+    of two and exact in any precision."""
     if r <= 0:
         return 0.0
-    return float(alpha) / float(r)
+    return float(np.float32(alpha) / np.float32(r))
 
 
 def adapter_param_count(d_in: int, d_out: int, r: int) -> int:

@@ -22,7 +22,28 @@ inline bool valid_dims(int32_t n_slots, int32_t d_in, int32_t d_out, int32_t max
 
 inline bool valid_pool(const lora_pool_t *p) {
     return p && valid_dims(p->n_slots, p->d_in, p->d_out, p->max_rank) && valid_dtype(p->dtype) &&
-           p->a && p->b && p->scale && p->rank && aligned16(p->a) && aligned16(p->b);
+           p->a && p->b && p->scale && p->rank && aligned16(p->a) && aligned16(p->b) &&
+           (p->row0 == nullptr) == (p->row0_host == nullptr);
+}
+
+// Rank rows of one slot: max_rank (padded pool) or its capacity (packed).
+inline int32_t slot_capacity(const lora_pool_t *p, int32_t slot) {
+    return p->row0_host ? p->row0_host[slot + 1] - p->row0_host[slot] : p->max_rank;
+}
+
+// Packed-pool capacities: multiples of 8 in [8, max_rank]; their sum must
+// keep every element offset in range.  *rows gets the sum.
+inline bool valid_capacities(const int32_t *cap, int32_t n_slots, int32_t d_in, int32_t d_out, int32_t max_rank,
+                             int64_t *rows) {
+    if (!cap) return false;
+    int64_t total = 0;
+    for (int32_t s = 0; s < n_slots; ++s) {
+        if (cap[s] < 8 || cap[s] > max_rank || (cap[s] % 8)) return false;
+        total += cap[s];
+    }
+    if (total >= ((int64_t)1 << 31)) return false;
+    *rows = total;
+    return true;
 }
 
 inline lora_status_t check_ws(const void *ws, size_t ws_bytes, int32_t T, int32_t n_slots,
@@ -132,7 +153,65 @@ lora_status_t lora_pool_create(lora_pool_t *pool, int32_t n_slots, int32_t d_in,
     p.b = b;
     p.scale = scale;
     p.rank = rank;
+    p.row0 = nullptr;
+    p.row0_host = nullptr;
     st = launch_pool_fill(a, ab, b, bb, scale, rank, n_slots, hs(stream));
+    if (st == LORA_OK) *pool = p;
+    return st;
+}
+
+lora_status_t lora_pool_bytes_packed(int32_t n_slots, int32_t d_in, int32_t d_out, const int32_t *capacity,
+                                     lora_dtype_t dtype, size_t *a_bytes, size_t *b_bytes) {
+    if (!a_bytes || !b_bytes || !valid_dtype(dtype) || !capacity) return LORA_ERR_INVALID_ARGUMENT;
+    if (n_slots > kMaxSlots) return LORA_ERR_UNSUPPORTED;
+    if (!valid_dims(n_slots, d_in, d_out, 8)) return LORA_ERR_INVALID_ARGUMENT;
+    int32_t cmax = 8;
+    for (int32_t s = 0; s < n_slots; ++s) cmax = capacity[s] > cmax ? capacity[s] : cmax;
+    int64_t rows = 0;
+    if (cmax > 128 || !valid_dims(n_slots, d_in, d_out, cmax) ||
+        !valid_capacities(capacity, n_slots, d_in, d_out, cmax, &rows))
+        return LORA_ERR_INVALID_ARGUMENT;
+    const size_t eb = dtype_bytes(dtype);
+    *a_bytes = (size_t)rows * d_in * eb;
+    *b_bytes = (size_t)rows * d_out * eb;
+    return LORA_OK;
+}
+
+lora_status_t lora_pool_create_packed(lora_pool_t *pool, int32_t n_slots, int32_t d_in, int32_t d_out,
+                                      int32_t max_rank, lora_dtype_t dtype, const int32_t *capacity,
+                                      int32_t *row0_host, void *a, void *b, float *scale, int32_t *rank,
+                                      int32_t *row0, lora_stream_t stream) {
+    if (!pool || !capacity || !row0_host || !row0 || !a || !b || !scale || !rank || !aligned16(a) ||
+        !aligned16(b) || !valid_dtype(dtype))
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (n_slots > kMaxSlots) return LORA_ERR_UNSUPPORTED;
+    int64_t rows = 0;
+    if (!valid_dims(n_slots, d_in, d_out, max_rank) ||
+        !valid_capacities(capacity, n_slots, d_in, d_out, max_rank, &rows))
+        return LORA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)rows * d_in >= ((int64_t)1 << 40) || (int64_t)rows * d_out >= ((int64_t)1 << 40))
+        return LORA_ERR_UNSUPPORTED;
+    row0_host[0] = 0;
+    for (int32_t s = 0; s < n_slots; ++s) row0_host[s + 1] = row0_host[s] + capacity[s];
+    const hipStream_t st_ = hs(stream);
+    if (hipMemcpyAsync(row0, row0_host, sizeof(int32_t) * (size_t)(n_slots + 1), hipMemcpyHostToDevice, st_) !=
+        hipSuccess)
+        return LORA_ERR_HIP;
+    lora_pool_t p;
+    p.n_slots = n_slots;
+    p.d_in = d_in;
+    p.d_out = d_out;
+    p.max_rank = max_rank;
+    p.dtype = dtype;
+    p.a = a;
+    p.b = b;
+    p.scale = scale;
+    p.rank = rank;
+    p.row0 = row0;
+    p.row0_host = row0_host;
+    const size_t eb = dtype_bytes(dtype);
+    lora_status_t st = launch_pool_fill(a, (size_t)rows * d_in * eb, b, (size_t)rows * d_out * eb, scale, rank,
+                                        n_slots, st_);
     if (st == LORA_OK) *pool = p;
     return st;
 }
@@ -142,7 +221,7 @@ lora_status_t lora_pool_upload(const lora_pool_t *pool, int32_t slot, const void
                                lora_stream_t stream) {
     if (!valid_pool(pool)) return LORA_ERR_INVALID_ARGUMENT;
     if (slot < 0 || slot >= pool->n_slots) return LORA_ERR_SLOT_OUT_OF_RANGE;
-    if (r > pool->max_rank) return LORA_ERR_RANK_EXCEEDS_MAX;
+    if (r > pool->max_rank || r > slot_capacity(pool, slot)) return LORA_ERR_RANK_EXCEEDS_MAX;
     if (r < 1 || !A || !B || lda < r || ldb < pool->d_out) return LORA_ERR_INVALID_ARGUMENT;
     return launch_pool_upload(*pool, slot, A, lda, B, ldb, r, alpha, hs(stream));
 }

@@ -117,6 +117,7 @@ lora_status_t lora_cache_create(lora_cache_t **out, int32_t n_slots, const lora_
         if (q.n_slots < n_slots || !q.a || !q.b || !q.scale || !q.rank || q.max_rank < 8 ||
             q.max_rank > 128 || q.max_rank != pools[0].max_rank || q.dtype != pools[0].dtype)
             return LORA_ERR_INVALID_ARGUMENT;
+        if (q.row0 || q.row0_host) return LORA_ERR_UNSUPPORTED;   // slots of one size only
     }
     lora_cache *c = new (std::nothrow) lora_cache;
     if (!c) return LORA_ERR_UNSUPPORTED;

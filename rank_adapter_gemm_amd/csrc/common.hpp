@@ -97,6 +97,15 @@ __device__ __forceinline__ void dma16(const void *gptr, const void *lds_wave_bas
                  : "memory", "m0");
 }
 
+// First rank row of slot s in a pool's A^T rows (times d_in: its first
+// element) and in its B octet rows (times d_out).  A padded pool (row0 null)
+// gives every slot max_rank rows; a packed pool gives slot s the rows
+// [row0[s], row0[s+1]).  Kernels read only rows below the slot's rank, and a
+// slot's rank never exceeds its row count.
+__device__ __forceinline__ int64_t slot_row0(const int32_t *row0, int32_t s, int32_t max_rank) {
+    return row0 ? (int64_t)row0[s] : (int64_t)s * max_rank;
+}
+
 // Row visited at sorted position p: identity without perm; a perm entry
 // outside [0, T) (segments not built for this batch) yields -1 = skip.
 __device__ __forceinline__ int32_t perm_row(const int32_t *perm, int32_t p, int32_t T) {

@@ -1,9 +1,10 @@
 // a5 -- expand as its own pass: y[t,:] += s_a * (v[t, 0:r] B_a).
 //
 // "Serving multiple LoRAs: segmented matrix multiplies and adapter
-// scheduling", section "Not merging the weights, computing in batches" (then
-// expand (xA) -> (xA)B and add it to the base output), with the scale applied
-// to the product as in lora_mixed_batch ("LoRAX, in depth", section
+// scheduling", section "Not merging the weights, computing in batches": the
+// second of the two low-rank products maps the rank-r vector back to d_out
+// values, which are added to the base product's row; the scale multiplies
+// that product, as in lora_mixed_batch ("LoRAX, in depth", section
 // "Computing a batch that mixes adapters").
 //
 // One workgroup per (token row, 2048-column chunk); each lane owns 8
@@ -24,6 +25,7 @@ __global__ void __launch_bounds__(256) k_expand_rows(const float *__restrict__ v
                                                      const typename elem<DT>::T *__restrict__ b,
                                                      const float *__restrict__ scale,
                                                      const int32_t *__restrict__ rank,
+                                                     const int32_t *__restrict__ row0,
                                                      int32_t n_slots, int32_t max_rank,
                                                      int32_t v_stride,
                                                      const int32_t *__restrict__ ids,
@@ -37,7 +39,7 @@ __global__ void __launch_bounds__(256) k_expand_rows(const float *__restrict__ v
     if (t < 0) return;
     const int32_t id = ids[t];
     if (id < 0 || id >= n_slots) return;
-    const int32_t r = rank[id];
+    const int32_t r = min(rank[id], max_rank);
     if (r <= 0) return;
     const float s = scale[id];
     for (int j = threadIdx.x; j < max_rank; j += 256) s_v[j] = v[(size_t)t * v_stride + j];
@@ -45,7 +47,7 @@ __global__ void __launch_bounds__(256) k_expand_rows(const float *__restrict__ v
     const int n0 = (blockIdx.y * 256 + threadIdx.x) * 8;
     if (n0 >= d_out) return;
     const int G = (r + 7) >> 3;
-    const E *bs = b + (size_t)id * max_rank * d_out;
+    const E *bs = b + slot_row0(row0, id, max_rank) * d_out;
     float acc[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
@@ -92,11 +94,11 @@ lora_status_t launch_expand(const float *v, int32_t v_stride, int32_t T, const l
     const dim3 grid(T, (p.d_out + 2047) / 2048);
     if (p.dtype == LORA_F32)
         hipLaunchKernelGGL(k_expand_rows<LORA_F32>, grid, dim3(256), 0, s, v, T, p.d_out,
-                           (const float *)p.b, p.scale, p.rank, p.n_slots, p.max_rank, v_stride, ids, perm,
+                           (const float *)p.b, p.scale, p.rank, p.row0, p.n_slots, p.max_rank, v_stride, ids, perm,
                            (float *)y);
     else
         hipLaunchKernelGGL(k_expand_rows<LORA_BF16>, grid, dim3(256), 0, s, v, T, p.d_out,
-                           (const uint16_t *)p.b, p.scale, p.rank, p.n_slots, p.max_rank, v_stride, ids,
+                           (const uint16_t *)p.b, p.scale, p.rank, p.row0, p.n_slots, p.max_rank, v_stride, ids,
                            perm, (uint16_t *)y);
     return hip_status(hipGetLastError());
 }

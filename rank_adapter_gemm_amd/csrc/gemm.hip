@@ -91,9 +91,9 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
     // t = m0 + tn + i * n_tiles_n (i < 64 / R) that fall in its row tile.
     // The A^T slices of those rows' adapters ride along in every DMA stage
     // (chunk c: row i, rank j, 8 k), so x, already in LDS for the base
-    // product, is read from HBM once.  All max_rank rows of a slot's A^T are
-    // loaded: those past the slot's rank are zero in the pool, so the first
-    // DMA waits on the ids alone.
+    // product, is read from HBM once.  Only the slot's first r rank rows are
+    // read from the pool; the stage slots of ranks past r take the zero
+    // vector, so A's bytes follow each adapter's true rank.
     int64_t arow[AI > 0 ? AI : 1];
     int acol[AI > 0 ? AI : 1];
     const int R = g.max_rank;
@@ -107,7 +107,7 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
             int64_t off = -1;
             if (t < T && t - m0 < BM) {
                 const int32_t id = g.ids[t];
-                if (id >= 0 && id < g.n_slots) off = ((int64_t)id * R + j) * K;
+                if (id >= 0 && id < g.n_slots && j < g.rank[id]) off = (slot_row0(g.row0, id, R) + j) * K;
             }
             arow[jj] = off;
             acol[jj] = 8 * q;
@@ -343,6 +343,7 @@ struct gemm_f32_args {
     const float *b;
     const float *scale;
     const int32_t *rank;
+    const int32_t *row0;
     int32_t n_slots, max_rank;
     const int32_t *ids;
     const float *v;
@@ -402,7 +403,7 @@ __global__ void __launch_bounds__(256) k_gemm_f32(gemm_f32_args g) {
             const int32_t raw = g.ids[t];
             if (raw >= 0 && raw < g.n_slots && g.rank[raw] > 0) {
                 id = raw;
-                r = g.rank[raw];
+                r = min(g.rank[raw], g.max_rank);
                 s = g.scale[raw];
             }
         }
@@ -412,7 +413,7 @@ __global__ void __launch_bounds__(256) k_gemm_f32(gemm_f32_args g) {
             if (n >= N) continue;
             float val = acc[i][j];
             if (LORA && id >= 0) {
-                const float *bq = g.b + ((int64_t)id * g.max_rank * N + (int64_t)n * 8);
+                const float *bq = g.b + (slot_row0(g.row0, id, g.max_rank) * N + (int64_t)n * 8);
                 const float *vi = g.v + t * g.v_stride;
                 float d = 0.0f;
                 for (int q = 0; q < r; ++q) d = fmaf(vi[q], bq[(int64_t)(q >> 3) * N * 8 + (q & 7)], d);
@@ -493,6 +494,7 @@ lora_status_t launch_gemm_fused_shrink(const void *x, const void *W, void *y, in
     g.b = (const uint16_t *)pool->b;
     g.scale = pool->scale;
     g.rank = pool->rank;
+    g.row0 = pool->row0;
     g.n_slots = pool->n_slots;
     g.max_rank = pool->max_rank;
     g.ids = ids;
@@ -563,7 +565,7 @@ lora_status_t launch_gemm_grouped(const void *x, const void *const *W, void *con
     int tn0 = 0;
     for (int i = 0; i < n; ++i) {
         g.sl[i] = gemm_slice{(const uint16_t *)W[i], (uint16_t *)y[i], Ns[i], tn0, (const uint16_t *)pools[i].b,
-                             pools[i].scale, pools[i].rank, v_off[i]};
+                             pools[i].scale, pools[i].rank, pools[i].row0, v_off[i]};
         tn0 += ceil_div(Ns[i], pl.bn);
     }
     // fields a slice overrides start at slice 0 (never read before selection)
@@ -573,6 +575,7 @@ lora_status_t launch_gemm_grouped(const void *x, const void *const *W, void *con
     g.b = g.sl[0].b;
     g.scale = g.sl[0].scale;
     g.rank = g.sl[0].rank;
+    g.row0 = g.sl[0].row0;
     g.n_tiles_m = ceil_div(T, pl.bm);
     g.n_tiles_n = tn0;
     g.col_strips = col_strips_pay(T, tn0 * pl.bn, tn0);
@@ -600,6 +603,7 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
         g.b = pool ? (const uint16_t *)pool->b : nullptr;
         g.scale = pool ? pool->scale : nullptr;
         g.rank = pool ? pool->rank : nullptr;
+        g.row0 = pool ? pool->row0 : nullptr;
         g.n_slots = pool ? pool->n_slots : 0;
         g.max_rank = pool ? pool->max_rank : 0;
         g.ids = ids;
@@ -633,6 +637,7 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
         g.b = pool ? (const float *)pool->b : nullptr;
         g.scale = pool ? pool->scale : nullptr;
         g.rank = pool ? pool->rank : nullptr;
+        g.row0 = pool ? pool->row0 : nullptr;
         g.n_slots = pool ? pool->n_slots : 0;
         g.max_rank = pool ? pool->max_rank : 0;
         g.ids = ids;

@@ -17,6 +17,7 @@ struct gemm_slice {
     const uint16_t *b;
     const float *scale;
     const int32_t *rank;
+    const int32_t *row0;
     int32_t v_off;
 };
 
@@ -29,6 +30,7 @@ struct gemm_args {
     const uint16_t *b;
     const float *scale;
     const int32_t *rank;
+    const int32_t *row0;           // packed pool: first rank row per slot; padded: null
     int32_t n_slots, max_rank;
     const int32_t *ids;
     const float *v;                // [T][v_stride] fp32, this pool's ranks at columns 0..max_rank-1
@@ -65,6 +67,7 @@ __device__ __forceinline__ int select_slice(gemm_args &g, int tn) {
     g.b = q.b;
     g.scale = q.scale;
     g.rank = q.rank;
+    g.row0 = q.row0;
     if (g.v) g.v += q.v_off;
     return tn - q.tn0;
 }
@@ -152,18 +155,29 @@ template <int NREAD, int NMFMA> __device__ __forceinline__ void sched_interleave
 // Loads of one 16-rank step ks of adapter a for one lane: its row's 8 ranks
 // of v (zeroed later unless the row belongs to a) and its columns' B octets
 // (zero past the slot's rank or the last column).
+// A slot's first rank row (see slot_row0), as a 32-bit index: loaded beside
+// the slot's rank and scale, so the B loads below wait for one round trip.
+__device__ __forceinline__ int32_t slot_row0_i(const gemm_args &g, int32_t a) {
+    return a < 0 ? 0 : (g.row0 ? g.row0[a] : a * g.max_rank);
+}
+
+// A value every lane of the wavefront holds (taken from one lane by a
+// shuffle), moved to a scalar register; the loads that depend on it become
+// scalar loads, which keeps the vector registers for the accumulators.
+__device__ __forceinline__ int32_t uniform_i(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
 template <int CB>
-__device__ __forceinline__ void lora_step_load(const gemm_args &g, int32_t a, int32_t ra, bool mine,
+__device__ __forceinline__ void lora_step_load(const gemm_args &g, int32_t a, int32_t ra, int32_t ro, bool mine,
                                                int32_t my_t, int ks, int half, int wcol0, int lane,
                                                float4 &v0, float4 &v1, uint4 (&bq)[CB]) {
-    const int R = g.max_rank, N = g.N;
+    const int N = g.N;
     const int j0 = 16 * ks + 8 * half;
     const int oct = 2 * ks + half;
     const bool j_ok = a >= 0 && j0 < ra;              // octets past the slot's rank: not read
     const float *vp = g.v + (mine && j_ok ? (int64_t)my_t * g.v_stride + j0 : 0);
     v0 = *reinterpret_cast<const float4 *>(vp);
     v1 = *reinterpret_cast<const float4 *>(vp + 4);
-    const int64_t abase = (int64_t)(a >= 0 ? a : 0) * R * N;
+    const int64_t abase = (int64_t)ro * N;            // slot a's first B octet row (ro = its first rank row)
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         const int col = wcol0 + cb * 32 + (lane & 31);
@@ -220,7 +234,7 @@ __device__ __forceinline__ void lora_pass_impl(const gemm_args &g, f32x16_t (&ac
     static_assert(RB % RG == 0 && (RF == 0 || RB % RF == 0), "row blocks come in whole groups");
     constexpr int RFG = RF > 0 ? RF : 1;
     const int half = lane >> 5;
-    int32_t my_id[RB], my_t[RB], my_r[RB], a0[RB], ra0[RB];
+    int32_t my_id[RB], my_t[RB], my_r[RB], my_o[RB], a0[RB], ra0[RB], ro0[RB];
     float my_s[RB], sa0[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -228,9 +242,10 @@ __device__ __forceinline__ void lora_pass_impl(const gemm_args &g, f32x16_t (&ac
         my_id[rb] = s_id[row];
         my_t[rb] = s_t[row];
         const uint64_t pend = __ballot(my_id[rb] >= 0) & 0xffffffffull;
-        a0[rb] = pend ? __shfl(my_id[rb], __ffsll((long long)pend) - 1, 64) : -1;
+        a0[rb] = uniform_i(pend ? __shfl(my_id[rb], __ffsll((long long)pend) - 1, 64) : -1);
         ra0[rb] = a0[rb] >= 0 ? g.rank[a0[rb]] : 0;
         sa0[rb] = a0[rb] >= 0 ? g.scale[a0[rb]] : 0.0f;
+        ro0[rb] = slot_row0_i(g, a0[rb]);
     }
 #pragma unroll
     for (int r0 = 0; r0 < RB; r0 += RG) {
@@ -244,8 +259,8 @@ __device__ __forceinline__ void lora_pass_impl(const gemm_args &g, f32x16_t (&ac
             for (int i = 0; i < RG; ++i)
 #pragma unroll
                 for (int u = 0; u < KB; ++u)
-                    lora_step_load<CB>(g, a0[r0 + i], ra0[r0 + i], my_id[r0 + i] == a0[r0 + i], my_t[r0 + i],
-                                       ks0 + u, half, wcol0, lane, v0[i][u], v1[i][u], bq[i][u]);
+                    lora_step_load<CB>(g, a0[r0 + i], ra0[r0 + i], ro0[r0 + i], my_id[r0 + i] == a0[r0 + i],
+                                       my_t[r0 + i], ks0 + u, half, wcol0, lane, v0[i][u], v1[i][u], bq[i][u]);
 #pragma unroll
             for (int i = 0; i < RG; ++i)
 #pragma unroll
@@ -264,15 +279,16 @@ __device__ __forceinline__ void lora_pass_impl(const gemm_args &g, f32x16_t (&ac
             uint64_t pend = __ballot(my_id[rb] >= 0 && my_id[rb] != a0[rb]) & 0xffffffffull;
             while (pend) {
                 const int first = __ffsll((long long)pend) - 1;
-                const int32_t a = __shfl(my_id[rb], first, 64);
+                const int32_t a = uniform_i(__shfl(my_id[rb], first, 64));
                 pend &= ~(__ballot(my_id[rb] == a) & 0xffffffffull);
                 const int32_t ra = g.rank[a];
                 const float sa = g.scale[a];
+                const int32_t ro = slot_row0_i(g, a);
                 const bool mine = my_id[rb] == a;
                 for (int ks = 0; ks * 16 < ra; ++ks) {
                     float4 v0, v1;
                     uint4 bq[CB];
-                    lora_step_load<CB>(g, a, ra, mine, my_t[rb], ks, half, wcol0, lane, v0, v1, bq);
+                    lora_step_load<CB>(g, a, ra, ro, mine, my_t[rb], ks, half, wcol0, lane, v0, v1, bq);
                     lora_step_mfma<CB>(acc[rb], sa, mine && 16 * ks + 8 * half < ra, v0, v1, bq);
                 }
             }
@@ -284,6 +300,7 @@ __device__ __forceinline__ void lora_pass_impl(const gemm_args &g, f32x16_t (&ac
     for (int rb = 0; rb < RB; ++rb) {
         my_r[rb] = my_id[rb] >= 0 ? g.rank[my_id[rb]] : 0;
         my_s[rb] = my_id[rb] >= 0 ? g.scale[my_id[rb]] : 0.0f;
+        my_o[rb] = slot_row0_i(g, my_id[rb]);
     }
 #pragma unroll
     for (int r0 = 0; r0 < RB; r0 += RFG) {
@@ -295,7 +312,7 @@ __device__ __forceinline__ void lora_pass_impl(const gemm_args &g, f32x16_t (&ac
             any |= pend[i];
         }
         while (any) {                                       // wave-uniform
-            int32_t a[RFG], ra[RFG];
+            int32_t a[RFG], ra[RFG], ro[RFG];
             float sa[RFG];
             bool mine[RFG];
             int nks = 0;
@@ -304,12 +321,14 @@ __device__ __forceinline__ void lora_pass_impl(const gemm_args &g, f32x16_t (&ac
             for (int i = 0; i < RFG; ++i) {
                 a[i] = -1;
                 ra[i] = 0;
+                ro[i] = 0;
                 sa[i] = 0.0f;
                 if (pend[i]) {
                     const int first = __ffsll((long long)pend[i]) - 1;
-                    a[i] = __shfl(my_id[r0 + i], first, 64);
-                    ra[i] = __shfl(my_r[r0 + i], first, 64);
-                    sa[i] = __shfl(my_s[r0 + i], first, 64);
+                    a[i] = uniform_i(__shfl(my_id[r0 + i], first, 64));
+                    ra[i] = uniform_i(__shfl(my_r[r0 + i], first, 64));
+                    ro[i] = uniform_i(__shfl(my_o[r0 + i], first, 64));
+                    sa[i] = __int_as_float(uniform_i(__float_as_int(__shfl(my_s[r0 + i], first, 64))));
                     pend[i] &= ~(__ballot(my_id[r0 + i] == a[i]) & 0xffffffffull);
                 }
                 mine[i] = a[i] >= 0 && my_id[r0 + i] == a[i];
@@ -321,8 +340,8 @@ __device__ __forceinline__ void lora_pass_impl(const gemm_args &g, f32x16_t (&ac
                 uint4 bq[RFG][CB];
 #pragma unroll
                 for (int i = 0; i < RFG; ++i)
-                    lora_step_load<CB>(g, a[i], ra[i], mine[i], my_t[r0 + i], ks, half, wcol0, lane, v0[i], v1[i],
-                                       bq[i]);
+                    lora_step_load<CB>(g, a[i], ra[i], ro[i], mine[i], my_t[r0 + i], ks, half, wcol0, lane, v0[i],
+                                       v1[i], bq[i]);
 #pragma unroll
                 for (int i = 0; i < RFG; ++i)
                     if (16 * ks < ra[i])                   // wave-uniform
@@ -419,6 +438,12 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g0) {
     const bool slot_ok = raw >= 0 && raw < g.n_slots;
     float4 pa[SP], pb[SP];
     uint4 bq[GP][8];
+    // B of a padded slot is prefetched from its first GP octets (at most
+    // max_rank ranks, all inside the slot, zero past its rank); a packed
+    // slot's octets past its capacity belong to the next slot, so there only
+    // the first octet (every slot holds at least 8 ranks) is prefetched.
+    const int gp_pre = g.row0 ? 1 : GP;
+    int64_t bbase = 0;
     if (t >= 0) {
 #pragma unroll
         for (int sidx = 0; sidx < SP; ++sidx)
@@ -428,10 +453,11 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g0) {
                 pb[sidx] = *reinterpret_cast<const float4 *>(src + 4);
             }
         if (LORA && slot_ok) {
+            bbase = slot_row0(g.row0, raw, R) * N;
 #pragma unroll
             for (int gg = 0; gg < GP; ++gg)
-                if (8 * gg < R) {
-                    const uint16_t *bp = g.b + ((int64_t)raw * R * N + ((int64_t)gg * N + n) * 8);
+                if (8 * gg < R && gg < gp_pre) {
+                    const uint16_t *bp = g.b + (bbase + ((int64_t)gg * N + n) * 8);
 #pragma unroll
                     for (int q = 0; q < 8; ++q) bq[gg][q] = ldg16(bp + q * 8);
                 }
@@ -440,7 +466,7 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g0) {
     int32_t rk = 0;
     float sc = 0.0f;
     if (LORA && t >= 0 && slot_ok) {
-        rk = g.rank[raw];
+        rk = min(g.rank[raw], R);
         sc = g.scale[raw];
     }
     const int G = (rk + 7) >> 3;
@@ -482,11 +508,11 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g0) {
         for (int gg = 0; gg < G; ++gg) {
             const float4 v0 = *reinterpret_cast<const float4 *>(vrow + gg * 8);
             const float4 v1 = *reinterpret_cast<const float4 *>(vrow + gg * 8 + 4);
-            const uint16_t *bp = g.b + ((int64_t)raw * R * N + ((int64_t)gg * N + n) * 8);
+            const uint16_t *bp = g.b + (bbase + ((int64_t)gg * N + n) * 8);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 uint4 bw;
-                if (gg < GP) {
+                if (gg < GP && gg < gp_pre) {
 #pragma unroll
                     for (int u = 0; u < GP; ++u)
                         if (u == gg) bw = bq[u][q];

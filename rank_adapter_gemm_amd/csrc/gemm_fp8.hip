@@ -394,6 +394,7 @@ lora_status_t launch_gemm_fp8(const uint8_t *xq, const float *xs, const uint8_t 
     g.b = pool ? (const uint16_t *)pool->b : nullptr;
     g.scale = pool ? pool->scale : nullptr;
     g.rank = pool ? pool->rank : nullptr;
+    g.row0 = pool ? pool->row0 : nullptr;
     g.n_slots = pool ? pool->n_slots : 0;
     g.max_rank = pool ? pool->max_rank : 0;
     g.ids = ids;

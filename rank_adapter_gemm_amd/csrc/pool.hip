@@ -7,12 +7,14 @@
 // slot buffers sized for the maximum LoRA rank; "Serving multiple LoRAs ...",
 // exercise 2: kernels allocate by the maximum rank).
 //
-// Layout per slot (chosen for the kernels' reads):
-//   A^T [max_rank][d_in]           a rank row is contiguous over d_in, so the
-//                                  shrink reads only the first r rows;
-//   B   [max_rank/8][d_out][8]     8 consecutive ranks of one output column are
-//                                  16 contiguous bytes (bf16), so the expand
-//                                  reads only the first ceil(r/8) octets.
+// Layout per slot (chosen for the kernels' reads), C = max_rank rank rows
+// (padded pool) or the slot's own capacity (packed pool, slots back to back
+// from row0[s]):
+//   A^T [C][d_in]           a rank row is contiguous over d_in, so the
+//                           shrink reads only the first r rows;
+//   B   [C/8][d_out][8]     8 consecutive ranks of one output column are
+//                           16 contiguous bytes (bf16), so the expand
+//                           reads only the first ceil(r/8) octets.
 #include "common.hpp"
 
 namespace lora {
@@ -33,9 +35,9 @@ __global__ void __launch_bounds__(256) k_fill_meta(float *scale, int32_t *rank, 
 template <typename E>
 __global__ void __launch_bounds__(256) k_upload(E *a_slot, E *b_slot, const E *A, int32_t lda,
                                                 const E *B, int32_t ldb, int32_t r, int32_t d_in,
-                                                int32_t d_out, int32_t max_rank) {
-    const size_t na = (size_t)max_rank * d_in;
-    const size_t nb = (size_t)max_rank * d_out;
+                                                int32_t d_out, int32_t rows) {
+    const size_t na = (size_t)rows * d_in;
+    const size_t nb = (size_t)rows * d_out;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < na; e += stride) {
         const int32_t j = (int32_t)(e / d_in), i = (int32_t)(e % d_in);  // A^T[j][i] = A[i][j]
@@ -73,21 +75,36 @@ lora_status_t launch_pool_fill(void *a, size_t a_bytes, void *b, size_t b_bytes,
     return hip_status(hipGetLastError());
 }
 
+// First rank row and rank-row count of a slot (host side): padded pools give
+// every slot max_rank rows, packed pools the rows [row0[s], row0[s+1]).
+static void slot_rows(const lora_pool_t &p, int32_t slot, size_t &row0, int32_t &rows) {
+    if (p.row0_host) {
+        row0 = (size_t)p.row0_host[slot];
+        rows = p.row0_host[slot + 1] - p.row0_host[slot];
+    } else {
+        row0 = (size_t)slot * p.max_rank;
+        rows = p.max_rank;
+    }
+}
+
 lora_status_t launch_pool_upload(const lora_pool_t &p, int32_t slot, const void *A, int32_t lda,
                                  const void *B, int32_t ldb, int32_t r, float alpha, hipStream_t s) {
     const size_t eb = p.dtype == LORA_F32 ? 4 : 2;
-    const size_t a_slot = (size_t)p.max_rank * p.d_in, b_slot = (size_t)p.max_rank * p.d_out;
+    size_t row0;
+    int32_t rows;
+    slot_rows(p, slot, row0, rows);
+    const size_t a_slot = (size_t)rows * p.d_in, b_slot = (size_t)rows * p.d_out;
     const size_t n = a_slot > b_slot ? a_slot : b_slot;
-    char *a = (char *)p.a + (size_t)slot * a_slot * eb;
-    char *b = (char *)p.b + (size_t)slot * b_slot * eb;
+    char *a = (char *)p.a + row0 * p.d_in * eb;
+    char *b = (char *)p.b + row0 * p.d_out * eb;
     if (p.dtype == LORA_F32)
         hipLaunchKernelGGL(k_upload<uint32_t>, dim3(grid_for(n)), dim3(256), 0, s, (uint32_t *)a,
                            (uint32_t *)b, (const uint32_t *)A, lda, (const uint32_t *)B, ldb, r,
-                           p.d_in, p.d_out, p.max_rank);
+                           p.d_in, p.d_out, rows);
     else
         hipLaunchKernelGGL(k_upload<uint16_t>, dim3(grid_for(n)), dim3(256), 0, s, (uint16_t *)a,
                            (uint16_t *)b, (const uint16_t *)A, lda, (const uint16_t *)B, ldb, r,
-                           p.d_in, p.d_out, p.max_rank);
+                           p.d_in, p.d_out, rows);
     // s = alpha / r in fp32 ("LoRAX, in depth", section "Computing a batch
     // that mixes adapters"), kept per slot and applied at expand time.
     hipLaunchKernelGGL(k_set_meta, dim3(1), dim3(64), 0, s, p.scale, p.rank, slot,
@@ -145,9 +162,12 @@ lora_status_t launch_pool_meta(const lora_pool_t &p, int32_t slot, float scale, 
 
 lora_status_t launch_pool_clear(const lora_pool_t &p, int32_t slot, hipStream_t s) {
     const size_t eb = p.dtype == LORA_F32 ? 4 : 2;
-    const size_t a_bytes = (size_t)p.max_rank * p.d_in * eb, b_bytes = (size_t)p.max_rank * p.d_out * eb;
-    char *a = (char *)p.a + (size_t)slot * a_bytes;
-    char *b = (char *)p.b + (size_t)slot * b_bytes;
+    size_t row0;
+    int32_t rows;
+    slot_rows(p, slot, row0, rows);
+    const size_t a_bytes = (size_t)rows * p.d_in * eb, b_bytes = (size_t)rows * p.d_out * eb;
+    char *a = (char *)p.a + row0 * p.d_in * eb;
+    char *b = (char *)p.b + row0 * p.d_out * eb;
     hipLaunchKernelGGL(k_fill_zero, dim3(grid_for(a_bytes / 16)), dim3(256), 0, s, (uint4 *)a, a_bytes / 16);
     hipLaunchKernelGGL(k_fill_zero, dim3(grid_for(b_bytes / 16)), dim3(256), 0, s, (uint4 *)b, b_bytes / 16);
     hipLaunchKernelGGL(k_set_meta, dim3(1), dim3(64), 0, s, p.scale, p.rank, slot, 0.0f, 0);

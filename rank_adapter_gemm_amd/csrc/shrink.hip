@@ -1,16 +1,17 @@
 // a4 -- shrink: v[t, 0:r] = x[t,:] A_a  (fp32 result of rank width).
 //
 // "Serving multiple LoRAs: segmented matrix multiplies and adapter
-// scheduling", section "Not merging the weights, computing in batches"
-// (first shrink x -> xA down to r dimensions), and "Serving LoRA adapters:
-// from the model name to the wrapped layer", Step 4 (shrink into an fp32
-// buffer of rank width).  The BGMV form gathers each token's own A; the SGMV
+// scheduling", section "Not merging the weights, computing in batches": the
+// low-rank term is computed in two products, and this is the first, which
+// maps each token row from d_in values to r; "Serving LoRA adapters: from the
+// model name to the wrapped layer", Step 4: its result is kept in an fp32
+// buffer of rank width.  The BGMV form gathers each token's own A; the SGMV
 // form walks adapter-contiguous segments so one read of A serves a segment.
 //
 // Two kernels:
 //  * k_shrink_rows  (BGMV): one 512-thread workgroup per token row; x[t] is
-//    read once with 16-byte coalesced loads, the slot's A^T rows (max_rank
-//    of them, masked by its rank) are gathered in batches of independent loads, each lane keeps
+//    read once with 16-byte coalesced loads, the slot's first r A^T rows (its
+//    true rank) are gathered in batches of independent loads, each lane keeps
 //    per-rank partial sums, which are reduced across the wavefront with a
 //    transposing butterfly of cross-lane swaps and then across the 8
 //    wavefronts through LDS.  fp32 or bf16 inputs.
@@ -29,6 +30,7 @@ namespace lora {
 struct slice_set {
     const void *a[kMaxSlices];
     const int32_t *rank[kMaxSlices];
+    const int32_t *row0[kMaxSlices];     // packed pools: first rank row per slot; padded: null
     int32_t n;
 };
 
@@ -106,11 +108,11 @@ __global__ void __launch_bounds__(512) k_shrink_rows(const typename elem<DT>::T 
         for (int j = tid; j < max_rank; j += NW * 64) vt[j] = 0.0f;
         continue;
     }
-    // The slot's rank only masks the sums: the loads cover max_rank rows
-    // (a slot's rows past its rank are zero in the pool), so they go out
-    // together with the rank's, one round trip after the id.
-    const int32_t r = ss.rank[sl][id];
-    const E *At = reinterpret_cast<const E *>(ss.a[sl]) + (size_t)id * max_rank * d_in;
+    // Only the slot's first r rank rows are read (its rank and, in a packed
+    // pool, its first row come one round trip after the id): the bytes of A
+    // follow the adapter's true rank, not the pool's max_rank.
+    const int32_t r = min(ss.rank[sl][id], max_rank);
+    const E *At = reinterpret_cast<const E *>(ss.a[sl]) + slot_row0(ss.row0[sl], id, max_rank) * d_in;
     float acc[RM];
 #pragma unroll
     for (int j = 0; j < RM; ++j) acc[j] = 0.0f;
@@ -118,18 +120,18 @@ __global__ void __launch_bounds__(512) k_shrink_rows(const typename elem<DT>::T 
     for (int kv = tid; kv < nvec; kv += NW * 64) {
         const uint4 xq = ldg16(xt + (size_t)kv * VN);
         float xf[VN];
+        if (r > 0) vec16<DT>::widen(xq, xf);
 #pragma unroll
         for (int c = 0; c < RM; c += RC) {
-            if (c < max_rank) {                           // uniform: rows left in the slot
-                // RC independent loads in flight; rows past max_rank re-read
-                // the last row (a cache hit) and are masked out below.
+            if (c < r) {                                  // uniform: rank rows left in the slot
+                // RC independent loads in flight; rows past the rank re-read
+                // the last rank row (a cache hit) and are masked out below.
                 uint4 aq[RC];
 #pragma unroll
                 for (int j = 0; j < RC; ++j) {
-                    const int row = min(c + j, max_rank - 1);
+                    const int row = min(c + j, r - 1);
                     aq[j] = ldg16(At + (size_t)row * d_in + (size_t)kv * VN);
                 }
-                if (c == 0) vec16<DT>::widen(xq, xf);
 #pragma unroll
                 for (int j = 0; j < RC; ++j) {
                     float af[VN];
@@ -300,7 +302,8 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
         // rank column r of the concatenated slices: slice r / max_rank
         const int sl = r / max_rank, jj = r - sl * max_rank;
         const int32_t rs = sl < ss.n ? ss.rank[sl][aid] : 0;
-        arow[j] = jj < rs ? reinterpret_cast<const uint16_t *>(ss.a[sl]) + ((int64_t)aid * max_rank + jj) * d_in
+        arow[j] = jj < rs ? reinterpret_cast<const uint16_t *>(ss.a[sl]) +
+                                (slot_row0(ss.row0[sl], aid, max_rank) + jj) * d_in
                           : nullptr;
         acol[j] = 8 * (slot ^ (r % CH));
     }
@@ -440,6 +443,7 @@ lora_status_t launch_quant_shrink_rows(const void *x, int32_t T, const lora_pool
     for (int i = 0; i < kMaxSlices; ++i) {
         ss.a[i] = pool->a;
         ss.rank[i] = pool->rank;
+        ss.row0[i] = pool->row0;
     }
     const uint16_t *xe = (const uint16_t *)x;
 #define LORA_QSHRINK_ROWS(RMV)                                                                            \
@@ -464,6 +468,7 @@ lora_status_t launch_shrink(const void *x, int32_t T, const lora_pool_t *pools, 
         const lora_pool_t &q = pools[i < n_slices ? i : 0];
         ss.a[i] = q.a;
         ss.rank[i] = q.rank;
+        ss.row0[i] = q.row0;
     }
     const int32_t VS = n_slices * p.max_rank;
     int32_t *err = ws_ptr<int32_t>(ws, L.header);

@@ -34,7 +34,8 @@ LORA_FLAG_SEPARATE_EXPAND = 0x2
 
 # Every symbol include/lora.h declares.
 EXPORTED = (
-    "lora_pool_bytes", "lora_pool_create", "lora_pool_upload", "lora_pool_clear",
+    "lora_pool_bytes", "lora_pool_create", "lora_pool_bytes_packed", "lora_pool_create_packed",
+    "lora_pool_upload", "lora_pool_clear",
     "lora_workspace_bytes", "lora_workspace_init", "lora_segments_view", "lora_build_segments",
     "lora_shrink", "lora_expand", "lora_gemm", "lora_gemm_expand", "lora_linear_forward",
     "lora_workspace_bytes_sliced", "lora_shrink_sliced", "lora_linear_forward_sliced",
@@ -57,7 +58,8 @@ class lora_pool_t(ctypes.Structure):
     _fields_ = [("n_slots", ctypes.c_int32), ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32),
                 ("max_rank", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("a", ctypes.c_void_p), ("b", ctypes.c_void_p),
-                ("scale", ctypes.c_void_p), ("rank", ctypes.c_void_p)]
+                ("scale", ctypes.c_void_p), ("rank", ctypes.c_void_p),
+                ("row0", ctypes.c_void_p), ("row0_host", ctypes.c_void_p)]
 
 
 class lora_segments_t(ctypes.Structure):
@@ -98,6 +100,9 @@ def load(path: str = LIB_PATH):
     sig = {
         "lora_pool_bytes": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, P(c_sz), P(c_sz)]),
         "lora_pool_create": (c_i32, [P(lora_pool_t), c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
+        "lora_pool_bytes_packed": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_i32, P(c_sz), P(c_sz)]),
+        "lora_pool_create_packed": (c_i32, [P(lora_pool_t), c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp,
+                                            c_vp, c_vp, c_vp, c_vp, c_vp]),
         "lora_pool_upload": (c_i32, [P(lora_pool_t), c_i32, c_vp, c_i32, c_vp, c_i32, c_i32, c_f, c_vp]),
         "lora_pool_clear": (c_i32, [P(lora_pool_t), c_i32, c_vp]),
         "lora_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32]),
@@ -188,6 +193,31 @@ def lora_pool_create(n_slots, d_in, d_out, max_rank, dtype, a, b, scale, rank, s
     pool = lora_pool_t()
     _ok(load().lora_pool_create(ctypes.byref(pool), n_slots, d_in, d_out, max_rank, dtype, _ptr(a),
                                 _ptr(b), _ptr(scale), _ptr(rank), _stream(stream)), "lora_pool_create")
+    return pool
+
+
+def lora_pool_bytes_packed(n_slots, d_in, d_out, capacity, dtype):
+    """capacity: a host int32 array (numpy or list) of n_slots rank-row counts."""
+    import numpy as np
+    cap = np.ascontiguousarray(np.asarray(capacity, dtype=np.int32))
+    a = ctypes.c_size_t()
+    b = ctypes.c_size_t()
+    _ok(load().lora_pool_bytes_packed(n_slots, d_in, d_out, cap.ctypes.data, dtype, ctypes.byref(a),
+                                      ctypes.byref(b)), "lora_pool_bytes_packed")
+    return a.value, b.value
+
+
+def lora_pool_create_packed(n_slots, d_in, d_out, max_rank, dtype, capacity, row0_host, a, b, scale, rank, row0,
+                            stream=None):
+    """capacity: host int32 array [n_slots]; row0_host: host int32 numpy array [n_slots + 1] that the
+    caller keeps alive as long as the pool (the descriptor points at it)."""
+    import numpy as np
+    cap = np.ascontiguousarray(np.asarray(capacity, dtype=np.int32))
+    assert row0_host.dtype == np.int32 and row0_host.flags.c_contiguous and row0_host.size == n_slots + 1
+    pool = lora_pool_t()
+    _ok(load().lora_pool_create_packed(ctypes.byref(pool), n_slots, d_in, d_out, max_rank, dtype, cap.ctypes.data,
+                                       row0_host.ctypes.data, _ptr(a), _ptr(b), _ptr(scale), _ptr(rank), _ptr(row0),
+                                       _stream(stream)), "lora_pool_create_packed")
     return pool
 
 
@@ -393,18 +423,32 @@ def lora_version() -> str:
 
 # ---- plumbing: device buffers held by torch ------------------------------------------
 class AdapterPool:
-    """Owns the torch device buffers of one pool and its lora_pool_t."""
+    """Owns the torch device buffers of one pool and its lora_pool_t.  With
+    `capacity` (n_slots rank-row counts, multiples of 8) the pool is packed:
+    slot s holds capacity[s] rank rows, with no padding to max_rank."""
 
-    def __init__(self, n_slots, d_in, d_out, max_rank, dtype: torch.dtype, device="cuda", stream=None):
+    def __init__(self, n_slots, d_in, d_out, max_rank, dtype: torch.dtype, device="cuda", stream=None,
+                 capacity=None):
+        import numpy as np
         code = dtype_code(dtype)
-        a_bytes, b_bytes = lora_pool_bytes(n_slots, d_in, d_out, max_rank, code)
+        if capacity is None:
+            a_bytes, b_bytes = lora_pool_bytes(n_slots, d_in, d_out, max_rank, code)
+        else:
+            a_bytes, b_bytes = lora_pool_bytes_packed(n_slots, d_in, d_out, capacity, code)
         self.a = torch.empty(a_bytes, dtype=torch.uint8, device=device)
         self.b = torch.empty(b_bytes, dtype=torch.uint8, device=device)
         self.scale = torch.empty(n_slots, dtype=torch.float32, device=device)
         self.rank = torch.empty(n_slots, dtype=torch.int32, device=device)
         self.dtype = dtype
-        self.pool = lora_pool_create(n_slots, d_in, d_out, max_rank, code, self.a, self.b,
-                                     self.scale, self.rank, stream)
+        if capacity is None:
+            self.row0 = self.row0_host = None
+            self.pool = lora_pool_create(n_slots, d_in, d_out, max_rank, code, self.a, self.b,
+                                         self.scale, self.rank, stream)
+        else:
+            self.row0 = torch.empty(n_slots + 1, dtype=torch.int32, device=device)
+            self.row0_host = np.zeros(n_slots + 1, dtype=np.int32)
+            self.pool = lora_pool_create_packed(n_slots, d_in, d_out, max_rank, code, capacity, self.row0_host,
+                                                self.a, self.b, self.scale, self.rank, self.row0, stream)
 
     def upload(self, slot, A, B, r, alpha, lda=None, ldb=None, stream=None):
         lora_pool_upload(self.pool, slot, A, B, r, alpha, lda, ldb, stream)

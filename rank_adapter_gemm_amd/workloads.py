@@ -187,32 +187,45 @@ def make_workload(name: str, device: str | torch.device = "cpu", seed: int | Non
     return wl
 
 
-def sample_rows(wl: Workload, n_random: int = 32, seed: int = 0, max_rows: int | None = None) -> np.ndarray:
-    """A bounded, seeded row sample for oracle checks at full size: the first
-    and last row of every adapter run in sorted order, up to 2 rows per
-    distinct adapter, up to 16 base-only rows, the first and last row of the
-    batch, plus n_random uniform rows."""
+def sample_rows(wl: Workload, n_random: int = 32, seed: int = 0, max_rows: int | None = None,
+                n_base: int = 64) -> np.ndarray:
+    """A seeded, stratified row sample for oracle checks at full size.
+
+    Strata, in priority order: the first row of every adapter segment (rows
+    in stable sorted order, so one row per distinct adapter and rank class),
+    the last row of every segment, up to two further rows per segment, up to
+    n_base base-only rows, the first and last row of the batch, and n_random
+    uniform rows.  Without max_rows every stratum is kept whole; with it the
+    strata are taken in that order until max_rows rows are reached, so a
+    truncated sample still holds one row of every adapter before anything
+    else."""
     rng = np.random.default_rng(seed)
     ids = wl.ids
     T = wl.T
-    rows = {0, T - 1}
     order = np.argsort(ids, kind="stable")
     sid = ids[order]
     starts = np.flatnonzero(np.r_[True, sid[1:] != sid[:-1]])
     ends = np.r_[starts[1:], T] - 1
-    for s, e in zip(starts, ends):
-        rows.add(int(order[s]))
-        rows.add(int(order[e]))
-        if e > s:
-            rows.update(int(order[i]) for i in rng.choice(np.arange(s, e + 1), size=min(2, e - s + 1),
-                                                         replace=False))
+    firsts, lasts, inner = [], [], []
     base = np.flatnonzero(ids < 0)
-    if base.size:
-        rows.update(int(i) for i in rng.choice(base, size=min(16, base.size), replace=False))
-    rows.update(int(i) for i in rng.integers(0, T, size=n_random))
-    out = np.asarray(sorted(rows), dtype=np.int64)
-    if max_rows is not None and out.size > max_rows:
-        keep = {0, T - 1}
-        keep.update(int(i) for i in rng.choice(out, size=max_rows - 2, replace=False))
-        out = np.asarray(sorted(keep), dtype=np.int64)
-    return out
+    for s, e in zip(starts, ends):
+        if sid[s] < 0:
+            continue
+        firsts.append(int(order[s]))
+        lasts.append(int(order[e]))
+        if e - s >= 2:
+            inner.extend(int(order[i]) for i in rng.choice(np.arange(s + 1, e), size=min(2, e - s - 1),
+                                                          replace=False))
+    base_pick = [int(i) for i in rng.choice(base, size=min(n_base, base.size), replace=False)] if base.size else []
+    strata = [firsts, lasts, inner, base_pick, [0, T - 1], [int(i) for i in rng.integers(0, T, size=n_random)]]
+    rows: list = []
+    seen = set()
+    for stratum in strata:
+        for r in stratum:
+            if r in seen:
+                continue
+            if max_rows is not None and len(rows) >= max_rows:
+                break
+            seen.add(r)
+            rows.append(r)
+    return np.asarray(sorted(rows), dtype=np.int64)

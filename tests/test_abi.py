@@ -56,6 +56,45 @@ def test_pool_bytes():
         L.lora_pool_bytes(4, 64, 64, 8, 7)
 
 
+def test_packed_pool_bytes_and_validation(lib):
+    """A packed pool stores each slot's own rank rows: bytes are sum(capacity)
+    rows of d_in (A) and of d_out (B) instead of n_slots * max_rank; the
+    capacities must be multiples of 8 in [8, 128]; an upload above a slot's
+    capacity is LORA_ERR_RANK_EXCEEDS_MAX before anything is enqueued."""
+    import numpy as np
+    cap = [8, 16, 32, 64, 8]
+    a, b = L.lora_pool_bytes_packed(5, 8192, 28672, cap, L.LORA_BF16)
+    assert a == sum(cap) * 8192 * 2 and b == sum(cap) * 28672 * 2
+    pa, pb = L.lora_pool_bytes(5, 8192, 28672, 64, L.LORA_BF16)
+    assert a * 320 == pa * 128 and b * 320 == pb * 128        # 128 of 320 padded rows
+    for bad in ([8, 12], [8, 0], [8, 136], [4, 8]):
+        with pytest.raises(L.LoraError) as e:
+            L.lora_pool_bytes_packed(len(bad), 64, 64, bad, L.LORA_BF16)
+        assert e.value.status == L.LORA_ERR_INVALID_ARGUMENT
+    fake = 1 << 40
+    row0 = np.array([0, 8, 24, 56], dtype=np.int32)            # capacities 8, 16, 32
+    p = L.lora_pool_t(3, 64, 64, 32, L.LORA_BF16, fake, fake, fake, fake, fake, row0.ctypes.data)
+    up = lib.lora_pool_upload
+    assert up(ctypes.byref(p), 0, fake, 9, fake, 64, 9, 1.0, None) == L.LORA_ERR_RANK_EXCEEDS_MAX
+    assert up(ctypes.byref(p), 1, fake, 17, fake, 64, 17, 1.0, None) == L.LORA_ERR_RANK_EXCEEDS_MAX
+    assert up(ctypes.byref(p), 2, fake, 33, fake, 64, 33, 1.0, None) == L.LORA_ERR_RANK_EXCEEDS_MAX
+    assert up(ctypes.byref(p), 3, fake, 8, fake, 64, 8, 1.0, None) == L.LORA_ERR_SLOT_OUT_OF_RANGE
+    # a descriptor with only one of row0 / row0_host is not a valid pool
+    half = L.lora_pool_t(3, 64, 64, 32, L.LORA_BF16, fake, fake, fake, fake, fake, None)
+    assert up(ctypes.byref(half), 0, fake, 8, fake, 64, 8, 1.0, None) == L.LORA_ERR_INVALID_ARGUMENT
+    # creation checks its capacities (and max_rank against them) before any GPU work
+    cr = lib.lora_pool_create_packed
+    out = L.lora_pool_t()
+    r0 = np.zeros(4, dtype=np.int32)
+    for caps, R in (([8, 16, 44], 64), ([8, 16, 64], 32), ([8, 16, 0], 32)):
+        c = np.asarray(caps, dtype=np.int32)
+        assert cr(ctypes.byref(out), 3, 64, 64, R, L.LORA_BF16, c.ctypes.data, r0.ctypes.data, fake, fake, fake,
+                  fake, fake, None) == L.LORA_ERR_INVALID_ARGUMENT
+    # packed pools cannot back a residency cache
+    h = ctypes.c_void_p()
+    assert lib.lora_cache_create(ctypes.byref(h), 3, ctypes.byref(p), 1, 8) == L.LORA_ERR_UNSUPPORTED
+
+
 def test_workspace_bytes():
     assert L.lora_workspace_bytes(-1, 4, 8) == 0
     assert L.lora_workspace_bytes(10, 0, 8) == 0

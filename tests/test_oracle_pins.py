@@ -410,6 +410,9 @@ def test_scale_values():
     assert lora_scale(4.0, 2) == 2.0 and lora_scale(2.0, 2) == 1.0
     assert lora_scale(2 * 64, 64) == 2.0
     assert lora_scale(5.0, 0) == 0.0
+    # one fp32 value per adapter: 1/3 is the fp32 number 0x3eaaaaab = 11184811 * 2^-25
+    assert lora_scale(1.0, 3) == 11184811 / 2 ** 25
+    assert lora_scale(1.0, 3) != 1.0 / 3.0
 
 
 # ---------------------------------------------------------------------------
