@@ -72,20 +72,34 @@ typedef enum {
 typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype_t;
 
 /* How the low-rank term is batched ("Serving multiple LoRAs ...", section
- * "Not merging the weights, computing in batches"):
+ * "Not merging the weights, computing in batches": BGMV gathers each
+ * request's adapter, the form for decode; SGMV shares one adapter read per
+ * segment, the form for prefill; "Multi-LoRA Serving: Architecture for
+ * Thousands of Adapters", section "S-LoRA, Punica and the batched kernels":
+ * separate prefill and decode kernels):
  *   BGMV: every row gathers its own adapter (rows in their original order);
  *   SGMV: rows are grouped into adapter-contiguous segments (a stable sort by
  *         slot, built by lora_build_segments) and each segment shares one
  *         read of its adapter;
- *   AUTO: in lora_linear_forward, SGMV when T >= 1024, else BGMV; in
- *         lora_shrink and lora_expand (which cannot know whether segments
- *         were built), BGMV.
+ *   AUTO: in the forwards, a batch of fewer than 1024 rows is all BGMV (its
+ *         segments are short); a larger one is split per segment: segments
+ *         of at least L rows (the prefill chunks) take SGMV -- the grouped
+ *         shrink and the expand fused into the base GEMM -- and shorter ones
+ *         (decode rows) take BGMV -- the per-row shrink and a per-row expand
+ *         after the GEMM.  L is 16 by default, or LORA_FLAG_SHORT_SEGMENT(L)
+ *         for bf16 pools.  In lora_shrink and lora_expand (which cannot know
+ *         whether segments were built), AUTO is BGMV.
  * The result does not depend on the mode beyond fp32 rounding order. */
 typedef enum { LORA_MODE_AUTO = 0, LORA_MODE_BGMV = 1, LORA_MODE_SGMV = 2 } lora_mode_t;
 
-/* Flags for lora_linear_forward. */
+/* Flags for the forwards (lora_linear_forward, _sliced, _fp8). */
 #define LORA_FLAG_SEGMENTS_READY 0x1  /* segments already built in this workspace for these ids */
 #define LORA_FLAG_SEPARATE_EXPAND 0x2 /* expand as its own read-modify-write pass, not in the GEMM epilogue */
+/* AUTO mode: segments of fewer than L rows (1 <= L <= 255) take the per-row
+ * path; 0 (no flag) means the default, 16.  Used when the forward builds
+ * the segments (a later call with LORA_FLAG_SEGMENTS_READY follows the
+ * build). */
+#define LORA_FLAG_SHORT_SEGMENT(L) ((((uint32_t)(L)) & 0xffu) << 8)
 
 /*
  * The HBM adapter pool of one projection: n_slots stacked slots (the stacked
@@ -132,9 +146,18 @@ typedef struct {
  *   n_seg     [1]            number of adapter segments (the -1 block is not one)
  * ("Serving multiple LoRAs ...": the stable argsort by adapter and the
  * consecutive-unique counts of the SGMV routine; "LoRAX, in depth":
- * segment boundaries of length n_segments + 1 and the owner of each). */
+ * segment boundaries of length n_segments + 1 and the owner of each).
+ * Two more arrays order the rows for the base GEMM of a mixed batch:
+ *   gemm_perm [T]            the rows of the -1 block and of every segment of
+ *                            at least L rows, in perm order, then the rows of
+ *                            the shorter segments, in perm order (a stable
+ *                            partition of perm; L is the short-segment
+ *                            threshold of the build, 1 for lora_build_segments,
+ *                            so there gemm_perm equals perm)
+ *   n_fused   [1]            the number of rows before the short segments'. */
 typedef struct {
     int32_t *offsets, *perm, *seg_id, *seg_start, *n_seg;
+    int32_t *gemm_perm, *n_fused;
 } lora_segments_t;
 
 /* ---- a1: adapter pool ----------------------------------------------------- */
@@ -267,9 +290,13 @@ lora_status_t lora_gemm(const void *x, const void *W, void *y, int32_t T, int32_
 
 /* y = x W + s_a v[t, 0:r_a] B_a per row (the expand inside the GEMM
  * epilogue, one rounding), with v from lora_shrink on the same ids.  In SGMV
- * mode the GEMM visits rows in segment order (lora_build_segments on the same
- * ids and ws first); BGMV and AUTO keep the original row order.  Shapes and
- * dtypes as for lora_linear_forward; v DEVICE fp32 [T, max_rank]. */
+ * mode the GEMM visits rows in the GEMM order of the segments built in ws
+ * (lora_build_segments, or a forward, on the same ids first): the rows of
+ * segments shorter than the build's threshold come last and get their term
+ * from a per-row expand after the GEMM (bf16 pools; two roundings for those
+ * rows), exactly the GEMM step of lora_linear_forward.  BGMV and AUTO keep
+ * the original row order.  Shapes and dtypes as for lora_linear_forward;
+ * v DEVICE fp32 [T, max_rank]. */
 lora_status_t lora_gemm_expand(const void *x, const void *W, void *y, int32_t T,
                                const lora_pool_t *pool, const int32_t *ids, const float *v,
                                lora_mode_t mode, void *ws, size_t ws_bytes, lora_stream_t stream);

@@ -68,6 +68,18 @@ inline bool use_sgmv(lora_mode_t mode, int32_t T) {
     return T >= 1024;
 }
 
+// Flag bits the forwards accept: the two flags and the short-segment threshold.
+constexpr uint32_t kForwardFlags = LORA_FLAG_SEGMENTS_READY | LORA_FLAG_SEPARATE_EXPAND | 0xff00u;
+
+// Segments of fewer rows than this take the per-row path: AUTO mode on bf16
+// pools (the threshold from the flags, else the default); SGMV mode groups
+// every segment.
+inline int32_t short_len_for(lora_mode_t mode, uint32_t flags, int32_t dtype) {
+    if (mode != LORA_MODE_AUTO || dtype != LORA_BF16) return 1;
+    const int32_t n = (int32_t)((flags >> 8) & 0xffu);
+    return n > 0 ? n : kShortSegDefault;
+}
+
 inline bool valid_mode(int32_t m) {
     return m == LORA_MODE_AUTO || m == LORA_MODE_BGMV || m == LORA_MODE_SGMV;
 }
@@ -87,12 +99,16 @@ inline lora_status_t check_slices(const lora_pool_t *pools, int32_t n) {
 }
 
 // Base product plus the low-rank term from v (row stride v_stride), fused
-// into the GEMM or as a separate pass.
+// into the GEMM or as a separate pass.  With segments, the GEMM visits rows
+// in the GEMM order (long segments, then short ones), fuses the term of the
+// long segments' rows and leaves the short segments' rows to a per-row
+// expand after it.
 lora_status_t gemm_and_expand(const void *x, const void *W, void *y, int32_t T, const lora_pool_t &p,
                               const int32_t *ids, const float *v, int32_t v_stride, bool sgmv,
                               uint32_t flags, const ws_layout &L, void *ws, size_t ws_bytes,
                               hipStream_t s) {
-    const int32_t *perm = sgmv ? ws_ptr<int32_t>(ws, L.perm) : nullptr;
+    const int32_t *gperm = sgmv ? ws_ptr<int32_t>(ws, L.gperm) : nullptr;
+    const int32_t *n_fused = sgmv ? ws_ptr<int32_t>(ws, L.header) + kHdrNLong : nullptr;
     float *partial = ws_ptr<float>(ws, L.gemm_partial);
     const size_t partial_bytes = ws_bytes - L.gemm_partial;
     if (flags & LORA_FLAG_SEPARATE_EXPAND) {
@@ -101,8 +117,10 @@ lora_status_t gemm_and_expand(const void *x, const void *W, void *y, int32_t T, 
         if (st != LORA_OK) return st;
         return launch_expand(v, v_stride, T, p, ids, sgmv, y, L, ws, s);
     }
-    return launch_gemm(x, W, y, T, p.d_in, p.d_out, p.dtype, &p, ids, v, v_stride, perm, partial,
-                       partial_bytes, s);
+    lora_status_t st = launch_gemm(x, W, y, T, p.d_in, p.d_out, p.dtype, &p, ids, v, v_stride, gperm, partial,
+                                   partial_bytes, s, p.dtype == LORA_BF16 ? n_fused : nullptr);
+    if (st == LORA_OK && sgmv) st = launch_expand_short(v, v_stride, T, p, y, L, ws, s);
+    return st;
 }
 
 }  // namespace
@@ -255,6 +273,8 @@ lora_status_t lora_segments_view(void *ws, size_t ws_bytes, int32_t T, int32_t n
     out->seg_id = ws_ptr<int32_t>(ws, L.seg_id);
     out->seg_start = ws_ptr<int32_t>(ws, L.seg_start);
     out->n_seg = ws_ptr<int32_t>(ws, L.n_seg);
+    out->gemm_perm = ws_ptr<int32_t>(ws, L.gperm);
+    out->n_fused = ws_ptr<int32_t>(ws, L.header) + kHdrNLong;
     return LORA_OK;
 }
 
@@ -317,16 +337,17 @@ lora_status_t lora_gemm_expand(const void *x, const void *W, void *y, int32_t T,
     lora_status_t st = check_ws(ws, ws_bytes, T, pool->n_slots, pool->max_rank, &L);
     if (st != LORA_OK) return st;
     if (T == 0) return LORA_OK;
-    const int32_t *perm = (mode == LORA_MODE_SGMV) ? ws_ptr<int32_t>(ws, L.perm) : nullptr;
-    return launch_gemm(x, W, y, T, pool->d_in, pool->d_out, pool->dtype, pool, ids, v, pool->max_rank,
-                       perm, ws_ptr<float>(ws, L.gemm_partial), ws_bytes - L.gemm_partial, hs(stream));
+    // SGMV: the GEMM step of a forward -- rows in the GEMM order of the
+    // segments in ws, the short segments' rows expanded after the GEMM.
+    return gemm_and_expand(x, W, y, T, *pool, ids, v, pool->max_rank, mode == LORA_MODE_SGMV, 0, L, ws, ws_bytes,
+                           hs(stream));
 }
 
 lora_status_t lora_linear_forward(const void *x, const void *W, void *y, int32_t T,
                                   const lora_pool_t *pool, const int32_t *ids, lora_mode_t mode,
                                   uint32_t flags, void *ws, size_t ws_bytes,
                                   lora_stream_t stream) {
-    if (!valid_pool(pool) || T < 0 || !valid_mode(mode) || (flags & ~3u))
+    if (!valid_pool(pool) || T < 0 || !valid_mode(mode) || (flags & ~kForwardFlags))
         return LORA_ERR_INVALID_ARGUMENT;
     if (T > 0 && (!x || !W || !y || !ids || !aligned16(x) || !aligned16(W) || !aligned16(y)))
         return LORA_ERR_INVALID_ARGUMENT;
@@ -337,7 +358,7 @@ lora_status_t lora_linear_forward(const void *x, const void *W, void *y, int32_t
     const hipStream_t s = hs(stream);
     const bool sgmv = use_sgmv(mode, T);
     if (sgmv && !(flags & LORA_FLAG_SEGMENTS_READY)) {
-        st = launch_segments(ids, T, pool->n_slots, L, ws, s);
+        st = launch_segments(ids, T, pool->n_slots, L, ws, s, short_len_for(mode, flags, pool->dtype));
         if (st != LORA_OK) return st;
     }
     // Decode-sized BGMV batches: the shrink runs inside the split-K GEMM,
@@ -381,7 +402,7 @@ lora_status_t lora_linear_forward_sliced(const void *x, const void *const *W, vo
                                          void *ws, size_t ws_bytes, lora_stream_t stream) {
     lora_status_t st = check_slices(pools, n_slices);
     if (st != LORA_OK) return st;
-    if (T < 0 || !valid_mode(mode) || (flags & ~3u) || !W || !y) return LORA_ERR_INVALID_ARGUMENT;
+    if (T < 0 || !valid_mode(mode) || (flags & ~kForwardFlags) || !W || !y) return LORA_ERR_INVALID_ARGUMENT;
     if (T > 0) {
         if (!x || !ids || !aligned16(x)) return LORA_ERR_INVALID_ARGUMENT;
         for (int i = 0; i < n_slices; ++i)
@@ -407,10 +428,10 @@ lora_status_t lora_linear_forward_sliced(const void *x, const void *const *W, vo
     float *v = ws_ptr<float>(ws, L.v);
     if (any_shared) {
         if (sgmv && !(flags & LORA_FLAG_SEGMENTS_READY)) {
-            st = launch_segments(ids, T, pools[0].n_slots, L, ws, s);
+            st = launch_segments(ids, T, pools[0].n_slots, L, ws, s, short_len_for(mode, flags, pools[0].dtype));
             if (st != LORA_OK) return st;
         }
-        st = launch_shrink(x, T, pools, n_slices, ids, sgmv, v, L, ws, s);   // one x read, one launch
+        st = launch_shrink(x, T, pools, n_slices, ids, sgmv, v, L, ws, s);   // one x read for all slices
         if (st != LORA_OK) return st;
     }
     // bf16 slices on the shared shrink: one grouped GEMM with the fused
@@ -439,10 +460,14 @@ lora_status_t lora_linear_forward_sliced(const void *x, const void *const *W, vo
                                  ws_bytes, s);
         if (st != LORA_OK) return st;
     }
-    if (ng > 0)
+    if (ng > 0) {
         st = launch_gemm_grouped(x, gW, gy, T, gp, ng, ids, v, goff, VS,
-                                 sgmv ? ws_ptr<int32_t>(ws, L.perm) : nullptr, ws_ptr<float>(ws, L.gemm_partial),
-                                 ws_bytes - L.gemm_partial, s);
+                                 sgmv ? ws_ptr<int32_t>(ws, L.gperm) : nullptr, ws_ptr<float>(ws, L.gemm_partial),
+                                 ws_bytes - L.gemm_partial, s,
+                                 sgmv ? ws_ptr<int32_t>(ws, L.header) + kHdrNLong : nullptr);
+        for (int i = 0; i < ng && st == LORA_OK && sgmv; ++i)
+            st = launch_expand_short(v + goff[i], VS, T, gp[i], gy[i], L, ws, s);
+    }
     return st;
 }
 
@@ -485,7 +510,7 @@ lora_status_t lora_linear_forward_fp8(const void *x, const uint8_t *wq, const fl
                                       lora_mode_t mode, uint32_t flags, void *ws, size_t ws_bytes,
                                       lora_stream_t stream) {
     if (!valid_pool(pool) || pool->dtype != LORA_BF16 || (pool->d_in % 16) || T < 0 || !valid_mode(mode) ||
-        (flags & ~3u))
+        (flags & ~kForwardFlags))
         return LORA_ERR_INVALID_ARGUMENT;
     if (T > 0 && (!x || !wq || !w_scale || !y || !ids || !aligned16(x) || !aligned16(wq) ||
                   !aligned16(w_scale) || !aligned16(y)))
@@ -497,7 +522,7 @@ lora_status_t lora_linear_forward_fp8(const void *x, const uint8_t *wq, const fl
     const hipStream_t s = hs(stream);
     const bool sgmv = use_sgmv(mode, T);
     if (sgmv && !(flags & LORA_FLAG_SEGMENTS_READY)) {
-        st = launch_segments(ids, T, pool->n_slots, L, ws, s);
+        st = launch_segments(ids, T, pool->n_slots, L, ws, s, short_len_for(mode, flags, pool->dtype));
         if (st != LORA_OK) return st;
     }
     uint8_t *xq = ws_ptr<uint8_t>(ws, L.xq);
@@ -512,7 +537,7 @@ lora_status_t lora_linear_forward_fp8(const void *x, const uint8_t *wq, const fl
         st = launch_quant_shrink_rows(x, T, pool, ids, v, xq, xs, ws_ptr<int32_t>(ws, L.header), s);
     }
     if (st != LORA_OK) return st;
-    const int32_t *perm = sgmv ? ws_ptr<int32_t>(ws, L.perm) : nullptr;
+    const int32_t *gperm = sgmv ? ws_ptr<int32_t>(ws, L.gperm) : nullptr;
     float *partial = ws_ptr<float>(ws, L.gemm_partial);
     const size_t partial_bytes = ws_bytes - L.gemm_partial;
     if (flags & LORA_FLAG_SEPARATE_EXPAND) {
@@ -521,8 +546,10 @@ lora_status_t lora_linear_forward_fp8(const void *x, const uint8_t *wq, const fl
         if (st != LORA_OK) return st;
         return launch_expand(v, pool->max_rank, T, *pool, ids, sgmv, y, L, ws, s);
     }
-    return launch_gemm_fp8(xq, xs, wq, w_scale, y, T, pool->d_in, pool->d_out, pool, ids, v, pool->max_rank,
-                           perm, partial, partial_bytes, s);
+    st = launch_gemm_fp8(xq, xs, wq, w_scale, y, T, pool->d_in, pool->d_out, pool, ids, v, pool->max_rank, gperm,
+                         partial, partial_bytes, s, sgmv ? ws_ptr<int32_t>(ws, L.header) + kHdrNLong : nullptr);
+    if (st == LORA_OK && sgmv) st = launch_expand_short(v, pool->max_rank, T, *pool, y, L, ws, s);
+    return st;
 }
 
 lora_status_t lora_get_device_error(void *ws, size_t ws_bytes, lora_stream_t stream,
@@ -533,7 +560,7 @@ lora_status_t lora_get_device_error(void *ws, size_t ws_bytes, lora_stream_t str
     if (hipMemcpyAsync(&h, ws, sizeof h, hipMemcpyDeviceToHost, s) != hipSuccess) return LORA_ERR_HIP;
     if (hipStreamSynchronize(s) != hipSuccess) return LORA_ERR_HIP;
     *first_bad_row = (h == kErrNone) ? -1 : h;
-    return launch_ws_init(ws, s);
+    return launch_ws_init(ws, s, true);                   // the segments built stay valid
 }
 
 }  // extern "C"

@@ -124,6 +124,15 @@ __device__ __forceinline__ void flag_bad_row(int32_t *err, int32_t row) {
 // Workspace layout (host side).  Regions are 256-byte aligned.
 // ---------------------------------------------------------------------------
 constexpr int32_t kSegTile = 1024;     // rows per segment-builder tile
+// Mixed batches (AUTO mode): adapter segments shorter than this many rows
+// take the per-row (BGMV) shrink and expand, longer ones the grouped (SGMV)
+// shrink and the expand fused into the base GEMM.
+constexpr int32_t kShortSegDefault = 16;
+// Workspace header words (int32): the error word, the number of rows whose
+// low-rank term is fused into the GEMM (those before the short-segment rows
+// in the GEMM's row order), the short-segment threshold of the build and the
+// number of short segments.
+constexpr int32_t kHdrErr = 0, kHdrNLong = 1, kHdrShortLen = 2, kHdrNShort = 3;
 constexpr int32_t kShrinkRows = 32;    // rows of one segment per grouped-shrink work block
 constexpr int32_t kMaxKSplit = 16;     // shrink k-split factor bound
 constexpr int32_t kMaxSlices = 4;      // pools sharing one shrink (projections that share x)
@@ -146,6 +155,9 @@ struct ws_layout {
     size_t blk_start;   // int32[n_slots + 2]: first shrink work block of each segment
     size_t blk_seg;     // int32[ceil(T / kShrinkRows) + n_slots]: segment of each work block
     size_t perm;        // int32[T]
+    size_t gperm;       // int32[T]: the GEMM's row order (long-segment rows, then short-segment rows)
+    size_t gbase;       // int32[n_slots + 2]: first GEMM position of each key's rows
+    size_t skey;        // int32[n_slots]: key of each short segment, ascending
     size_t tile_hist;   // int32[(n_slots + 1) * n_tiles]
     size_t v;           // fp32[T * max_rank]
     size_t partial;     // fp32[kMaxKSplit * T * max_rank]
@@ -172,6 +184,9 @@ inline ws_layout make_ws_layout(int32_t T, int32_t n_slots, int32_t max_rank, in
     L.blk_start = o; o = align256(o + 4 * (size_t)(n_slots + 2));
     L.blk_seg = o;   o = align256(o + 4 * ((t + kShrinkRows - 1) / kShrinkRows + (size_t)n_slots + 1));
     L.perm = o;      o = align256(o + 4 * t);
+    L.gperm = o;     o = align256(o + 4 * t);
+    L.gbase = o;     o = align256(o + 4 * (size_t)(n_slots + 2));
+    L.skey = o;      o = align256(o + 4 * (size_t)n_slots);
     L.tile_hist = o; o = align256(o + 4 * (size_t)(n_slots + 1) * n_tiles);
     L.v = o;         o = align256(o + 4 * t * (size_t)max_rank);
     L.partial = o;   o = align256(o + 4 * (size_t)kMaxKSplit * t * (size_t)max_rank);
@@ -225,9 +240,15 @@ struct copy_batch {
     uint32_t max_bytes;
 };
 lora_status_t launch_copy_batch(const copy_batch &c, hipStream_t s);
-lora_status_t launch_ws_init(void *ws, hipStream_t s);
+lora_status_t launch_ws_init(void *ws, hipStream_t s, bool err_only = false);
+// Segments of ids (short_len: segments of fewer rows take the per-row path;
+// 1 = none do) into the workspace, with the GEMM's row order.
 lora_status_t launch_segments(const int32_t *ids, int32_t T, int32_t n_slots, const ws_layout &L,
-                              void *ws, hipStream_t s);
+                              void *ws, hipStream_t s, int32_t short_len = 1);
+// Separate expand of the short segments' rows (the GEMM left their term out),
+// one work item per short segment and column chunk.
+lora_status_t launch_expand_short(const float *v, int32_t v_stride, int32_t T, const lora_pool_t &p, void *y,
+                                  const ws_layout &L, void *ws, hipStream_t s);
 // Shrink for n_slices pools that share x, ids, n_slots, d_in, max_rank and
 // dtype: v[t][s * max_rank + j] for slice s (row stride n_slices * max_rank).
 lora_status_t launch_shrink(const void *x, int32_t T, const lora_pool_t *pools, int32_t n_slices,
@@ -244,14 +265,17 @@ lora_status_t launch_gemm_fused_shrink(const void *x, const void *W, void *y, in
                                        int32_t *err, float *partial, size_t partial_bytes,
                                        hipStream_t s);
 bool gemm_grouping_pays(int32_t T, int32_t K, const int32_t *Ns, int32_t n, size_t partial_bytes);
+// n_fused (device, may be null): rows at GEMM positions >= *n_fused get no
+// low-rank term here (the short-segment rows; their expand is separate).
 lora_status_t launch_gemm_grouped(const void *x, const void *const *W, void *const *y, int32_t T,
                                   const lora_pool_t *pools, int32_t n, const int32_t *ids, const float *v,
                                   const int32_t *v_off, int32_t v_stride, const int32_t *perm, float *partial,
-                                  size_t partial_bytes, hipStream_t s);
+                                  size_t partial_bytes, hipStream_t s, const int32_t *n_fused = nullptr);
 lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int32_t d_in,
                           int32_t d_out, int32_t dtype, const lora_pool_t *pool,
                           const int32_t *ids, const float *v, int32_t v_stride,
-                          const int32_t *perm, float *partial, size_t partial_bytes, hipStream_t s);
+                          const int32_t *perm, float *partial, size_t partial_bytes, hipStream_t s,
+                          const int32_t *n_fused = nullptr);
 // FP8 base (E4M3 codes, fp32 scales): per-row and per-column quantizers and
 // y = s_x s_w (xq wq^T) (+ s v B when pool != nullptr), bf16 y.
 lora_status_t launch_quant_rows_fp8(const void *x, int32_t T, int32_t K, uint8_t *xq, float *xs, hipStream_t s);
@@ -262,6 +286,6 @@ lora_status_t launch_quant_cols_fp8(const void *W, int32_t K, int32_t N, uint8_t
 lora_status_t launch_gemm_fp8(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *wsc, void *y,
                               int32_t T, int32_t d_in, int32_t d_out, const lora_pool_t *pool,
                               const int32_t *ids, const float *v, int32_t v_stride, const int32_t *perm,
-                              float *partial, size_t partial_bytes, hipStream_t s);
+                              float *partial, size_t partial_bytes, hipStream_t s, const int32_t *n_fused = nullptr);
 
 }  // namespace lora

@@ -210,11 +210,14 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
         __shared__ int32_t s_meta_t_buf[BM], s_meta_id_buf[BM];
         s_meta_t = s_meta_t_buf;
         s_meta_id = s_meta_id_buf;
+        // mixed batches: rows from GEMM position n_fused on (short segments)
+        // get their low-rank term from the separate per-row expand
+        const int32_t n_fused = (LORA && g.n_fused) ? *g.n_fused : T;
         for (int i = tid; i < BM; i += WV * 64) {
             const int p = m0 + i;
             const int32_t t = (p < T) ? perm_row(g.perm, p, T) : -1;
             int32_t id = -1;
-            if (LORA && t >= 0) {
+            if (LORA && t >= 0 && (!g.n_fused || p < n_fused)) {
                 const int32_t raw = g.ids[t];
                 if (raw >= 0 && raw < g.n_slots && g.rank[raw] > 0) id = raw;
             }
@@ -546,7 +549,7 @@ bool gemm_grouping_pays(int32_t T, int32_t K, const int32_t *Ns, int32_t n, size
 lora_status_t launch_gemm_grouped(const void *x, const void *const *W, void *const *y, int32_t T,
                                   const lora_pool_t *pools, int32_t n, const int32_t *ids, const float *v,
                                   const int32_t *v_off, int32_t v_stride, const int32_t *perm, float *partial,
-                                  size_t partial_bytes, hipStream_t s) {
+                                  size_t partial_bytes, hipStream_t s, const int32_t *n_fused) {
     if (n < 1 || n > kMaxSlices || pools[0].dtype != LORA_BF16) return LORA_ERR_INVALID_ARGUMENT;
     int32_t Ns[kMaxSlices];
     for (int i = 0; i < n; ++i) Ns[i] = pools[i].d_out;
@@ -560,6 +563,7 @@ lora_status_t launch_gemm_grouped(const void *x, const void *const *W, void *con
     g.ids = ids;
     g.v = v;
     g.v_stride = v_stride;
+    g.n_fused = n_fused;
     const gemm_plan pl = plan_gemm(T, g.K, Ns, n, partial ? partial_bytes : 0);
     g.n_slices = n;
     int tn0 = 0;
@@ -590,7 +594,8 @@ lora_status_t launch_gemm_grouped(const void *x, const void *const *W, void *con
 lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int32_t d_in,
                           int32_t d_out, int32_t dtype, const lora_pool_t *pool,
                           const int32_t *ids, const float *v, int32_t v_stride,
-                          const int32_t *perm, float *partial, size_t partial_bytes, hipStream_t s) {
+                          const int32_t *perm, float *partial, size_t partial_bytes, hipStream_t s,
+                          const int32_t *n_fused) {
     if (dtype == LORA_BF16) {
         gemm_args g{};
         g.x = (const uint16_t *)x;
@@ -609,6 +614,7 @@ lora_status_t launch_gemm(const void *x, const void *W, void *y, int32_t T, int3
         g.ids = ids;
         g.v = v;
         g.v_stride = v_stride;
+        g.n_fused = n_fused;
         const gemm_plan pl = plan_gemm(T, d_in, d_out, partial ? partial_bytes : 0);
         g.n_tiles_m = ceil_div(T, pl.bm);
         g.n_tiles_n = ceil_div(d_out, pl.bn);

@@ -46,6 +46,7 @@ struct gemm_args {
     const uint8_t *wq;             // FP8 base: E4M3 codes of the W columns [N][K]
     const float *xs;               // FP8 base: row scales [T] (powers of two)
     const float *wsc;              // FP8 base: column scales [N] (powers of two)
+    const int32_t *n_fused;        // mixed batches: rows at positions >= *n_fused get no low-rank term here
     int32_t col_strips;            // tile order: 1 = strips of kGroupN column tiles (see grouped_tile)
     int32_t n_slices;              // grouped launch: 0 (one output), else slices sl[0..n_slices)
     gemm_slice sl[kMaxSlices];     // column tiles numbered slice after slice
@@ -434,7 +435,8 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(gemm_args g0) {
     // ranks past its own are zero in the pool and are not summed), so they
     // wait for one round trip (the id), not two.
     const int32_t t = (p < T && n < N) ? perm_row(g.perm, p, T) : -1;
-    const int32_t raw = (LORA && t >= 0) ? g.ids[t] : -1;
+    const bool fused = !g.n_fused || p < *g.n_fused;      // short-segment rows: expanded separately
+    const int32_t raw = (LORA && t >= 0 && fused) ? g.ids[t] : -1;
     const bool slot_ok = raw >= 0 && raw < g.n_slots;
     float4 pa[SP], pb[SP];
     uint4 bq[GP][8];

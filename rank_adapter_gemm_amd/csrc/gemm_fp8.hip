@@ -260,11 +260,12 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_fp8(gemm_args g) {
     // Per-row metadata: token row, usable adapter slot or -1, E8M0 code of
     // the row scale (1.0 for rows past T).
     __shared__ int32_t s_meta_t[BM], s_meta_id[BM], s_esx[BM];
+    const int32_t n_fused = (LORA && g.n_fused) ? *g.n_fused : T;   // short-segment rows: separate expand
     for (int i = tid; i < BM; i += WV * 64) {
         const int p = m0 + i;
         const int32_t t = (p < T) ? perm_row(g.perm, p, T) : -1;
         int32_t id = -1;
-        if (LORA && t >= 0) {
+        if (LORA && t >= 0 && (!g.n_fused || p < n_fused)) {
             const int32_t raw = g.ids[t];
             if (raw >= 0 && raw < g.n_slots && g.rank[raw] > 0) id = raw;
         }
@@ -380,7 +381,7 @@ lora_status_t launch_quant_cols_fp8(const void *W, int32_t K, int32_t N, uint8_t
 lora_status_t launch_gemm_fp8(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *wsc, void *y,
                               int32_t T, int32_t d_in, int32_t d_out, const lora_pool_t *pool,
                               const int32_t *ids, const float *v, int32_t v_stride, const int32_t *perm,
-                              float *partial, size_t partial_bytes, hipStream_t s) {
+                              float *partial, size_t partial_bytes, hipStream_t s, const int32_t *n_fused) {
     gemm_args g{};
     g.xq = xq;
     g.wq = wq;
@@ -395,6 +396,7 @@ lora_status_t launch_gemm_fp8(const uint8_t *xq, const float *xs, const uint8_t 
     g.scale = pool ? pool->scale : nullptr;
     g.rank = pool ? pool->rank : nullptr;
     g.row0 = pool ? pool->row0 : nullptr;
+    g.n_fused = n_fused;
     g.n_slots = pool ? pool->n_slots : 0;
     g.max_rank = pool ? pool->max_rank : 0;
     g.ids = ids;

@@ -17,17 +17,21 @@
 //   1. per 1024-row tile, an LDS histogram of keys -> tile_hist[key][tile]
 //   2. one workgroup: exclusive scan of tile_hist in (key, tile) order, so
 //      entry (key, tile) becomes the first output position of that tile's rows
-//      with that key; offsets[], then the compaction of non-empty keys >= 1
+//      with that key; offsets[], the GEMM order's key bases (long segments
+//      first, short ones last), then the compaction of non-empty keys >= 1
 //   3. per tile, each row's rank among the earlier rows of its tile with the
 //      same key (stable: the tile's (key, row) pairs sorted in LDS),
-//      perm[base + rank] = t.
+//      perm[base + rank] = t, and its place in the GEMM order.
 #include "common.hpp"
 
 namespace lora {
 
-__global__ void k_ws_init(int32_t *header) {
+// Workspace header: the error word to "none"; with `all`, every other
+// header word (the segment build's) to zero as well.
+__global__ void k_ws_init(int32_t *header, int32_t all) {
     const int i = threadIdx.x;
-    if (i < 64) header[i] = (i == 0) ? kErrNone : 0;
+    if (i == 0) header[0] = kErrNone;
+    else if (all && i < 64) header[i] = 0;
 }
 
 __device__ __forceinline__ int32_t row_key(int32_t id, int32_t n_slots) {
@@ -85,7 +89,7 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *s_wa
 }
 
 // Compaction of non-empty adapter keys (k >= 1) in ascending order, and the
-// shrink work table: segment i covers work blocks [blk_start[i],
+// grouped shrink's work table: segment i covers work blocks [blk_start[i],
 // blk_start[i+1]) of kShrinkRows rows each.  s_off: the keys' first output
 // positions (s_off[nb] = T), in LDS; every thread of the block calls it.
 __device__ void compact_segments(const int32_t *s_off, int32_t nb, int32_t T, int32_t *s_wave,
@@ -114,6 +118,46 @@ __device__ void compact_segments(const int32_t *s_off, int32_t nb, int32_t T, in
         seg_start[seg_carry] = T;
         blk_start[seg_carry] = blk_carry;
         *n_seg = seg_carry;
+    }
+}
+
+// The GEMM's row order: the rows of the base block and of the segments of at
+// least short_len rows, in sorted order, then the rows of the shorter
+// segments, in sorted order (a stable partition of perm).  gbase[k] is the
+// first GEMM position of key k's rows; skey lists the short segments' keys
+// in ascending order; header[kHdrNLong] is the number of rows before the
+// short ones and header[kHdrNShort] the number of short segments.  Every
+// thread of the block calls it.
+__device__ void gemm_order(const int32_t *s_off, int32_t nb, int32_t T, int32_t short_len, int32_t *s_wave,
+                           int32_t *__restrict__ gbase, int32_t *__restrict__ skey, int32_t *__restrict__ header) {
+    int32_t n_short = 0;
+    for (int32_t k0 = 0; k0 < nb; k0 += blockDim.x) {
+        const int32_t k = k0 + threadIdx.x;
+        const int32_t len = (k < nb) ? (s_off[k + 1] - s_off[k]) : 0;
+        int32_t tot;
+        block_exclusive_scan((k >= 1 && len > 0 && len < short_len) ? len : 0, s_wave, &tot);
+        n_short += tot;
+    }
+    const int32_t n_long = T - n_short;
+    int32_t long_carry = 0, short_carry = 0, seg_carry = 0;
+    for (int32_t k0 = 0; k0 < nb; k0 += blockDim.x) {
+        const int32_t k = k0 + threadIdx.x;
+        const int32_t len = (k < nb) ? (s_off[k + 1] - s_off[k]) : 0;
+        const bool is_short = k >= 1 && len > 0 && len < short_len;
+        int32_t lt, st, nt;
+        const int32_t lp = block_exclusive_scan(is_short ? 0 : len, s_wave, &lt) + long_carry;
+        const int32_t sp = block_exclusive_scan(is_short ? len : 0, s_wave, &st) + short_carry;
+        const int32_t si = block_exclusive_scan(is_short ? 1 : 0, s_wave, &nt) + seg_carry;
+        if (k < nb) gbase[k] = is_short ? n_long + sp : lp;
+        if (is_short) skey[si] = k;
+        long_carry += lt;
+        short_carry += st;
+        seg_carry += nt;
+    }
+    if (threadIdx.x == 0) {
+        header[kHdrNLong] = n_long;
+        header[kHdrShortLen] = short_len;
+        header[kHdrNShort] = seg_carry;
     }
 }
 
@@ -158,13 +202,16 @@ __device__ void sort_tile(const int32_t *__restrict__ ids, int32_t T, int32_t n_
 constexpr int kScanItems = 4;
 
 __global__ void __launch_bounds__(1024) k_seg_scan(int32_t *__restrict__ tile_hist, int32_t n_slots,
-                                                   int32_t n_tiles, int32_t T,
+                                                   int32_t n_tiles, int32_t T, int32_t short_len,
                                                    int32_t *__restrict__ offsets,
                                                    int32_t *__restrict__ seg_id,
                                                    int32_t *__restrict__ seg_start,
                                                    int32_t *__restrict__ n_seg,
                                                    int32_t *__restrict__ blk_start,
-                                                   int32_t *__restrict__ blk_seg) {
+                                                   int32_t *__restrict__ blk_seg,
+                                                   int32_t *__restrict__ gbase,
+                                                   int32_t *__restrict__ skey,
+                                                   int32_t *__restrict__ header) {
     extern __shared__ int32_t s_off[];        // [n_slots + 2]
     __shared__ int32_t s_wave[48];
     const int32_t nb = n_slots + 1;
@@ -196,27 +243,34 @@ __global__ void __launch_bounds__(1024) k_seg_scan(int32_t *__restrict__ tile_hi
     __syncthreads();
     for (int32_t k = threadIdx.x; k <= nb; k += blockDim.x) offsets[k] = s_off[k];
 
+    gemm_order(s_off, nb, T, short_len, s_wave, gbase, skey, header);
     compact_segments(s_off, nb, T, s_wave, seg_id, seg_start, n_seg, blk_start, blk_seg);
 }
 
 __global__ void __launch_bounds__(1024) k_seg_scatter(const int32_t *__restrict__ ids, int32_t T,
                                                       int32_t n_slots,
                                                       const int32_t *__restrict__ tile_hist,
-                                                      int32_t n_tiles, int32_t *__restrict__ perm) {
+                                                      int32_t n_tiles, int32_t *__restrict__ perm,
+                                                      const int32_t *__restrict__ offsets,
+                                                      const int32_t *__restrict__ gbase,
+                                                      int32_t *__restrict__ gperm) {
     __shared__ int32_t s_key[kSegTile], s_row[kSegTile];
     int32_t key, row, first;
     sort_tile(ids, T, n_slots, blockIdx.x * kSegTile, s_key, s_row, key, row, first);
     if (key == INT32_MAX) return;
-    perm[tile_hist[(size_t)key * n_tiles + blockIdx.x] + ((int)threadIdx.x - first)] = row;
+    const int32_t pos = tile_hist[(size_t)key * n_tiles + blockIdx.x] + ((int)threadIdx.x - first);
+    perm[pos] = row;
+    gperm[gbase[key] + (pos - offsets[key])] = row;      // same place within its key's block
 }
 
-lora_status_t launch_ws_init(void *ws, hipStream_t s) {
-    hipLaunchKernelGGL(k_ws_init, dim3(1), dim3(64), 0, s, ws_ptr<int32_t>(ws, 0));
+lora_status_t launch_ws_init(void *ws, hipStream_t s, bool err_only) {
+    hipLaunchKernelGGL(k_ws_init, dim3(1), dim3(64), 0, s, ws_ptr<int32_t>(ws, 0), err_only ? 0 : 1);
     return hip_status(hipGetLastError());
 }
 
 lora_status_t launch_segments(const int32_t *ids, int32_t T, int32_t n_slots, const ws_layout &L,
-                              void *ws, hipStream_t s) {
+                              void *ws, hipStream_t s, int32_t short_len) {
+    if (short_len < 1) short_len = 1;
     const int32_t n_tiles = (T + kSegTile - 1) / kSegTile;
     int32_t *err = ws_ptr<int32_t>(ws, L.header);
     int32_t *tile_hist = ws_ptr<int32_t>(ws, L.tile_hist);
@@ -224,12 +278,14 @@ lora_status_t launch_segments(const int32_t *ids, int32_t T, int32_t n_slots, co
     const size_t lds_off = sizeof(int32_t) * (size_t)(n_slots + 2);
     hipLaunchKernelGGL(k_seg_hist, dim3(n_tiles), dim3(256), lds_hist, s, ids, T, n_slots,
                        tile_hist, n_tiles, err);
-    hipLaunchKernelGGL(k_seg_scan, dim3(1), dim3(1024), lds_off, s, tile_hist, n_slots, n_tiles, T,
+    hipLaunchKernelGGL(k_seg_scan, dim3(1), dim3(1024), lds_off, s, tile_hist, n_slots, n_tiles, T, short_len,
                        ws_ptr<int32_t>(ws, L.offsets), ws_ptr<int32_t>(ws, L.seg_id),
                        ws_ptr<int32_t>(ws, L.seg_start), ws_ptr<int32_t>(ws, L.n_seg),
-                       ws_ptr<int32_t>(ws, L.blk_start), ws_ptr<int32_t>(ws, L.blk_seg));
+                       ws_ptr<int32_t>(ws, L.blk_start), ws_ptr<int32_t>(ws, L.blk_seg),
+                       ws_ptr<int32_t>(ws, L.gbase), ws_ptr<int32_t>(ws, L.skey), ws_ptr<int32_t>(ws, L.header));
     hipLaunchKernelGGL(k_seg_scatter, dim3(n_tiles), dim3(kSegTile), 0, s, ids, T, n_slots,
-                       tile_hist, n_tiles, ws_ptr<int32_t>(ws, L.perm));
+                       tile_hist, n_tiles, ws_ptr<int32_t>(ws, L.perm), ws_ptr<int32_t>(ws, L.offsets),
+                       ws_ptr<int32_t>(ws, L.gbase), ws_ptr<int32_t>(ws, L.gperm));
     return hip_status(hipGetLastError());
 }
 

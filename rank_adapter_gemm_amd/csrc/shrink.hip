@@ -78,21 +78,20 @@ __device__ __forceinline__ int owned_index(int lane) {
 // row's E4M3 codes and power-of-two scale, as k_quant_rows_fp8 does (amax
 // over the row, then the codes), after the shrink, with x from cache: one
 // launch and one HBM read of x for both.
-template <int DT, int RM, bool Q8 = false>
-__global__ void __launch_bounds__(512) k_shrink_rows(const typename elem<DT>::T *__restrict__ x,
-                                                     int32_t T, int32_t d_in, slice_set ss,
-                                                     int32_t n_slots, int32_t max_rank,
-                                                     const int32_t *__restrict__ ids,
-                                                     const int32_t *__restrict__ perm,
-                                                     float *__restrict__ v, int32_t *err,
-                                                     uint8_t *__restrict__ xq, float *__restrict__ xs) {
+// The shrink of the row at position p (through perm), by one 512-thread
+// workgroup (every thread calls it with the same p).
+template <int DT, int RM, bool Q8>
+__device__ __forceinline__ void shrink_row(const typename elem<DT>::T *__restrict__ x, int32_t T, int32_t d_in,
+                                           const slice_set &ss, int32_t n_slots, int32_t max_rank,
+                                           const int32_t *__restrict__ ids, const int32_t *__restrict__ perm,
+                                           float *__restrict__ v, int32_t *err, uint8_t *__restrict__ xq,
+                                           float *__restrict__ xs, int p) {
     static_assert(!Q8 || DT == LORA_BF16, "the FP8 base quantizes bf16 rows");
     typedef typename elem<DT>::T E;
     constexpr int VN = vec16<DT>::n;
     constexpr int NW = 8;                                 // wavefronts per workgroup
     constexpr int RC = RM < 16 ? RM : (RM > 32 ? 8 : 16); // rank rows per batch of loads
     __shared__ float s_red[NW][RM];
-    const int p = blockIdx.x;
     const int t = perm_row(perm, p, T);
     if (t < 0) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -200,6 +199,19 @@ __global__ void __launch_bounds__(512) k_shrink_rows(const typename elem<DT>::T 
         }
     }
 }
+
+// BGMV: one workgroup per row (position blockIdx.x through perm).
+template <int DT, int RM, bool Q8 = false>
+__global__ void __launch_bounds__(512) k_shrink_rows(const typename elem<DT>::T *__restrict__ x,
+                                                     int32_t T, int32_t d_in, slice_set ss,
+                                                     int32_t n_slots, int32_t max_rank,
+                                                     const int32_t *__restrict__ ids,
+                                                     const int32_t *__restrict__ perm,
+                                                     float *__restrict__ v, int32_t *err,
+                                                     uint8_t *__restrict__ xq, float *__restrict__ xs) {
+    shrink_row<DT, RM, Q8>(x, T, d_in, ss, n_slots, max_rank, ids, perm, v, err, xq, xs, blockIdx.x);
+}
+
 
 // ---------------------------------------------------------------------------
 // SGMV shrink, bf16: a grouped product over adapter segments.

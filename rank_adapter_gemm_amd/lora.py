@@ -32,6 +32,11 @@ LORA_MODE_SGMV = 2
 LORA_FLAG_SEGMENTS_READY = 0x1
 LORA_FLAG_SEPARATE_EXPAND = 0x2
 
+
+def LORA_FLAG_SHORT_SEGMENT(n: int) -> int:
+    """AUTO mode: segments of fewer than n rows take the per-row path."""
+    return (int(n) & 0xff) << 8
+
 # Every symbol include/lora.h declares.
 EXPORTED = (
     "lora_pool_bytes", "lora_pool_create", "lora_pool_bytes_packed", "lora_pool_create_packed",
@@ -64,7 +69,8 @@ class lora_pool_t(ctypes.Structure):
 
 class lora_segments_t(ctypes.Structure):
     _fields_ = [("offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p), ("seg_id", ctypes.c_void_p),
-                ("seg_start", ctypes.c_void_p), ("n_seg", ctypes.c_void_p)]
+                ("seg_start", ctypes.c_void_p), ("n_seg", ctypes.c_void_p), ("gemm_perm", ctypes.c_void_p),
+                ("n_fused", ctypes.c_void_p)]
 
 
 _lib = None
@@ -489,4 +495,4 @@ class Workspace:
 
         return {"offsets": view(seg.offsets, self.n_slots + 2), "perm": view(seg.perm, T),
                 "seg_id": view(seg.seg_id, self.n_slots), "seg_start": view(seg.seg_start, self.n_slots + 1),
-                "n_seg": view(seg.n_seg, 1)}
+                "n_seg": view(seg.n_seg, 1), "gemm_perm": view(seg.gemm_perm, T), "n_fused": view(seg.n_fused, 1)}

@@ -138,6 +138,11 @@ def test_validation_returns_before_launch(lib):
     assert f(fake, fake, fake, 16, ctypes.byref(ok), None, 0, 0, fake, ws_need, None) == L.LORA_ERR_INVALID_ARGUMENT
     assert f(fake, fake, fake, 16, ctypes.byref(ok), fake, 3, 0, fake, ws_need, None) == L.LORA_ERR_INVALID_ARGUMENT
     assert f(fake, fake, fake, 16, ctypes.byref(ok), fake, 0, 4, fake, ws_need, None) == L.LORA_ERR_INVALID_ARGUMENT
+    assert f(fake, fake, fake, 16, ctypes.byref(ok), fake, 0, 0x10000, fake, ws_need, None) == L.LORA_ERR_INVALID_ARGUMENT
+    # the short-segment threshold bits are accepted (T == 0: nothing enqueued)
+    assert f(None, None, None, 0, ctypes.byref(ok), None, 0, L.LORA_FLAG_SHORT_SEGMENT(200) | 3, fake, ws_need,
+             None) == L.LORA_OK
+    assert L.LORA_FLAG_SHORT_SEGMENT(16) == 0x1000
     # T == 0 is a no-op that returns OK without touching anything
     assert f(None, None, None, 0, ctypes.byref(ok), None, 0, 0, fake, ws_need, None) == L.LORA_OK
     assert lib.lora_shrink(None, 0, ctypes.byref(ok), None, 0, None, fake, ws_need, None) == L.LORA_OK
@@ -157,9 +162,10 @@ def test_segments_view_is_pointer_arithmetic(lib):
     need = L.lora_workspace_bytes(100, 10, 8)
     seg = L.lora_segments_t()
     assert lib.lora_segments_view(fake, need, 100, 10, 8, ctypes.byref(seg)) == L.LORA_OK
-    ptrs = [seg.offsets, seg.perm, seg.seg_id, seg.seg_start, seg.n_seg]
+    ptrs = [seg.offsets, seg.perm, seg.seg_id, seg.seg_start, seg.n_seg, seg.gemm_perm]
     assert all(fake <= p < fake + need for p in ptrs)
-    assert len(set(ptrs)) == 5 and all(p % 16 == 0 for p in ptrs)
+    assert len(set(ptrs)) == 6 and all(p % 16 == 0 for p in ptrs)
+    assert fake <= seg.n_fused < fake + 256 and seg.n_fused % 4 == 0
     # segment regions do not depend on max_rank (reuse across pools)
     seg2 = L.lora_segments_t()
     assert lib.lora_segments_view(fake, L.lora_workspace_bytes(100, 10, 64), 100, 10, 64,
