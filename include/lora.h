@@ -492,6 +492,31 @@ lora_status_t lora_linear_forward_fp8(const void *x, const uint8_t *wq, const fl
                                       lora_mode_t mode, uint32_t flags, void *ws, size_t ws_bytes,
                                       lora_stream_t stream);
 
+/* ---- the layer without a caller workspace ---------------------------------------- */
+
+/* For callers that cannot allocate device memory at call time: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * lora_linear_forward with its workspace in a library-owned device array of
+ * 64 MiB (LORA_NOALLOC_SCRATCH_BYTES) per GPU, held until the process ends
+ * and looked up at the first call on each device (that first call must not
+ * be under stream capture).  It calls no hipMalloc, hipFree or allocating
+ * library routine.  Arguments as for lora_linear_forward, on the current
+ * device's stream; err_out (DEVICE int32 [1], may be NULL) receives the
+ * smallest row index with a bad adapter id in this call, or -1.
+ * Limits: a batch whose workspace regions (segments, v, shrink partials:
+ * lora_workspace_bytes(T, n_slots, max_rank, 0)) exceed the array returns
+ * LORA_ERR_WORKSPACE_TOO_SMALL before enqueuing anything; the rest of the
+ * array holds GEMM split-K partials, so it can split K less far than a
+ * larger caller workspace would (results then differ in fp32 summation
+ * order only).  Every call on one GPU shares the array and it keeps the
+ * last call's contents: calls that overlap on one GPU (different streams
+ * without ordering) race and are not allowed; LORA_FLAG_SEGMENTS_READY
+ * refers to the segments left by the previous call on this GPU. */
+#define LORA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+lora_status_t lora_linear_forward_noalloc(const void *x, const void *W, void *y, int32_t T,
+                                          const lora_pool_t *pool, const int32_t *ids, lora_mode_t mode,
+                                          uint32_t flags, int32_t *err_out, lora_stream_t stream);
+
 /* ---- errors ------------------------------------------------------------------- */
 
 /* Synchronise `stream`, read the workspace's error word into *first_bad_row

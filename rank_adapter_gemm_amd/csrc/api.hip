@@ -3,6 +3,8 @@
 // entry point is stated in include/lora.h.
 #include <string.h>
 
+#include <mutex>
+
 #include "common.hpp"
 
 using namespace lora;
@@ -121,6 +123,40 @@ lora_status_t gemm_and_expand(const void *x, const void *W, void *y, int32_t T, 
                                    partial_bytes, s, p.dtype == LORA_BF16 ? n_fused : nullptr);
     if (st == LORA_OK && sgmv) st = launch_expand_short(v, v_stride, T, p, y, L, ws, s);
     return st;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace of lora_linear_forward_noalloc, for callers that cannot allocate:
+// a file-scope device array.  Every GPU the library runs on holds its own
+// copy until the process ends.  In host code the array's name is only a
+// stand-in: its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and kept in
+// g_scratch_ptr; kernels receive that address, never the name.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+static void *g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+lora_status_t scratch_of_current_device(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return LORA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return LORA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LORA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return LORA_OK;
+}
+
+// err_out[0] = the smallest bad row recorded in the workspace's error word,
+// or -1 if none.
+__global__ void k_error_out(const int32_t *header, int32_t *err_out) {
+    if (threadIdx.x == 0) err_out[0] = header[kHdrErr] == kErrNone ? -1 : header[kHdrErr];
 }
 
 }  // namespace
@@ -550,6 +586,30 @@ lora_status_t lora_linear_forward_fp8(const void *x, const uint8_t *wq, const fl
                          partial, partial_bytes, s, sgmv ? ws_ptr<int32_t>(ws, L.header) + kHdrNLong : nullptr);
     if (st == LORA_OK && sgmv) st = launch_expand_short(v, pool->max_rank, T, *pool, y, L, ws, s);
     return st;
+}
+
+lora_status_t lora_linear_forward_noalloc(const void *x, const void *W, void *y, int32_t T,
+                                          const lora_pool_t *pool, const int32_t *ids, lora_mode_t mode,
+                                          uint32_t flags, int32_t *err_out, lora_stream_t stream) {
+    if (!valid_pool(pool) || T < 0 || !valid_mode(mode) || (flags & ~kForwardFlags))
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (T > 0 && (!x || !W || !y || !ids || !aligned16(x) || !aligned16(W) || !aligned16(y)))
+        return LORA_ERR_INVALID_ARGUMENT;
+    if (T == 0) return LORA_OK;
+    // the batch's workspace regions (the rest of the scratch holds GEMM
+    // split-K partials, which only limits how far K is split)
+    const ws_layout L = make_ws_layout(T, pool->n_slots, pool->max_rank, 0);
+    if (L.total > kScratchBytes) return LORA_ERR_WORKSPACE_TOO_SMALL;
+    void *ws = nullptr;
+    lora_status_t st = scratch_of_current_device(&ws);
+    if (st != LORA_OK) return st;
+    const hipStream_t s = hs(stream);
+    st = launch_ws_init(ws, s, true);                     // the error word starts at "none"
+    if (st != LORA_OK) return st;
+    st = lora_linear_forward(x, W, y, T, pool, ids, mode, flags, ws, kScratchBytes, stream);
+    if (st != LORA_OK || !err_out) return st;
+    hipLaunchKernelGGL(k_error_out, dim3(1), dim3(64), 0, s, ws_ptr<int32_t>(ws, L.header), err_out);
+    return hip_status(hipGetLastError());
 }
 
 lora_status_t lora_get_device_error(void *ws, size_t ws_bytes, lora_stream_t stream,

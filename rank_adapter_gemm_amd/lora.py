@@ -48,9 +48,12 @@ EXPORTED = (
     "lora_cache_commit", "lora_cache_slot_of", "lora_cache_stats",
     "lora_quantize_rows_fp8", "lora_quantize_weight_fp8", "lora_gemm_fp8", "lora_workspace_bytes_fp8",
     "lora_linear_forward_fp8",
+    "lora_linear_forward_noalloc",
     "lora_get_device_error",
     "lora_status_string", "lora_version",
 )
+
+LORA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class LoraError(RuntimeError):
@@ -139,6 +142,8 @@ def load(path: str = LIB_PATH):
         "lora_workspace_bytes_fp8": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
         "lora_linear_forward_fp8": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32, P(lora_pool_t), c_vp, c_i32, c_u32,
                                             c_vp, c_sz, c_vp]),
+        "lora_linear_forward_noalloc": (c_i32, [c_vp, c_vp, c_vp, c_i32, P(lora_pool_t), c_vp, c_i32, c_u32, c_vp,
+                                                c_vp]),
         "lora_get_device_error": (c_i32, [c_vp, c_sz, c_vp, P(c_i32)]),
         "lora_status_string": (ctypes.c_char_p, [c_i32]),
         "lora_version": (ctypes.c_char_p, []),
@@ -287,6 +292,12 @@ def lora_linear_forward(x, W, y, T, pool, ids, mode, flags, ws, stream=None):
     _ok(load().lora_linear_forward(_ptr(x), _ptr(W), _ptr(y), T, ctypes.byref(pool), _ptr(ids), mode,
                                    flags, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
         "lora_linear_forward")
+
+
+def lora_linear_forward_noalloc(x, W, y, T, pool, ids, mode, flags, err_out=None, stream=None):
+    """lora_linear_forward with the library's own device scratch (no workspace argument)."""
+    _ok(load().lora_linear_forward_noalloc(_ptr(x), _ptr(W), _ptr(y), T, ctypes.byref(pool), _ptr(ids), mode, flags,
+                                           _ptr(err_out), _stream(stream)), "lora_linear_forward_noalloc")
 
 
 def lora_workspace_bytes_sliced(T, n_slots, max_rank, n_slices, d_out=0) -> int:
