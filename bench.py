@@ -45,7 +45,8 @@ RIDGE = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
 RIDGE_FP8 = MFMA_FP8_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
 MALL_BYTES = 256 * 2 ** 20
 CSRC = os.path.join(ROOT, "rank_adapter_gemm_amd", "csrc")
-KERNEL_SOURCE = {"gemm_expand": ["gemm.hip", "gemm_common.hpp"], "shrink": ["shrink.hip", "fp8_common.hpp"],
+KERNEL_SOURCE = {"gemm_expand": ["gemm.hip", "gemm_common.hpp", "expand.hip"], "gemm": ["gemm.hip", "gemm_common.hpp"],
+                 "shrink": ["shrink.hip", "fp8_common.hpp"],
                  "segments": ["segments.hip"], "expand": ["expand.hip"],
                  "forward": ["api.hip", "gemm.hip", "gemm_common.hpp", "shrink.hip", "fp8_common.hpp",
                              "segments.hip", "expand.hip"],
@@ -120,16 +121,19 @@ def trace_summary(path: str) -> None:
             for row in csv.DictReader(fh):
                 name = row.get("Kernel_Name", "?")
                 grid = row.get("Grid_Size_X") or row.get("Grid_Size") or "?"
+                if row.get("Grid_Size_Y") not in (None, "", "1"):
+                    grid = "%sx%s" % (grid, row["Grid_Size_Y"])
                 wg = row.get("Workgroup_Size_X") or row.get("Workgroup_Size") or "?"
                 dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
                 groups.setdefault((name, grid, wg), []).append(dur)
     for f in dbs:                      # rocpd output (the default format of rocprofv3)
         con = sqlite3.connect(f)
-        for name, grid, wg, start, end in con.execute(
-                "select name, grid_x, workgroup_x, start, end from kernels"):
-            groups.setdefault((name, str(grid), str(wg)), []).append((end - start) / 1e3)
+        for name, grid, gy, wg, start, end in con.execute(
+                "select name, grid_x, grid_y, workgroup_x, start, end from kernels"):
+            g = str(grid) if gy in (None, 1) else "%sx%s" % (grid, gy)
+            groups.setdefault((name, g, str(wg)), []).append((end - start) / 1e3)
         con.close()
-    print("| calls | avg us | min us | max us | total us | grid | wg | kernel |")
+    print("| calls | avg us | min us | max us | total us | grid (threads) | wg | kernel |")
     print("|---|---|---|---|---|---|---|---|")
     for (name, grid, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         short = name if len(name) <= 110 else name[:107] + "..."
@@ -175,29 +179,37 @@ def counter_summary(path: str) -> None:
 
 
 def record_traffic(fetch_dir: str, write_dir: str, key: str, kernel_sub: str, grid: str, source: str) -> None:
-    """HBM bytes per launch of one kernel (matched by a name substring and its
-    grid size) from a FETCH_SIZE run and a WRITE_SIZE run, each scaled by what
-    the same counter reads for the 1 GiB calibration copy of --calib-copy,
-    stored in profiles/traffic.json under `key` with the hash of the kernel's
-    source files (KERNEL_SOURCE[source])."""
+    """HBM bytes per launch of a launch group (kernels matched by name
+    substrings and grid sizes in threads, '+'-separated lists of equal
+    length; one launch of each per unit) from a FETCH_SIZE run and a
+    WRITE_SIZE run, each scaled by what the same counter reads for the 1 GiB
+    calibration copy of --calib-copy, stored in profiles/traffic.json under
+    `key` with the hash of the kernels' source files (KERNEL_SOURCE[source])."""
     import statistics
 
+    subs, grids = kernel_sub.split("+"), grid.split("+")
+    if len(subs) != len(grids):
+        print("--record-traffic: as many grids as kernel substrings", file=sys.stderr)
+        sys.exit(2)
+
     def mean_of(path, ctr):
-        vals, calib = [], []
+        vals = [[] for _ in subs]
+        calib = []
         for name, g, c, val, dur in _counter_rows(path):
             if c != ctr:
                 continue
-            if kernel_sub in name and g == grid:
-                vals.append(val)
-            elif "AUnaryFunctor" in name and g == "67108864":
+            if "AUnaryFunctor" in name and g == "67108864":
                 calib.append(val)
-        if not vals or not calib:
-            print("%s: no matching dispatches (kernel %d, calibration %d)" % (path, len(vals), len(calib)),
-                  file=sys.stderr)
+            for i, (sub, gr) in enumerate(zip(subs, grids)):
+                if sub in name and g == gr:
+                    vals[i].append(val)
+        if not all(vals) or not calib:
+            print("%s: no matching dispatches (kernels %s, calibration %d)" % (
+                path, [len(v) for v in vals], len(calib)), file=sys.stderr)
             sys.exit(1)
         # the calibration copy moves 1 GiB each way; the counter reads KiB
         factor = (1 << 30) / (statistics.fmean(calib) * 1024)
-        return statistics.fmean(vals) * 1024 * factor, factor
+        return sum(statistics.fmean(v) for v in vals) * 1024 * factor, factor
 
     fetch, ff = mean_of(fetch_dir, "FETCH_SIZE")
     write, wf = mean_of(write_dir, "WRITE_SIZE")
@@ -411,7 +423,7 @@ def main():
     if "gemm" not in names and not fp8:
         names.append("gemm")
     if args.no_breakdown:             # only what the roofline needs
-        names = ["gemm_fp8"] if fp8 else ["gemm_expand"]
+        names = ["gemm_fp8"] if fp8 else (["gemm"] if args.separate_expand else ["gemm_expand"])
     smode = L.LORA_MODE_SGMV if sgmv else L.LORA_MODE_BGMV
 
     def call(name, k, i):
@@ -580,15 +592,18 @@ def main():
     roof["algorithmic_flops_per_launch"] = int(fl_d)
     roof["traffic"] = stored_traffic("forward_fp8" if fp8 else "forward", args.workload, roof["projection"])
     forward_call = dict(roof)
+    gname = "gemm" if args.separate_expand else "gemm_expand"
     if roof["bound"] == "mfma" and not fp8:
-        cand = [(per_launch[("gemm_expand", k)], k) for k in groups[kd] if ("gemm_expand", k) in per_launch]
+        cand = [(per_launch[(gname, k)], k) for k in groups[kd] if (gname, k) in per_launch]
         t_k, kk = max(cand)
         pk = wl.projections[kk]
-        b_k, f_k = work("gemm_expand", pk)
+        b_k, f_k = work(gname, pk)
         roof = dict(bound="mfma", achieved=round(f_k / (t_k * 1e-3) / 1e12, 2), peak=MFMA_BF16_PEAK_TFS,
                     unit="TFLOP/s")
         roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-        roof["kernel"] = ("k_gemm_bf16 (base GEMM + fused expand of the long segments) + k_expand_short "
+        roof["kernel"] = ("k_gemm_bf16 (base GEMM, no adapters: the expand is a separate pass)"
+                          if args.separate_expand else
+                          "k_gemm_bf16 (base GEMM + fused expand of the long segments) + k_expand_short "
                           "(per-row expand of the short segments), one lora_gemm_expand call" if sgmv else
                           "k_gemm_bf16 (base GEMM + fused expand)")
         roof["projection"] = pk.name
@@ -597,7 +612,7 @@ def main():
         roof["avg_launch_us"] = round(t_k * 1e3, 3)
         roof["algorithmic_bytes_per_launch"] = int(b_k)
         roof["algorithmic_flops_per_launch"] = int(f_k)
-        roof["traffic"] = stored_traffic("gemm_expand", args.workload, pk.name)
+        roof["traffic"] = stored_traffic(gname, args.workload, pk.name)
     # LoRA overhead: the step's forward calls against the base products alone
     base_ms = sum(per_launch[(n_, k)] for (n_, k) in per_launch if n_ in ("gemm", "gemm_fp8", "quantize"))
     overhead = dict(forward_us=round(1e3 * sum(fwd.values()), 3), base_only_us=round(1e3 * base_ms, 3) if base_ms else None,
@@ -721,7 +736,15 @@ def stored_traffic(kernel: str, workload: str, projection: str | None = None):
         data = json.load(open(path))
     except ValueError:
         return None
-    ent = data.get("%s/%s" % (workload, kernel) + ("/" + projection if projection else ""))
+    key = "%s/%s" % (workload, kernel)
+    ent = data.get(key + ("/" + projection if projection else ""))
+    if ent is None and projection:
+        # a record may cover several projections of one launch shape
+        # ("gate,up": the counter means were taken over both launches)
+        for k, v in data.items():
+            if k.startswith(key + "/") and projection in k[len(key) + 1:].split(","):
+                ent = v
+                break
     if not ent or ent.get("source_sha") != source_sha(kernel):
         return None
     return ent.get("hbm_bytes_per_launch")

@@ -218,9 +218,9 @@ lora_status_t lora_pool_clear(const lora_pool_t *pool, int32_t slot, lora_stream
  * tiles of small batches, and for the last, mostly idle round of tiles of
  * larger ones; without it every tile runs whole.  The two differ in fp32
  * summation order and in how the low-rank term is added: a whole tile feeds
- * s_a * v to the matrix cores as two bf16 parts (about 16 significant
- * bits), a split tile's reduction sums it in fp32.  Returns 0 on bad
- * arguments. */
+ * s_a * v to the matrix cores as three bf16 parts (its full fp32 value) and
+ * sums in the accumulator's order, a split tile's reduction sums it on the
+ * vector units.  Returns 0 on bad arguments. */
 size_t lora_workspace_bytes(int32_t T, int32_t n_slots, int32_t max_rank, int32_t d_out);
 
 /* Prepare a freshly allocated DEVICE workspace: clears the error word and

@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
     // A stage's shrink operands are read from LDS at the stage hand-off and
     // multiplied after the stage's first MFMA group, so the FMAs never wait
     // on LDS in front of the matrix cores.
-    constexpr int SHC = ACH / WV;                        // chunks of 8 k per thread and stage
+    constexpr int SHC = ACH / WV > 0 ? ACH / WV : 1;     // chunks of 8 k per thread and stage
     uint4 sh_xq[SHC], sh_aq[SHC];
     auto shrink_load = [&](int buf) {
         if (!SH || sh_t >= T) return;
@@ -261,13 +261,17 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
             for (int e = 0; e < 8; ++e) sh_acc = fmaf(xf[e], af[e], sh_acc);
         }
     };
-    static_assert(5 * PER <= 63, "vmcnt counts at most 63 loads");
+    static_assert((NS - 1) * PER <= 63, "vmcnt counts at most 63 loads");
+    // vmcnt immediates of the stage counts a ring of NS stages can reach
+    // (counts past 63 only for depths this ring never has)
+    constexpr int V1 = PER, V2 = 2 * PER > 63 ? 63 : 2 * PER, V3 = 3 * PER > 63 ? 63 : 3 * PER;
+    constexpr int V4 = 4 * PER > 63 ? 63 : 4 * PER, V5 = 5 * PER > 63 ? 63 : 5 * PER;
     auto wait_stage = [&](int ahead) {                    // later stages still in flight
-        if (ahead >= 5) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 * PER) : "memory");
-        else if (ahead == 4) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * PER) : "memory");
-        else if (ahead == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PER) : "memory");
-        else if (ahead == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory");
-        else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory");
+        if (ahead >= 5) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(V5) : "memory");
+        else if (ahead == 4) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(V4) : "memory");
+        else if (ahead == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(V3) : "memory");
+        else if (ahead == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(V2) : "memory");
+        else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(V1) : "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
 #pragma unroll

@@ -147,9 +147,9 @@ template <int NREAD, int NMFMA> __device__ __forceinline__ void sched_interleave
 
 // The expand on MFMA: acc[rb][cb] += (s_a v[t]) B_a for the rows of each
 // distinct adapter a among a wavefront's 32-row block (found with ballots;
-// other rows get zero operands).  v is split into bf16 high and low parts so
-// the fp32 intermediate keeps about 16 mantissa bits; B octets (8 ranks of
-// one column, 16 bytes) are exactly the MFMA B operand of one lane.
+// other rows get zero operands).  s v is split into three bf16 parts, which
+// carry its full fp32 value; B octets (8 ranks of one column, 16 bytes) are
+// exactly the MFMA B operand of one lane.
 // Operand mapping of v_mfma_f32_32x32x16_bf16 per lane l: A = row (l % 32),
 // ranks 16 ks + 8 (l / 32) + 0..7; B = column (l % 32), the same ranks.
 
@@ -196,20 +196,28 @@ __device__ __forceinline__ void lora_step_mfma(f32x16_t (&acc)[CB], float sa, bo
                                                const float4 &v1, const uint4 (&bq)[CB]) {
     const uint32_t m = use ? ~0u : 0u;
     const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    uint32_t hi[4], lo[4];
+    // s v as three bf16 parts: hi = bf16(f), mid = bf16(f - hi), lo =
+    // bf16(f - hi - mid), each difference exact in fp32, so hi + mid + lo is
+    // f to within 2^-27 |f| (below fp32's own rounding): v enters the expand
+    // at fp32 precision, and the products with B's bf16 values are exact.
+    uint32_t hi[4], md[4], lo[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const float f0 = __uint_as_float(__float_as_uint(sa * vv[2 * e]) & m);
         const float f1 = __uint_as_float(__float_as_uint(sa * vv[2 * e + 1]) & m);
         hi[e] = pack_bf16x2(f0, f1);
-        lo[e] = pack_bf16x2(f0 - bf16_lo(hi[e]), f1 - bf16_hi(hi[e]));
+        const float r0 = f0 - bf16_lo(hi[e]), r1 = f1 - bf16_hi(hi[e]);
+        md[e] = pack_bf16x2(r0, r1);
+        lo[e] = pack_bf16x2(r0 - bf16_lo(md[e]), r1 - bf16_hi(md[e]));
     }
     const bf16x8_t ahi = __builtin_bit_cast(bf16x8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+    const bf16x8_t amd = __builtin_bit_cast(bf16x8_t, make_uint4(md[0], md[1], md[2], md[3]));
     const bf16x8_t alo = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         const bf16x8_t bb = __builtin_bit_cast(bf16x8_t, bq[cb]);
         acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bb, acc[cb], 0, 0, 0);
+        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(amd, bb, acc[cb], 0, 0, 0);
         acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bb, acc[cb], 0, 0, 0);
     }
 }

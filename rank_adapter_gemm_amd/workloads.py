@@ -19,6 +19,10 @@ Five workloads, named by what they are:
   stress_70b       512 decode + 2 prefill chunks of 2048 = 4608 rows, 514 requests
                    shuffled, ids uniform over 256 slots, ranks from {8,16,32,64}
                    padded to 64, alpha = 2r, 5 projections of a 70B model
+  decode_70b       the decode rows alone: 512 single-token requests on the 70B
+                   q projection with the same adapter mix (measures the
+                   per-row shrink's true-rank reads; not one of the five
+                   parity configurations)
 
 The adapter orientation is the pages' row-vector form: A [d_in, r], B [r, d_out].
 """
@@ -29,7 +33,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-WORKLOADS = ("tiny_fp32", "decode_bgmv", "prefill_sgmv", "layer_8b", "stress_70b")
+WORKLOADS = ("tiny_fp32", "decode_bgmv", "prefill_sgmv", "layer_8b", "stress_70b", "decode_70b")
 
 
 @dataclass
@@ -103,6 +107,9 @@ def _spec(name: str):
                     projs=[("q", 8192, 8192, "attn_in"), ("o", 8192, 8192, "attn_out"),
                            ("gate", 8192, 28672, "mlp_in"), ("up", 8192, 28672, "mlp_in"),
                            ("down", 28672, 8192, "mlp_mid")])
+    if name == "decode_70b":
+        return dict(seed=6, dtype=torch.bfloat16, n_slots=256, max_rank=64,
+                    projs=[("q", 8192, 8192, "attn_in")])
     raise ValueError("unknown workload %r (one of %s)" % (name, ", ".join(WORKLOADS)))
 
 
@@ -130,6 +137,9 @@ def _rows(name: str, rng: np.random.Generator, n_slots: int):
         perm = rng.permutation(len(lengths))
         lengths = [lengths[i] for i in perm]
         owners = [owners[i] for i in perm]
+    elif name == "decode_70b":
+        lengths = [1] * 512
+        owners = rng.integers(0, n_slots, size=len(lengths)).tolist()
     elif name == "stress_70b":
         lengths = [1] * 512 + [2048] * 2
         owners = rng.integers(0, n_slots, size=len(lengths)).tolist()
@@ -154,7 +164,7 @@ def make_workload(name: str, device: str | torch.device = "cpu", seed: int | Non
     lengths, owners, ids = _rows(name, rng, n_slots)
     T = int(ids.shape[0])
 
-    if name == "stress_70b":
+    if name in ("stress_70b", "decode_70b"):
         ranks = rng.choice(np.array([8, 16, 32, 64], dtype=np.int32), size=n_slots).astype(np.int32)
         alphas = 2.0 * ranks.astype(np.float64)
     else:

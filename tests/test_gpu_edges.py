@@ -276,3 +276,33 @@ def test_padding_to_max_rank_does_not_change_results(T):
     base = outs[(16, L.LORA_MODE_BGMV)]
     for key, y in outs.items():
         assert torch.max((y - base).abs() / (1 + base.abs())).item() <= 2 ** -7, key
+
+
+def test_fused_expand_carries_v_at_fp32():
+    """The fused expand feeds s v to the matrix cores at its full fp32 value.
+    Exact inputs: x = (1, 1, 1, 0, ...), A's three rank columns give
+    v = (1 + 2^-9 + 2^-20, -1, -2^-9) exactly in fp32, B = 1 on those ranks,
+    s = 1 and W = 0, so y = 2^-20 exactly (a bf16 value).  A bf16 high/low
+    split of v (16 bits) would lose the 2^-20 and give 0.  Whole tiles
+    (2048 x 4096 is 256 tiles of 256 x 128, no K split) and the separate
+    expand both give 2^-20 on every element."""
+    T, d_in, d_out = 2048, 64, 4096
+    x = torch.zeros(T, d_in, dtype=torch.bfloat16, device="cuda")
+    x[:, :3] = 1.0
+    W = torch.zeros(d_in, d_out, dtype=torch.bfloat16, device="cuda")
+    A = torch.zeros(d_in, 3, dtype=torch.float32)
+    A[0, 0], A[1, 0], A[2, 0] = 1.0, 2.0 ** -9, 2.0 ** -20
+    A[0, 1] = -1.0
+    A[1, 2] = -(2.0 ** -9)
+    A = A.to(torch.bfloat16).cuda()
+    B = torch.ones(3, d_out, dtype=torch.bfloat16, device="cuda")
+    pool = L.AdapterPool(1, d_in, d_out, 8, torch.bfloat16)
+    pool.upload(0, A, B, 3, 3.0)                         # s = alpha / r = 1
+    ids = torch.zeros(T, dtype=torch.int32, device="cuda")
+    for mode in (L.LORA_MODE_AUTO, L.LORA_MODE_SGMV, L.LORA_MODE_BGMV):
+        for flags in FLAGS:
+            ws = L.Workspace(T, 1, 8, d_out)
+            y = torch.empty(T, d_out, dtype=torch.bfloat16, device="cuda")
+            L.lora_linear_forward(x, W, y, T, pool.pool, ids, mode, flags, ws.buf)
+            torch.cuda.synchronize()
+            assert (y.float() == 2.0 ** -20).all(), "mode %d flags %d" % (mode, flags)

@@ -4,9 +4,9 @@ multiple LoRAs: segmented matrix multiplies and adapter scheduling", section
 for prefill segments, both in one forward).
 
 In AUTO mode a batch of at least 1024 rows is split by segment length:
-segments of at least L rows take the grouped shrink and the expand fused into
-the GEMM; shorter ones (decode rows) take the per-row shrink and a per-row
-expand after the GEMM, and are visited last by the GEMM.  The GEMM's row
+every segment takes the grouped shrink; segments of at least L rows take the
+expand fused into the GEMM, shorter ones (decode rows) a per-row expand after
+the GEMM, which visits their rows last.  The GEMM's row
 order is checked bit for bit against the order derived from the oracle's
 segment metadata; the outputs against the fp64 oracle for several L, every
 expand path, packed pools, sliced calls and the FP8 base."""
