@@ -327,6 +327,9 @@ def main():
                      n_slices=max(len(g) for g in groups),
                      fp8_d_in=max(p.d_in for p in wl.projections) if fp8 else 0)
     v = torch.empty(T, R, dtype=torch.float32, device=dev)
+    # lora_gemm takes its split-K scratch from the start of the buffer it is
+    # given; a buffer of its own keeps the segments in ws intact
+    gemm_ws = torch.empty(128 << 20, dtype=torch.uint8, device=dev)
     if fp8:
         xq8 = torch.empty(T, max(p.d_in for p in wl.projections), dtype=torch.uint8, device=dev)
         xs8 = torch.empty(T, dtype=torch.float32, device=dev)
@@ -435,7 +438,7 @@ def main():
         elif name == "shrink":
             L.lora_shrink(x, T, pool, ids, smode, v, ws.buf)
         elif name == "gemm":
-            L.lora_gemm(x, W, y, T, pr.d_in, pr.d_out, L.dtype_code(wl.dtype), ws=ws.buf)
+            L.lora_gemm(x, W, y, T, pr.d_in, pr.d_out, L.dtype_code(wl.dtype), ws=gemm_ws)
         elif name == "expand":
             L.lora_expand(v, T, pool, ids, smode, y, ws.buf)
         elif name == "quantize":

@@ -280,8 +280,11 @@ lora_status_t lora_expand(const float *v, int32_t T, const lora_pool_t *pool, co
  * that mixes adapters": the base output of all rows first).
  * y = x W (no adapters): x DEVICE [T, d_in], W DEVICE [d_in, d_out],
  * y DEVICE [T, d_out], all of `dtype`; fp32 accumulation, one rounding.
- * ws (DEVICE, may be NULL) is scratch for a K split of small batches, used
- * only if ws_bytes holds the fp32 partials. */
+ * ws (DEVICE, may be NULL) is scratch for a K split, used from its first byte
+ * and only if ws_bytes holds the fp32 partials: a forward workspace passed
+ * here loses its segments (build them again before an SGMV call on it).
+ * Kernels that read segment tables check every index they take from them,
+ * so tables overwritten this way give wrong rows, not invalid accesses. */
 lora_status_t lora_gemm(const void *x, const void *W, void *y, int32_t T, int32_t d_in,
                         int32_t d_out, lora_dtype_t dtype, void *ws, size_t ws_bytes,
                         lora_stream_t stream);

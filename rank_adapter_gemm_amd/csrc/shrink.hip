@@ -254,7 +254,7 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
     const int32_t *__restrict__ seg_id,
     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ n_seg_p,
     const int32_t *__restrict__ blk_start, const int32_t *__restrict__ blk_seg,
-    int32_t n_work_upper, int32_t k_chunk,
+    int32_t n_work_upper, int32_t n_slots, int32_t k_chunk,
     float *__restrict__ v, float *__restrict__ partial, int32_t *err) {
     typedef shrink_cfg<RCH, NS_> C;
     constexpr int BR = C::BR, NR = C::NR, BK = C::BK, CH = C::CH, XST = C::XST, STAGE = C::STAGE;
@@ -268,7 +268,7 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
         // base-only block: sorted positions [0, offsets[1]) get v = 0
         if (blockIdx.y != 0) return;
         const int p0 = (wid - n_work_upper) * BR;
-        const int pend = min(offsets[1], p0 + BR);
+        const int pend = min(min(offsets[1], p0 + BR), T);
         for (int e = tid; e < BR * VS; e += 256) {
             const int p = p0 + e / VS, j = e % VS;
             if (p < pend) {
@@ -278,12 +278,21 @@ __global__ void __launch_bounds__(256) k_shrink_grouped(
         }
         return;
     }
-    const int nseg = *n_seg_p;
+    // Every index taken from the segment tables is checked against the
+    // tables' sizes (n_slots + 2 entries; wid is below the block table's
+    // size) and T: overwritten tables give wrong rows, never an access
+    // outside the buffers.
+    const int nseg = min(*n_seg_p, n_slots);
     if (nseg <= 0 || wid >= blk_start[nseg]) return;
     const int lo = blk_seg[wid];                         // this block's segment
+    if (lo < 0 || lo >= nseg) return;
     const int32_t aid = seg_id[lo];
-    const int p0 = seg_start[lo] + (wid - blk_start[lo]) * BR;
-    const int pend = min(seg_start[lo + 1], p0 + BR);
+    if (aid < 0 || aid >= n_slots) return;
+    const int64_t s0 = seg_start[lo], s1 = seg_start[lo + 1];
+    const int64_t q0 = s0 + ((int64_t)wid - blk_start[lo]) * BR;
+    if (s0 < 0 || s1 > T || q0 < s0 || q0 >= s1) return;
+    const int p0 = (int)q0;
+    const int pend = (int)(s1 < q0 + BR ? s1 : q0 + BR);
     bool any_rank = false, any_empty = false;
     for (int sl = 0; sl < ss.n; ++sl) {
         const int32_t rs = ss.rank[sl][aid];
@@ -419,7 +428,8 @@ __global__ void __launch_bounds__(256) k_shrink_reduce(const float *__restrict__
                                                        const int32_t *__restrict__ offsets,
                                                        float *__restrict__ v) {
     const size_t n = (size_t)T * max_rank;
-    const size_t e0 = (size_t)offsets[1] * max_rank;
+    const int32_t o1 = offsets[1];                        // first adapter row (sorted order)
+    const size_t e0 = (size_t)(o1 < 0 ? 0 : (o1 > T ? T : o1)) * max_rank;
     for (size_t e = e0 + blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n;
          e += (size_t)gridDim.x * blockDim.x) {
         const int p = (int)(e / max_rank), j = (int)(e % max_rank);
@@ -514,7 +524,7 @@ lora_status_t launch_shrink(const void *x, int32_t T, const lora_pool_t *pools, 
                        p.max_rank, perm, offsets, ws_ptr<int32_t>(ws, L.seg_id),                  \
                        ws_ptr<int32_t>(ws, L.seg_start), ws_ptr<int32_t>(ws, L.n_seg),            \
                        ws_ptr<int32_t>(ws, L.blk_start), ws_ptr<int32_t>(ws, L.blk_seg),          \
-                       n_work_upper, k_chunk, v, partial, err)
+                       n_work_upper, p.n_slots, k_chunk, v, partial, err)
     switch (rc) {
         case 1: if (deep) LORA_SHRINK_GROUPED(1, 3); else LORA_SHRINK_GROUPED(1, 2); break;
         case 2: if (deep) LORA_SHRINK_GROUPED(2, 3); else LORA_SHRINK_GROUPED(2, 2); break;

@@ -147,3 +147,49 @@ def test_mixed_batch_fp8_thresholds_agree():
         assert L.lora_get_device_error(ws.buf) == -1
         outs.append(y.float())
     assert torch.max((outs[1] - outs[0]).abs() / (1 + outs[0].abs())).item() <= 2 ** -6
+
+
+def test_overwritten_segment_tables_stay_in_bounds():
+    """lora_gemm takes its split-K scratch from the first byte of the buffer it
+    is given, so a forward workspace passed to it loses its segment tables.
+    SGMV calls on such tables (here: overwritten by the plain GEMM's fp32
+    partials, then by seeded random words over the whole workspace) give
+    wrong rows but read and write only inside their buffers; building the
+    segments again (after preparing the randomised workspace again) restores
+    parity."""
+    ranks = [8, 16, 32, 64, 8, 24, 40, 64]
+    b = Batch(300, [700, 500, 300], 512, 1024, ranks, 64, seed=21)
+    assert b.T >= 1024
+    sl = b.slices[0]
+    pool = sl["padded"].pool
+    ws = L.Workspace(b.T, b.n_slots, 64, 1024)
+    y = torch.zeros(b.T, 1024, dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros(b.T, 64, dtype=torch.float32, device="cuda")
+    sgmv, ready = L.LORA_MODE_SGMV, L.LORA_FLAG_SEGMENTS_READY
+
+    def calls():
+        L.lora_shrink(b.x, b.T, pool, b.ids_dev, sgmv, v, ws.buf)
+        L.lora_gemm_expand(b.x, sl["W"], y, b.T, pool, b.ids_dev, v, sgmv, ws.buf)
+        L.lora_expand(v, b.T, pool, b.ids_dev, sgmv, y, ws.buf)
+        L.lora_linear_forward(b.x, sl["W"], y, b.T, pool, b.ids_dev, L.LORA_MODE_AUTO, ready, ws.buf)
+        L.lora_linear_forward(b.x, sl["W"], y, b.T, pool, b.ids_dev, sgmv, ready | L.LORA_FLAG_SEPARATE_EXPAND,
+                              ws.buf)
+        torch.cuda.synchronize()
+
+    L.lora_build_segments(b.ids_dev, b.T, b.n_slots, 64, ws.buf)
+    L.lora_gemm(b.x, sl["W"], y, b.T, 512, 1024, L.LORA_BF16, ws=ws.buf)
+    calls()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(21)
+    words = ws.buf.numel() // 4
+    ws.buf[:4 * words].view(torch.int32).copy_(
+        torch.randint(-2 ** 31, 2 ** 31 - 1, (words,), generator=g, device="cuda", dtype=torch.int64).to(torch.int32))
+    calls()
+    # the random words also replaced the error word and counters: a workspace
+    # overwritten as a whole is prepared again, as after allocation
+    L.lora_workspace_init(ws.buf)
+    y.zero_()
+    L.lora_linear_forward(b.x, sl["W"], y, b.T, pool, b.ids_dev, sgmv, 0, ws.buf)
+    torch.cuda.synchronize()
+    assert L.lora_get_device_error(ws.buf) == -1
+    assert_parity(y, b.oracle(), torch.bfloat16, "after rebuilding the segments")
