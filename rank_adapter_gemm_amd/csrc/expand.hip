@@ -99,16 +99,18 @@ __global__ void __launch_bounds__(256) k_expand_rows(const float *__restrict__ v
 // one 256-thread workgroup (every thread calls it with the same arguments).
 // Each thread loads all rank octets of B for its two adjacent columns into
 // registers once (ranks up to 64; larger ranks stream eight octets at a
-// time), before anything that waits on the rows, and applies them to the
-// rows one at a time; one load instruction of a wave reads the octets of 128
-// consecutive columns.  Rows are staged kXRows at a time: their indices and
-// v in LDS, their y values prefetched.  Ranks are summed in octet order
-// before scaling, as the per-row expand does; y is updated in fp32 and
-// written back with one rounding.  The kernel is memory-latency bound: one
-// item's chain is its record, the row indices, then v and y.  Measured on the
-// 70B-shaped batch's short segments: 13% (d_out 28672) and 40% (d_out 8192)
-// faster than 2048-column items that streamed B one octet ahead.
-constexpr int kXRows = 4;                      // rows staged per pass
+// time), before anything that waits on the rows; one load instruction of a
+// wave reads the octets of 128 consecutive columns.  Up to kXStage rows are
+// staged at once (indices and v in LDS), then computed kXGroup rows at a
+// time with the next group's y values already loading.  Ranks are summed in
+// octet order before scaling, as the per-row expand does; y is updated in
+// fp32 and written back with one rounding.  Measured on the 70B-shaped
+// batch's short segments: 13% (d_out 28672) and 40% (d_out 8192) faster
+// than 2048-column items that streamed B one octet ahead; staging 16 rows
+// at once instead of 4 took the prefill's separate expand from 1243 to
+// 1071 us.
+constexpr int kXStage = 16;                    // rows whose indices and v are staged at once
+constexpr int kXGroup = 8;                     // rows per compute group (y prefetched one group ahead)
 constexpr int kCpt = 2;                        // adjacent columns per thread
 constexpr int kXCols = 256 * kCpt;             // columns per work item
 
@@ -133,10 +135,17 @@ __device__ __forceinline__ void expand_adapter_rows(int a, int p0, int len, cons
 #pragma unroll
         for (int c = 0; c < kCpt; ++c)
             bq[g][c] = (g < G && col_ok) ? ldg16(bs + (int64_t)g * d_out * 8 + c * 8) : zero;
-    for (int q0 = 0; q0 < len; q0 += kXRows) {
-        const int nq = min(kXRows, len - q0);
+    auto yload = [&](int qb, int nq, uint32_t (&yv)[kXGroup]) {
+#pragma unroll
+        for (int q = 0; q < kXGroup; ++q) {
+            const int32_t t = qb + q < nq ? s_t[qb + q] : -1;
+            yv[q] = (t >= 0 && col_ok) ? *reinterpret_cast<const uint32_t *>(y + (size_t)t * d_out + n) : 0u;
+        }
+    };
+    for (int q0 = 0; q0 < len; q0 += kXStage) {
+        const int nq = min(kXStage, len - q0);
         __syncthreads();                                  // s_v, s_t are free
-        if (threadIdx.x < kXRows)
+        if (threadIdx.x < kXStage)
             s_t[threadIdx.x] = (int)threadIdx.x < nq ? perm_row(perm, p0 + q0 + threadIdx.x, T) : -1;
         __syncthreads();
         for (int e = threadIdx.x; e < nq * max_rank; e += 256) {
@@ -144,52 +153,53 @@ __device__ __forceinline__ void expand_adapter_rows(int a, int p0, int len, cons
             const int32_t t = s_t[qq];
             s_v[qq][j] = t >= 0 ? v[(size_t)t * v_stride + j] : 0.0f;
         }
-        uint32_t yv[kXRows];
-#pragma unroll
-        for (int qq = 0; qq < kXRows; ++qq) {
-            const int32_t t = s_t[qq];
-            yv[qq] = (t >= 0 && col_ok) ? *reinterpret_cast<const uint32_t *>(y + (size_t)t * d_out + n) : 0u;
-        }
+        uint32_t ya[kXGroup], yb[kXGroup];
+        yload(0, nq, ya);
         __syncthreads();
-        for (int qq = 0; qq < nq; ++qq) {
-            float acc[kCpt];
+        for (int qb = 0; qb < nq; qb += kXGroup) {
+            if (qb + kXGroup < nq) yload(qb + kXGroup, nq, yb);   // next group's y, under this group's FMAs
 #pragma unroll
-            for (int c = 0; c < kCpt; ++c) acc[c] = 0.0f;
-            for (int g0 = 0; g0 < G; g0 += 8) {
-                if (g0 > 0 || (G > 8 && (q0 > 0 || qq > 0))) {
+            for (int q = 0; q < kXGroup; ++q) {
+                if (qb + q >= nq) break;
+                float acc[kCpt];
 #pragma unroll
-                    for (int g = 0; g < 8; ++g)
+                for (int c = 0; c < kCpt; ++c) acc[c] = 0.0f;
+                // ranks up to 64 stay in bq; larger ranks stream eight octets at a time
+                for (int g0 = 0; g0 < G; g0 += 8) {
+                    if (G > 8) {
 #pragma unroll
-                        for (int c = 0; c < kCpt; ++c)
-                            bq[g][c] = (g0 + g < G && col_ok) ? ldg16(bs + (int64_t)(g0 + g) * d_out * 8 + c * 8)
-                                                              : zero;
-                }
+                        for (int g = 0; g < 8; ++g)
 #pragma unroll
-                for (int g = 0; g < 8; ++g) {
-                    if (g0 + g >= G) break;
-                    const float4 v0 = *reinterpret_cast<const float4 *>(&s_v[qq][8 * (g0 + g)]);
-                    const float4 v1 = *reinterpret_cast<const float4 *>(&s_v[qq][8 * (g0 + g) + 4]);
+                            for (int c = 0; c < kCpt; ++c)
+                                bq[g][c] = (g0 + g < G && col_ok)
+                                               ? ldg16(bs + (int64_t)(g0 + g) * d_out * 8 + c * 8) : zero;
+                    }
 #pragma unroll
-                    for (int c = 0; c < kCpt; ++c) {
-                        float bf[8];
-                        vec16<LORA_BF16>::widen(bq[g][c], bf);
-                        float s_ = acc[c];
-                        s_ = fmaf(v0.x, bf[0], s_); s_ = fmaf(v0.y, bf[1], s_);
-                        s_ = fmaf(v0.z, bf[2], s_); s_ = fmaf(v0.w, bf[3], s_);
-                        s_ = fmaf(v1.x, bf[4], s_); s_ = fmaf(v1.y, bf[5], s_);
-                        s_ = fmaf(v1.z, bf[6], s_); s_ = fmaf(v1.w, bf[7], s_);
-                        acc[c] = s_;
+                    for (int g = 0; g < 8; ++g) {
+                        if (g0 + g >= G) break;
+                        const float4 v0 = *reinterpret_cast<const float4 *>(&s_v[qb + q][8 * (g0 + g)]);
+                        const float4 v1 = *reinterpret_cast<const float4 *>(&s_v[qb + q][8 * (g0 + g) + 4]);
+#pragma unroll
+                        for (int c = 0; c < kCpt; ++c) {
+                            float bf[8];
+                            vec16<LORA_BF16>::widen(bq[g][c], bf);
+                            float s_ = acc[c];
+                            s_ = fmaf(v0.x, bf[0], s_); s_ = fmaf(v0.y, bf[1], s_);
+                            s_ = fmaf(v0.z, bf[2], s_); s_ = fmaf(v0.w, bf[3], s_);
+                            s_ = fmaf(v1.x, bf[4], s_); s_ = fmaf(v1.y, bf[5], s_);
+                            s_ = fmaf(v1.z, bf[6], s_); s_ = fmaf(v1.w, bf[7], s_);
+                            acc[c] = s_;
+                        }
                     }
                 }
+                const int32_t t = s_t[qb + q];
+                if (t >= 0 && col_ok) {
+                    const float y0 = fmaf(sc, acc[0], bf16_lo(ya[q])), y1 = fmaf(sc, acc[1], bf16_hi(ya[q]));
+                    *reinterpret_cast<uint32_t *>(y + (size_t)t * d_out + n) = pack_bf16x2(y0, y1);
+                }
             }
-            const int32_t t = s_t[qq];
-            if (t < 0 || !col_ok) continue;
-            uint32_t yw = 0;
 #pragma unroll
-            for (int u = 0; u < kXRows; ++u)
-                if (u == qq) yw = yv[u];
-            const float y0 = fmaf(sc, acc[0], bf16_lo(yw)), y1 = fmaf(sc, acc[1], bf16_hi(yw));
-            *reinterpret_cast<uint32_t *>(y + (size_t)t * d_out + n) = pack_bf16x2(y0, y1);
+            for (int q = 0; q < kXGroup; ++q) ya[q] = yb[q];
         }
     }
 }
@@ -211,8 +221,8 @@ __global__ void __launch_bounds__(256) k_expand_short(const float *__restrict__ 
                                                       const int32_t *__restrict__ skey,
                                                       const int32_t *__restrict__ header,
                                                       uint16_t *__restrict__ y) {
-    __shared__ __attribute__((aligned(16))) float s_v[kXRows][128];
-    __shared__ int32_t s_t[kXRows];
+    __shared__ __attribute__((aligned(16))) float s_v[kXStage][128];
+    __shared__ int32_t s_t[kXStage];
     const int n_short = min(header[kHdrNShort], n_slots);   // skey holds n_slots entries
     for (int i = blockIdx.x; i < n_short; i += gridDim.x) {
         const int key = skey[i];
@@ -242,8 +252,8 @@ __global__ void __launch_bounds__(256) k_expand_blocks(const float *__restrict__
                                                        const int32_t *__restrict__ blk_start,
                                                        const int32_t *__restrict__ blk_seg,
                                                        uint16_t *__restrict__ y) {
-    __shared__ __attribute__((aligned(16))) float s_v[kXRows][128];
-    __shared__ int32_t s_t[kXRows];
+    __shared__ __attribute__((aligned(16))) float s_v[kXStage][128];
+    __shared__ int32_t s_t[kXStage];
     const int nseg = min(*n_seg_p, n_slots), wid = blockIdx.x;   // blk_start, seg_start: n_slots + 2 entries
     if (nseg <= 0 || wid >= blk_start[nseg]) return;
     const int lo = blk_seg[wid];
