@@ -254,7 +254,7 @@ def main():
     dev = "cuda"
     wl = make_workload(args.workload, device=dev)
     mode = {"auto": L.LORA_MODE_AUTO, "bgmv": L.LORA_MODE_BGMV, "sgmv": L.LORA_MODE_SGMV}[args.mode]
-    sgmv = mode == L.LORA_MODE_SGMV or (mode == L.LORA_MODE_AUTO and wl.T >= 1024)
+    sgmv = mode == L.LORA_MODE_SGMV or (mode == L.LORA_MODE_AUTO and wl.T >= L.LORA_AUTO_SGMV_MIN_ROWS)
     eb = 4 if wl.dtype == torch.float32 else 2
     T, R = wl.T, wl.max_rank
     if args.single_adapter:

@@ -81,16 +81,26 @@ typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype_t;
  *   SGMV: rows are grouped into adapter-contiguous segments (a stable sort by
  *         slot, built by lora_build_segments) and each segment shares one
  *         read of its adapter;
- *   AUTO: in the forwards, a batch of fewer than 1024 rows is all BGMV (its
- *         segments are short); a larger one is split per segment: segments
- *         of at least L rows (the prefill chunks) take SGMV -- the grouped
- *         shrink and the expand fused into the base GEMM -- and shorter ones
- *         (decode rows) take BGMV -- the per-row shrink and a per-row expand
- *         after the GEMM.  L is 16 by default, or LORA_FLAG_SHORT_SEGMENT(L)
- *         for bf16 pools.  In lora_shrink and lora_expand (which cannot know
- *         whether segments were built), AUTO is BGMV.
+ *   AUTO: in the forwards, a batch of fewer than LORA_AUTO_SGMV_MIN_ROWS
+ *         rows is all BGMV (its segments are short, and up to 256 rows the
+ *         shrink can ride inside the base GEMM); a larger one is built into
+ *         segments, whose shrink is grouped (one read of each adapter's A
+ *         per segment block), and split per segment for the expand:
+ *         segments of at least L rows (the prefill chunks) take SGMV's
+ *         expand fused into the base GEMM, shorter ones (decode rows) a
+ *         per-row expand after the GEMM that reads each segment's B once.
+ *         L is 16 by default, or LORA_FLAG_SHORT_SEGMENT(L) for bf16 pools.
+ *         In lora_shrink and lora_expand (which cannot know whether
+ *         segments were built), AUTO is BGMV.
  * The result does not depend on the mode beyond fp32 rounding order. */
 typedef enum { LORA_MODE_AUTO = 0, LORA_MODE_BGMV = 1, LORA_MODE_SGMV = 2 } lora_mode_t;
+
+/* AUTO's batch size from which the forwards build segments (see above).
+ * Measured on 512 decode rows of a 70B-shaped q projection (8192 x 8192,
+ * ranks 8-64, 218 distinct adapters): 245 us with segments against 266 us
+ * per row; on 256 rows of a 4096 x 4096 projection (rank 16) the per-row
+ * path with the shrink inside the GEMM takes 33 us against 71 us. */
+#define LORA_AUTO_SGMV_MIN_ROWS 512
 
 /* Flags for the forwards (lora_linear_forward, _sliced, _fp8). */
 #define LORA_FLAG_SEGMENTS_READY 0x1  /* segments already built in this workspace for these ids */

@@ -67,7 +67,7 @@ inline lora_status_t check_ws_fp8(const void *ws, size_t ws_bytes, int32_t T, in
 inline bool use_sgmv(lora_mode_t mode, int32_t T) {
     if (mode == LORA_MODE_SGMV) return true;
     if (mode == LORA_MODE_BGMV) return false;
-    return T >= 1024;
+    return T >= LORA_AUTO_SGMV_MIN_ROWS;
 }
 
 // Flag bits the forwards accept: the two flags and the short-segment threshold.

@@ -28,6 +28,7 @@ LORA_BF16 = 1
 LORA_MODE_AUTO = 0
 LORA_MODE_BGMV = 1
 LORA_MODE_SGMV = 2
+LORA_AUTO_SGMV_MIN_ROWS = 512      # AUTO builds segments from this many rows on
 
 LORA_FLAG_SEGMENTS_READY = 0x1
 LORA_FLAG_SEPARATE_EXPAND = 0x2

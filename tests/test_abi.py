@@ -32,6 +32,17 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_header_constants_match_the_binding():
+    """The integer #defines of include/lora.h and the binding's copies agree."""
+    src = open(os.path.join(ROOT, "include", "lora.h")).read()
+    defs = dict(re.findall(r"#define\s+(LORA_[A-Z0-9_]+)\s+(0x[0-9a-fA-F]+|\d+)\b", src))
+    assert int(defs["LORA_AUTO_SGMV_MIN_ROWS"], 0) == L.LORA_AUTO_SGMV_MIN_ROWS
+    assert int(defs["LORA_FLAG_SEGMENTS_READY"], 0) == L.LORA_FLAG_SEGMENTS_READY
+    assert int(defs["LORA_FLAG_SEPARATE_EXPAND"], 0) == L.LORA_FLAG_SEPARATE_EXPAND
+    m = re.search(r"#define\s+LORA_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == L.LORA_NOALLOC_SCRATCH_BYTES
+
+
 def test_version_and_status_strings(lib):
     assert "gfx950" in L.lora_version()
     for code in range(7):

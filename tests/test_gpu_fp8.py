@@ -120,7 +120,7 @@ FWD_SHAPES = [
     (300, 208, 264, 16, [3, 16, 0, 9, 13]),     # 128x64 whole tiles, ragged everything
     (37, 2048, 1024, 16, [16, 16, 7, 0]),       # decode-sized split-K
     (200, 1024, 4096, 32, [32, 17, 8, 0, 32]),  # decode-sized, larger rank
-    (1500, 512, 512, 16, [16, 4, 16, 12]),      # SGMV-sized (AUTO picks SGMV at T >= 1024)
+    (1500, 512, 512, 16, [16, 4, 16, 12]),      # SGMV-sized (AUTO picks SGMV from LORA_AUTO_SGMV_MIN_ROWS rows)
     (2048, 512, 3584, 8, [8, 8, 3]),            # 256x128 whole tiles with the fused expand
     (1, 16, 8, 8, [8, 5]),                      # the smallest shape: one row, one K step, one column octet
     (1, 4096, 4096, 16, [16, 16, 16]),          # one decode row

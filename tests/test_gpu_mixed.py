@@ -3,7 +3,7 @@ multiple LoRAs: segmented matrix multiplies and adapter scheduling", section
 "Not merging the weights, computing in batches": BGMV for decode rows, SGMV
 for prefill segments, both in one forward).
 
-In AUTO mode a batch of at least 1024 rows is split by segment length:
+In AUTO mode a batch of at least LORA_AUTO_SGMV_MIN_ROWS rows is split by segment length:
 every segment takes the grouped shrink; segments of at least L rows take the
 expand fused into the GEMM, shorter ones (decode rows) a per-row expand after
 the GEMM, which visits their rows last.  The GEMM's row
@@ -93,7 +93,7 @@ def test_mixed_batch_every_threshold(which):
     each other."""
     ranks = [8, 16, 32, 64, 8, 24, 40, 64, 16, 56, 8, 32, 48, 16, 8, 64]
     b = Batch(200, [700, 400, 300, 9, 5, 17], 1024, 2048, ranks, 64, seed=11)
-    assert b.T >= 1024
+    assert b.T >= L.LORA_AUTO_SGMV_MIN_ROWS
     ref = b.oracle()
     outs = []
     runs = [(L.LORA_MODE_AUTO, L.LORA_FLAG_SHORT_SEGMENT(n)) for n in (0, 1, 4, 64, 255)]
@@ -159,7 +159,7 @@ def test_overwritten_segment_tables_stay_in_bounds():
     parity."""
     ranks = [8, 16, 32, 64, 8, 24, 40, 64]
     b = Batch(300, [700, 500, 300], 512, 1024, ranks, 64, seed=21)
-    assert b.T >= 1024
+    assert b.T >= L.LORA_AUTO_SGMV_MIN_ROWS
     sl = b.slices[0]
     pool = sl["padded"].pool
     ws = L.Workspace(b.T, b.n_slots, 64, 1024)
