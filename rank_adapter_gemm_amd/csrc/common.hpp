@@ -247,6 +247,9 @@ lora_status_t launch_segments(const int32_t *ids, int32_t T, int32_t n_slots, co
                               void *ws, hipStream_t s, int32_t short_len = 1);
 // Separate expand of the short segments' rows (the GEMM left their term out),
 // one work item per short segment and column chunk.
+lora_status_t launch_expand_tiles(const float *v, int32_t v_stride, int32_t T, const lora_pool_t &p,
+                                  const int32_t *ids, const int32_t *gperm, const int32_t *n_fused, void *y,
+                                  hipStream_t s);
 lora_status_t launch_expand_short(const float *v, int32_t v_stride, int32_t T, const lora_pool_t &p, void *y,
                                   const ws_layout &L, void *ws, hipStream_t s);
 // Shrink for n_slices pools that share x, ids, n_slots, d_in, max_rank and

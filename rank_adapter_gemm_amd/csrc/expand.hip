@@ -234,39 +234,6 @@ __global__ void __launch_bounds__(256) k_expand_short(const float *__restrict__ 
     }
 }
 
-// The separate expand in SGMV mode: one work item per (work block of at most
-// kShrinkRows rows of one segment, the grouped shrink's table; column
-// chunk), so B is read once per block instead of once per row.  Base-only
-// rows belong to no segment and are left as they are.  The grid's x extent
-// is at most the block table's size; every index taken from the tables is
-// checked as in k_expand_short.
-__global__ void __launch_bounds__(256) k_expand_blocks(const float *__restrict__ v, int32_t v_stride, int32_t T,
-                                                       int32_t d_out, const uint16_t *__restrict__ b,
-                                                       const float *__restrict__ scale,
-                                                       const int32_t *__restrict__ rank,
-                                                       const int32_t *__restrict__ row0, int32_t n_slots,
-                                                       int32_t max_rank, const int32_t *__restrict__ perm,
-                                                       const int32_t *__restrict__ seg_id,
-                                                       const int32_t *__restrict__ seg_start,
-                                                       const int32_t *__restrict__ n_seg_p,
-                                                       const int32_t *__restrict__ blk_start,
-                                                       const int32_t *__restrict__ blk_seg,
-                                                       uint16_t *__restrict__ y) {
-    __shared__ __attribute__((aligned(16))) float s_v[kXStage][128];
-    __shared__ int32_t s_t[kXStage];
-    const int nseg = min(*n_seg_p, n_slots), wid = blockIdx.x;   // blk_start, seg_start: n_slots + 2 entries
-    if (nseg <= 0 || wid >= blk_start[nseg]) return;
-    const int lo = blk_seg[wid];
-    if (lo < 0 || lo >= nseg) return;
-    const int a = seg_id[lo];
-    if (a < 0 || a >= n_slots) return;
-    const int64_t s0 = seg_start[lo], s1 = seg_start[lo + 1];
-    const int64_t p0 = s0 + ((int64_t)wid - blk_start[lo]) * kShrinkRows;
-    if (s0 < 0 || s1 > T || p0 < s0 || p0 >= s1) return;
-    const int len = (int)((s1 < p0 + kShrinkRows ? s1 : p0 + kShrinkRows) - p0);
-    expand_adapter_rows(a, (int)p0, len, perm, v, v_stride, T, d_out, b, scale, rank, row0, max_rank, y, s_v, s_t);
-}
-
 lora_status_t launch_expand_short(const float *v, int32_t v_stride, int32_t T, const lora_pool_t &p, void *y,
                                   const ws_layout &L, void *ws, hipStream_t s) {
     if (p.dtype != LORA_BF16) return LORA_OK;
@@ -286,14 +253,12 @@ lora_status_t launch_expand(const float *v, int32_t v_stride, int32_t T, const l
                             hipStream_t s) {
     const int32_t *perm = sgmv ? ws_ptr<int32_t>(ws, L.perm) : nullptr;
     if (sgmv && p.dtype == LORA_BF16 && T > 0) {
-        const int32_t n_work_upper = (T + kShrinkRows - 1) / kShrinkRows + (T < p.n_slots ? T : p.n_slots);
-        hipLaunchKernelGGL(k_expand_blocks, dim3(n_work_upper, (p.d_out + kXCols - 1) / kXCols), dim3(256), 0, s,
-                           v, v_stride, T, p.d_out, (const uint16_t *)p.b, p.scale, p.rank, p.row0, p.n_slots,
-                           p.max_rank, perm,
-                           ws_ptr<int32_t>(ws, L.seg_id), ws_ptr<int32_t>(ws, L.seg_start),
-                           ws_ptr<int32_t>(ws, L.n_seg), ws_ptr<int32_t>(ws, L.blk_start),
-                           ws_ptr<int32_t>(ws, L.blk_seg), (uint16_t *)y);
-        return hip_status(hipGetLastError());
+        // as in the fused forward: rows in the GEMM order, long segments on
+        // the matrix cores, the short ones per row
+        lora_status_t st = launch_expand_tiles(v, v_stride, T, p, ids, ws_ptr<int32_t>(ws, L.gperm),
+                                               ws_ptr<int32_t>(ws, L.header) + kHdrNLong, y, s);
+        if (st == LORA_OK) st = launch_expand_short(v, v_stride, T, p, y, L, ws, s);
+        return st;
     }
     const dim3 grid(T, (p.d_out + 2047) / 2048);
     if (p.dtype == LORA_F32)

@@ -221,7 +221,7 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
                 const int32_t raw = g.ids[t];
                 if (raw >= 0 && raw < g.n_slots && g.rank[raw] > 0) id = raw;
             }
-            s_meta_t[i] = t;
+            s_meta_t[i] = (g.accum_y && id < 0) ? -1 : t;   // adding: rows without a term stay untouched
             s_meta_id[i] = id;
         }
     }
@@ -544,6 +544,45 @@ bool gemm_grouping_pays(int32_t T, int32_t K, const int32_t *Ns, int32_t n, size
         if (pl.bm != 256 || pl.bn != 256 || pl.tail != 0) return true;
     }
     return false;
+}
+
+// The separate expand of rows in the GEMM order on the matrix cores: the
+// LoRA kernel with no K steps runs its expand pass (s v in three bf16 parts
+// times B, fp32 accumulators) on each 256 x 256 tile of rows and adds the
+// tile to y (read, fp32 sum, one rounding to bf16).  Rows without a usable
+// adapter, and rows at GEMM positions from *n_fused on (short segments, left
+// to the per-row expand), are neither read nor written.
+lora_status_t launch_expand_tiles(const float *v, int32_t v_stride, int32_t T, const lora_pool_t &p,
+                                  const int32_t *ids, const int32_t *gperm, const int32_t *n_fused, void *y,
+                                  hipStream_t s) {
+    if (p.dtype != LORA_BF16 || T <= 0) return LORA_ERR_INVALID_ARGUMENT;
+    gemm_args g{};
+    g.T = T;
+    g.K = 0;
+    g.N = p.d_out;
+    g.y = (uint16_t *)y;
+    g.perm = gperm;
+    g.n_fused = n_fused;
+    g.b = (const uint16_t *)p.b;
+    g.scale = p.scale;
+    g.rank = p.rank;
+    g.row0 = p.row0;
+    g.n_slots = p.n_slots;
+    g.max_rank = p.max_rank;
+    g.ids = ids;
+    g.v = v;
+    g.v_stride = v_stride;
+    g.n_tiles_m = ceil_div(T, 256);
+    g.n_tiles_n = ceil_div(p.d_out, 256);
+    g.tile_base = 0;
+    g.n_tiles = g.n_tiles_m * g.n_tiles_n;
+    g.splits = 1;
+    g.k_chunk = 0;
+    g.col_strips = col_strips_pay(T, p.d_out, g.n_tiles_n);
+    g.accum_y = 1;
+    // no K steps: one small stage keeps the LDS at the epilogue's size
+    hipLaunchKernelGGL((k_gemm_bf16<true, 256, 256, 16, 1, false, false, 8, 2>), dim3(g.n_tiles), dim3(512), 0, s, g);
+    return hip_status(hipGetLastError());
 }
 
 // Base products of several outputs that share x (projections of one

@@ -49,6 +49,7 @@ struct gemm_args {
     const int32_t *n_fused;        // mixed batches: rows at positions >= *n_fused get no low-rank term here
     int32_t col_strips;            // tile order: 1 = strips of kGroupN column tiles (see grouped_tile)
     int32_t n_slices;              // grouped launch: 0 (one output), else slices sl[0..n_slices)
+    int32_t accum_y;               // whole tiles: add the tile to y (read, fp32 sum, one rounding) instead of storing it
     gemm_slice sl[kMaxSlices];     // column tiles numbered slice after slice
 };
 
@@ -380,6 +381,16 @@ __device__ __forceinline__ void gemm_store_tile(const gemm_args &g, f32x16_t (&a
     const int n = n0 + wn * WN + 8 * q;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
+        // adding to y: this block's y values load before the staging below
+        uint4 yq[SPLIT ? 1 : PASSES];
+        if (!SPLIT && g.accum_y) {
+#pragma unroll
+            for (int k = 0; k < PASSES; ++k) {
+                const int i = wm * WM + rb * 32 + rr + RPP * k;
+                const int32_t tk = s_meta_t ? s_meta_t[i] : -1;
+                yq[k] = (tk >= 0 && n < N) ? ldg16(g.y + (int64_t)tk * N + n) : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
         __syncthreads();
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
@@ -401,7 +412,13 @@ __device__ __forceinline__ void gemm_store_tile(const gemm_args &g, f32x16_t (&a
                 *reinterpret_cast<float4 *>(dst) = o0;
                 *reinterpret_cast<float4 *>(dst + 4) = o1;
             } else {
-                const float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+                float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+                if (g.accum_y) {
+                    float yf[8];
+                    vec16<LORA_BF16>::widen(yq[SPLIT ? 0 : k], yf);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[e] += yf[e];
+                }
                 stg16(g.y + (int64_t)tk * N + n, vec16<LORA_BF16>::narrow(o));
             }
         }

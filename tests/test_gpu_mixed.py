@@ -193,3 +193,27 @@ def test_overwritten_segment_tables_stay_in_bounds():
     torch.cuda.synchronize()
     assert L.lora_get_device_error(ws.buf) == -1
     assert_parity(y, b.oracle(), torch.bfloat16, "after rebuilding the segments")
+
+
+@pytest.mark.parametrize("dT", [-1, 0])
+def test_auto_threshold_builds_segments_from_min_rows(dT):
+    """AUTO takes the per-row path below LORA_AUTO_SGMV_MIN_ROWS rows (no
+    segments are built in a fresh workspace) and builds segments from that
+    many rows on; both agree with the oracle."""
+    T_dec = L.LORA_AUTO_SGMV_MIN_ROWS + dT
+    ranks = [8, 16, 32, 64, 8, 24, 40, 64, 16, 56, 8, 32]
+    b = Batch(T_dec, [], 512, 1024, ranks, 64, seed=30 + dT)
+    assert b.T == T_dec
+    ws = L.Workspace(b.T, b.n_slots, 64, 1024)
+    ws.segments(b.T)["n_seg"].fill_(-7)                 # a sentinel only a segment build overwrites
+    y = torch.empty(b.T, 1024, dtype=torch.bfloat16, device="cuda")
+    L.lora_linear_forward(b.x, b.slices[0]["W"], y, b.T, b.slices[0]["padded"].pool, b.ids_dev, L.LORA_MODE_AUTO, 0,
+                          ws.buf)
+    torch.cuda.synchronize()
+    assert L.lora_get_device_error(ws.buf) == -1
+    n_seg = int(ws.segments(b.T)["n_seg"].cpu()[0])
+    if dT < 0:
+        assert n_seg == -7
+    else:
+        assert n_seg == len(np.unique(b.ids[b.ids >= 0]))
+    assert_parity(y, b.oracle(), torch.bfloat16, "T=%d" % b.T)
