@@ -157,7 +157,8 @@ struct ws_layout {
     size_t perm;        // int32[T]
     size_t gperm;       // int32[T]: the GEMM's row order (long-segment rows, then short-segment rows)
     size_t gbase;       // int32[n_slots + 2]: first GEMM position of each key's rows
-    size_t skey;        // int32[n_slots]: key of each short segment, ascending
+    size_t srec;        // int4[n_slots]: short segments {key, first GEMM position, rows, 0}, ascending keys;
+                        // key 0 from entry n_short to min(n_slots, T)
     size_t tile_hist;   // int32[(n_slots + 1) * n_tiles]
     size_t v;           // fp32[T * max_rank]
     size_t partial;     // fp32[kMaxKSplit * T * max_rank]
@@ -186,7 +187,7 @@ inline ws_layout make_ws_layout(int32_t T, int32_t n_slots, int32_t max_rank, in
     L.perm = o;      o = align256(o + 4 * t);
     L.gperm = o;     o = align256(o + 4 * t);
     L.gbase = o;     o = align256(o + 4 * (size_t)(n_slots + 2));
-    L.skey = o;      o = align256(o + 4 * (size_t)n_slots);
+    L.srec = o;      o = align256(o + 16 * (size_t)n_slots);
     L.tile_hist = o; o = align256(o + 4 * (size_t)(n_slots + 1) * n_tiles);
     L.v = o;         o = align256(o + 4 * t * (size_t)max_rank);
     L.partial = o;   o = align256(o + 4 * (size_t)kMaxKSplit * t * (size_t)max_rank);

@@ -207,30 +207,28 @@ __device__ __forceinline__ void expand_adapter_rows(int a, int p0, int len, cons
 // The per-row (BGMV) expand of a mixed batch's short segments, whose rows the
 // GEMM visits last and leaves without their low-rank term: one work item per
 // (short segment, column chunk); a short segment's rows are consecutive in
-// the GEMM order.  Every index taken from the segment tables is checked
-// against the tables' sizes and T, so tables that something else overwrote
-// give wrong rows, never an access outside the buffers.
+// the GEMM order.  Item i reads the segment build's record i ({key, first
+// GEMM position, rows}; key 0 past the last short segment), so its chain to
+// the B loads is one record and the slot's rank.  Every field taken from the
+// record is checked against the tables' sizes and T, so tables that
+// something else overwrote give wrong rows, never an access outside the
+// buffers.
 __global__ void __launch_bounds__(256) k_expand_short(const float *__restrict__ v, int32_t v_stride, int32_t T,
                                                       int32_t d_out, const uint16_t *__restrict__ b,
                                                       const float *__restrict__ scale,
                                                       const int32_t *__restrict__ rank,
                                                       const int32_t *__restrict__ row0, int32_t n_slots,
                                                       int32_t max_rank, const int32_t *__restrict__ gperm,
-                                                      const int32_t *__restrict__ offsets,
-                                                      const int32_t *__restrict__ gbase,
-                                                      const int32_t *__restrict__ skey,
-                                                      const int32_t *__restrict__ header,
-                                                      uint16_t *__restrict__ y) {
+                                                      const int4 *__restrict__ srec, uint16_t *__restrict__ y) {
     __shared__ __attribute__((aligned(16))) float s_v[kXStage][128];
     __shared__ int32_t s_t[kXStage];
-    const int n_short = min(header[kHdrNShort], n_slots);   // skey holds n_slots entries
-    for (int i = blockIdx.x; i < n_short; i += gridDim.x) {
-        const int key = skey[i];
-        if (key < 1 || key > n_slots) continue;              // offsets, gbase: n_slots + 2 entries
-        const int64_t p0 = gbase[key], len = (int64_t)offsets[key + 1] - offsets[key];
-        if (p0 < 0 || len < 1 || p0 + len > T) continue;
-        expand_adapter_rows(key - 1, (int)p0, (int)len, gperm, v, v_stride, T, d_out, b, scale, rank, row0,
-                            max_rank, y, s_v, s_t);
+    const int n_rec = min(n_slots, T);                      // records written by the segment build
+    for (int i = blockIdx.x; i < n_rec; i += gridDim.x) {
+        const int4 rec = srec[i];                           // {key, first GEMM position, rows, 0}
+        if (rec.x == 0) break;                              // no short segment from here on
+        if (rec.x < 1 || rec.x > n_slots || rec.y < 0 || rec.z < 1 || (int64_t)rec.y + rec.z > T) continue;
+        expand_adapter_rows(rec.x - 1, rec.y, rec.z, gperm, v, v_stride, T, d_out, b, scale, rank, row0, max_rank, y,
+                            s_v, s_t);
     }
 }
 
@@ -242,9 +240,7 @@ lora_status_t launch_expand_short(const float *v, int32_t v_stride, int32_t T, c
     if (segs > T) segs = T;
     hipLaunchKernelGGL(k_expand_short, dim3(segs, chunks), dim3(256), 0, s, v, v_stride, T, p.d_out,
                        (const uint16_t *)p.b, p.scale, p.rank, p.row0, p.n_slots, p.max_rank,
-                       ws_ptr<int32_t>(ws, L.gperm),
-                       ws_ptr<int32_t>(ws, L.offsets), ws_ptr<int32_t>(ws, L.gbase), ws_ptr<int32_t>(ws, L.skey),
-                       ws_ptr<int32_t>(ws, L.header), (uint16_t *)y);
+                       ws_ptr<int32_t>(ws, L.gperm), ws_ptr<int4>(ws, L.srec), (uint16_t *)y);
     return hip_status(hipGetLastError());
 }
 

@@ -124,12 +124,14 @@ __device__ void compact_segments(const int32_t *s_off, int32_t nb, int32_t T, in
 // The GEMM's row order: the rows of the base block and of the segments of at
 // least short_len rows, in sorted order, then the rows of the shorter
 // segments, in sorted order (a stable partition of perm).  gbase[k] is the
-// first GEMM position of key k's rows; skey lists the short segments' keys
-// in ascending order; header[kHdrNLong] is the number of rows before the
-// short ones and header[kHdrNShort] the number of short segments.  Every
-// thread of the block calls it.
+// first GEMM position of key k's rows; srec lists the short segments in
+// ascending key order as {key, first GEMM position, rows, 0}, then key 0 up
+// to entry min(n_slots, T) (so the per-row expand reads one record per
+// item); header[kHdrNLong] is the number of rows before the short ones and
+// header[kHdrNShort] the number of short segments.  Every thread of the
+// block calls it.
 __device__ void gemm_order(const int32_t *s_off, int32_t nb, int32_t T, int32_t short_len, int32_t *s_wave,
-                           int32_t *__restrict__ gbase, int32_t *__restrict__ skey, int32_t *__restrict__ header) {
+                           int32_t *__restrict__ gbase, int4 *__restrict__ srec, int32_t *__restrict__ header) {
     int32_t n_short = 0;
     for (int32_t k0 = 0; k0 < nb; k0 += blockDim.x) {
         const int32_t k = k0 + threadIdx.x;
@@ -149,11 +151,13 @@ __device__ void gemm_order(const int32_t *s_off, int32_t nb, int32_t T, int32_t 
         const int32_t sp = block_exclusive_scan(is_short ? len : 0, s_wave, &st) + short_carry;
         const int32_t si = block_exclusive_scan(is_short ? 1 : 0, s_wave, &nt) + seg_carry;
         if (k < nb) gbase[k] = is_short ? n_long + sp : lp;
-        if (is_short) skey[si] = k;
+        if (is_short) srec[si] = make_int4(k, n_long + sp, len, 0);
         long_carry += lt;
         short_carry += st;
         seg_carry += nt;
     }
+    const int32_t n_rec = min(nb - 1, T);
+    for (int32_t i = seg_carry + threadIdx.x; i < n_rec; i += blockDim.x) srec[i] = make_int4(0, 0, 0, 0);
     if (threadIdx.x == 0) {
         header[kHdrNLong] = n_long;
         header[kHdrShortLen] = short_len;
@@ -210,7 +214,7 @@ __global__ void __launch_bounds__(1024) k_seg_scan(int32_t *__restrict__ tile_hi
                                                    int32_t *__restrict__ blk_start,
                                                    int32_t *__restrict__ blk_seg,
                                                    int32_t *__restrict__ gbase,
-                                                   int32_t *__restrict__ skey,
+                                                   int4 *__restrict__ srec,
                                                    int32_t *__restrict__ header) {
     extern __shared__ int32_t s_off[];        // [n_slots + 2]
     __shared__ int32_t s_wave[48];
@@ -243,7 +247,7 @@ __global__ void __launch_bounds__(1024) k_seg_scan(int32_t *__restrict__ tile_hi
     __syncthreads();
     for (int32_t k = threadIdx.x; k <= nb; k += blockDim.x) offsets[k] = s_off[k];
 
-    gemm_order(s_off, nb, T, short_len, s_wave, gbase, skey, header);
+    gemm_order(s_off, nb, T, short_len, s_wave, gbase, srec, header);
     compact_segments(s_off, nb, T, s_wave, seg_id, seg_start, n_seg, blk_start, blk_seg);
 }
 
@@ -282,7 +286,7 @@ lora_status_t launch_segments(const int32_t *ids, int32_t T, int32_t n_slots, co
                        ws_ptr<int32_t>(ws, L.offsets), ws_ptr<int32_t>(ws, L.seg_id),
                        ws_ptr<int32_t>(ws, L.seg_start), ws_ptr<int32_t>(ws, L.n_seg),
                        ws_ptr<int32_t>(ws, L.blk_start), ws_ptr<int32_t>(ws, L.blk_seg),
-                       ws_ptr<int32_t>(ws, L.gbase), ws_ptr<int32_t>(ws, L.skey), ws_ptr<int32_t>(ws, L.header));
+                       ws_ptr<int32_t>(ws, L.gbase), ws_ptr<int4>(ws, L.srec), ws_ptr<int32_t>(ws, L.header));
     hipLaunchKernelGGL(k_seg_scatter, dim3(n_tiles), dim3(kSegTile), 0, s, ids, T, n_slots,
                        tile_hist, n_tiles, ws_ptr<int32_t>(ws, L.perm), ws_ptr<int32_t>(ws, L.offsets),
                        ws_ptr<int32_t>(ws, L.gbase), ws_ptr<int32_t>(ws, L.gperm));
