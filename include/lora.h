@@ -271,11 +271,15 @@ lora_status_t lora_shrink(const void *x, int32_t T, const lora_pool_t *pool, con
 /* The second low-rank product, added to the output:
  * y[t,:] += s_a * v[t, 0:r_a] B_a for rows with a usable adapter a = ids[t];
  * other rows are not touched ("Serving multiple LoRAs ...", section "Not
- * merging the weights, computing in batches": (xA)B added to the base row;
- * "LoRAX, in depth", section "Computing a batch that mixes adapters": the
- * scale multiplies that product; "Serving LoRA adapters ...", Step 4: the
- * expand is added to the base layer's output).  A read-modify-write of y (bf16 y is rounded
- * once, to nearest even, after the fp32 sum).
+ * merging the weights, computing in batches": the rank vector times B is
+ * added to the row's base output; "LoRAX, in depth", section "Computing a
+ * batch that mixes adapters": the scale multiplies that product; "Serving
+ * LoRA adapters ...", Step 4: the expand is added to the base layer's
+ * output).  A read-modify-write of y (bf16 y is rounded once, to nearest
+ * even, after the fp32 sum).  In SGMV mode with a bf16 pool the rows of
+ * segments of at least the build's threshold go through the matrix cores
+ * (s v as three bf16 parts, i.e. its full fp32 value) and shorter ones per
+ * row; the sums differ from BGMV's only in fp32 rounding order.
  *   v: DEVICE fp32 [T, max_rank];  y: DEVICE [T, d_out] (pool dtype).
  * SGMV requires lora_build_segments on the same ids and ws beforehand. */
 lora_status_t lora_expand(const float *v, int32_t T, const lora_pool_t *pool, const int32_t *ids,

@@ -7,14 +7,16 @@
 // that product, as in lora_mixed_batch ("LoRAX, in depth", section
 // "Computing a batch that mixes adapters").
 //
-// One workgroup per (token row, 2048-column chunk); each lane owns 8
-// consecutive output columns.  B is stored in rank octets [r/8][d_out][8], so
-// for one octet a lane reads its 8 columns x 8 ranks as 8 contiguous 16-byte
-// vectors and neighbouring lanes read neighbouring vectors.  Only the first
-// ceil(r/8) octets are read.  The row's v values are staged in LDS.  y is read,
-// updated in fp32 and written back with one rounding.  In SGMV mode the rows
-// are visited in segment order (through perm), so consecutive workgroups
-// share the same B in the caches.
+// Three forms, all reading B in rank octets [r/8][d_out][8] (the 8 ranks of
+// one output column are 16 contiguous bytes) and only the first ceil(r/8)
+// octets of a slot, summing ranks in octet order, and adding to y with one
+// rounding:
+//  * k_expand_rows (BGMV, and fp32 pools): one workgroup per (token row,
+//    2048 columns), rows in their own order;
+//  * expand_adapter_rows (rows that share one adapter), used by
+//    k_expand_short for the short segments of a mixed batch;
+//  * in SGMV mode the long segments' rows go through the LoRA GEMM kernel
+//    with no K steps (launch_expand_tiles in gemm.hip), on the matrix cores.
 #include "common.hpp"
 
 namespace lora {

@@ -21,8 +21,9 @@ Five workloads, named by what they are:
                    padded to 64, alpha = 2r, 5 projections of a 70B model
   decode_70b       the decode rows alone: 512 single-token requests on the 70B
                    q projection with the same adapter mix (measures the
-                   per-row shrink's true-rank reads; not one of the five
-                   parity configurations)
+                   per-row shrink's true-rank reads in BGMV mode and sets
+                   AUTO's segment threshold; not one of the five parity
+                   configurations)
 
 The adapter orientation is the pages' row-vector form: A [d_in, r], B [r, d_out].
 """
