@@ -47,6 +47,9 @@ template <bool LORA, int BM, int BN, int BK, int NS, bool SPLIT, bool SH = false
 __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
     static_assert(!SH || SPLIT, "the fused shrink runs in split-K mode");
     static_assert(!SH || (WV == 4 || WV == 8), "the fused shrink maps 4 or 8 threads to a (row, rank) pair");
+    // The single-stage LoRA instantiation is the expand-only pass
+    // (launch_expand_tiles: no K steps): it adds its tile to y.
+    constexpr bool ADD = LORA && !SPLIT && NS == 1;
     typedef gemm_cfg<BM, BN, BK, NS, SH, WV, WR> C;
     constexpr int WM = C::WM, WN = C::WN, RB = C::RB, CB = C::CB;
     constexpr int XCH = C::XCH, WCH = C::WCH, XSTAGE = C::XSTAGE, WSTAGE = C::WSTAGE;
@@ -221,7 +224,7 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
                 const int32_t raw = g.ids[t];
                 if (raw >= 0 && raw < g.n_slots && g.rank[raw] > 0) id = raw;
             }
-            s_meta_t[i] = (g.accum_y && id < 0) ? -1 : t;   // adding: rows without a term stay untouched
+            s_meta_t[i] = (ADD && id < 0) ? -1 : t;   // adding: rows without a term stay untouched
             s_meta_id[i] = id;
         }
     }
@@ -337,8 +340,8 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_bf16(gemm_args g) {
             flag_bad_row(g.err, fl_t);
     }
 
-    gemm_store_tile<BM, BN, WV, WR, SPLIT>(g, acc, reinterpret_cast<float *>(smem), s_meta_t, n0, w, lane,
-                                         tidx, split);
+    gemm_store_tile<BM, BN, WV, WR, SPLIT, ADD>(g, acc, reinterpret_cast<float *>(smem), s_meta_t, n0, w, lane,
+                                              tidx, split);
 }
 
 struct gemm_f32_args {
@@ -579,8 +582,8 @@ lora_status_t launch_expand_tiles(const float *v, int32_t v_stride, int32_t T, c
     g.splits = 1;
     g.k_chunk = 0;
     g.col_strips = col_strips_pay(T, p.d_out, g.n_tiles_n);
-    g.accum_y = 1;
-    // no K steps: one small stage keeps the LDS at the epilogue's size
+    // no K steps: one small stage keeps the LDS at the epilogue's size (the
+    // single-stage instantiation is the one that adds its tile to y)
     hipLaunchKernelGGL((k_gemm_bf16<true, 256, 256, 16, 1, false, false, 8, 2>), dim3(g.n_tiles), dim3(512), 0, s, g);
     return hip_status(hipGetLastError());
 }

@@ -49,7 +49,6 @@ struct gemm_args {
     const int32_t *n_fused;        // mixed batches: rows at positions >= *n_fused get no low-rank term here
     int32_t col_strips;            // tile order: 1 = strips of kGroupN column tiles (see grouped_tile)
     int32_t n_slices;              // grouped launch: 0 (one output), else slices sl[0..n_slices)
-    int32_t accum_y;               // whole tiles: add the tile to y (read, fp32 sum, one rounding) instead of storing it
     gemm_slice sl[kMaxSlices];     // column tiles numbered slice after slice
 };
 
@@ -367,11 +366,16 @@ __device__ __forceinline__ void lora_pass_impl(const gemm_args &g, f32x16_t (&ac
 // through its own LDS area; a lane then owns 8 consecutive columns of
 // several rows and writes them with 16-byte stores after one rounding (the
 // low-rank term is already in the accumulators).  In split-K mode the
-// staged fp32 rows go to the partial buffer instead.
-template <int BM, int BN, int WV, int WR, bool SPLIT, int RB, int CB>
+// staged fp32 rows go to the partial buffer instead.  ADD (the expand-only
+// pass) adds the tile to y instead: the block's y values load before its
+// staging, and the sum is rounded once.  It is a template parameter so that
+// the kernels that only store keep their registers (the y staging would
+// make the FP8 LoRA kernel spill).
+template <int BM, int BN, int WV, int WR, bool SPLIT, bool ADD, int RB, int CB>
 __device__ __forceinline__ void gemm_store_tile(const gemm_args &g, f32x16_t (&acc)[RB][CB], float *smem_f,
                                                 const int32_t *s_meta_t, int n0, int w, int lane,
                                                 int tidx, int split) {
+    static_assert(!(ADD && SPLIT), "split pieces store fp32 partials");
     constexpr int WM = BM / WR, WN = BN / (WV / WR), SLD = WN + 4;
     const int wm = w / (WV / WR), wn = w % (WV / WR);
     const int N = g.N;
@@ -382,8 +386,8 @@ __device__ __forceinline__ void gemm_store_tile(const gemm_args &g, f32x16_t (&a
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         // adding to y: this block's y values load before the staging below
-        uint4 yq[SPLIT ? 1 : PASSES];
-        if (!SPLIT && g.accum_y) {
+        uint4 yq[ADD ? PASSES : 1];
+        if constexpr (ADD) {
 #pragma unroll
             for (int k = 0; k < PASSES; ++k) {
                 const int i = wm * WM + rb * 32 + rr + RPP * k;
@@ -413,9 +417,9 @@ __device__ __forceinline__ void gemm_store_tile(const gemm_args &g, f32x16_t (&a
                 *reinterpret_cast<float4 *>(dst + 4) = o1;
             } else {
                 float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-                if (g.accum_y) {
+                if constexpr (ADD) {
                     float yf[8];
-                    vec16<LORA_BF16>::widen(yq[SPLIT ? 0 : k], yf);
+                    vec16<LORA_BF16>::widen(yq[k], yf);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) o[e] += yf[e];
                 }

@@ -335,7 +335,7 @@ __global__ void __launch_bounds__(WV * 64) k_gemm_fp8(gemm_args g) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    gemm_store_tile<BM, BN, WV, WR, SPLIT>(g, acc, reinterpret_cast<float *>(smem), s_meta_t, n0, w, lane,
+    gemm_store_tile<BM, BN, WV, WR, SPLIT, false>(g, acc, reinterpret_cast<float *>(smem), s_meta_t, n0, w, lane,
                                          tidx, split);
 }
 
