@@ -7,7 +7,9 @@ columns (d_in * d_out at most 2^25), each half the time from the multi-tile
 part of its range (T >= 256, d_in >= 512, d_out >= 1024); max_rank one of
 the allowed multiples of 8, 1-63 slots with random ranks (some empty), and
 an id mix drawn from uniform, skewed, one-adapter, all-base and sorted
-batches, with a share of base rows and, in some cases, out-of-range ids.  Each case runs every mode
+batches, with a share of base rows and, in some cases, out-of-range ids; a
+further set of forward cases uses packed pools (each slot's rank rounded up
+to 8 rows, some with an octet to spare).  Each case runs every mode
 (AUTO, BGMV, SGMV) with the fused and the separate expand and checks the
 sampled rows (the first and last rows, rows at 64-, 128- and 256-row tile
 edges and random rows) against the oracle, the device error word against
@@ -94,14 +96,18 @@ def describe(c, extra=""):
 class Layer:
     """x, W and one adapter pool on the GPU; A, B kept for the oracle."""
 
-    def __init__(self, c, d_out, dtype, seed, x=None):
+    def __init__(self, c, d_out, dtype, seed, x=None, packed=False):
         g = torch.Generator(device="cuda")
         g.manual_seed(seed)
         T, d_in, R = c["T"], c["d_in"], c["R"]
         self.dtype, self.d_out, self.ranks = dtype, d_out, c["ranks"]
         self.x = torch.randn(T, d_in, generator=g, device="cuda").to(dtype) if x is None else x
         self.W = (torch.randn(d_in, d_out, generator=g, device="cuda") / d_in ** 0.5).to(dtype)
-        self.pool = L.AdapterPool(len(self.ranks), d_in, d_out, R, dtype)
+        capacity = None
+        if packed:   # each slot its rank rounded up to 8 rows, some an octet more
+            extra = np.random.default_rng(seed).random(len(self.ranks)) < 0.3
+            capacity = [min(R, max(8, -(-int(r) // 8) * 8 + 8 * int(e))) for r, e in zip(self.ranks, extra)]
+        self.pool = L.AdapterPool(len(self.ranks), d_in, d_out, R, dtype, capacity=capacity)
         self.A, self.B, self.alphas = {}, {}, {}
         for s, r in enumerate(self.ranks):
             if r > 0:
@@ -121,12 +127,12 @@ class Layer:
                            rows=rows)["y"]
 
 
-@pytest.mark.parametrize("seed", range(64))
-def test_sweep_forward(seed):
+@pytest.mark.parametrize("seed,packed", [(s, False) for s in range(64)] + [(s, True) for s in range(64, 88)])
+def test_sweep_forward(seed, packed):
     c = draw_case(seed)
     dtype = torch.float32 if c["rng"].random() < 0.25 else torch.bfloat16
-    what = describe(c, " dtype=%s" % str(dtype).split(".")[-1])
-    lay = Layer(c, c["d_out"], dtype, seed)
+    what = describe(c, " dtype=%s%s" % (str(dtype).split(".")[-1], " packed" if packed else ""))
+    lay = Layer(c, c["d_out"], dtype, seed, packed=packed)
     ids_dev = torch.as_tensor(c["ids"], device="cuda")
     ref = lay.oracle(c["ids"], c["rows"])
     sel = torch.as_tensor(c["rows"], device="cuda")
